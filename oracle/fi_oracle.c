@@ -1,0 +1,162 @@
+/*
+ * fi_oracle.c -- CPU oracle for the exact online causal long convolution.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * includes this file; only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header or table with the GPU path.
+ *
+ * Source: the page "Flash Inference: Inferenza in Tempo Quasi-Lineare per
+ * Modelli di Sequenza a Convoluzione Lunga e Oltre" (lowest.today summary of
+ * arXiv 2410.12982), written [FI] below.
+ *
+ * What it computes is the plain definition, not the method: the method (the
+ * relaxed tiling of [FI] "Strategia di Tiling (Algoritmo 1)") reaches the same
+ * sums exactly up to rounding order, so the oracle is the definition written
+ * out, in fp64, with every sum taken in ascending input position.
+ *
+ * Conventions (0-indexed restatement of [FI] "Definizione del Compito" and
+ * "Definizione Specifica di LCSM"): channels are (b, c) with b in [0,B),
+ * c in [0,D); the filter h[j][c] (j in [0,L)) is shared across b; layouts are
+ * row-major with channels innermost: h[L][D], x[B][L][D], y[B][L][D].
+ *
+ *   y[b][t][c] = sum_{s=0}^{t} h[t-s][c] * x[b][s][c]        (lag 0 included)
+ *
+ * Closed loop: x[b][0][c] is given and, after y[b][t][c] is known,
+ * x[b][t+1][c] = tanh(y[b][t][c]) (the per-channel feedback that stands in for
+ * the model's block and sampler of [FI] "Algoritmo di Inferenza LCSM
+ * (Algoritmo 2)"); with bf16 storage the fed-back value is rounded to bf16,
+ * nearest-even.
+ *
+ * Mutation hooks: building with -DFIO_MUTANT=k plants one deliberate mistake
+ * (k = 1..6, listed at each hook).  The test suite builds every mutant on the
+ * CPU and checks that each one fails at least one pin; the normal build never
+ * defines FIO_MUTANT.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef FIO_MUTANT
+#define FIO_MUTANT 0
+#endif
+
+/* Channels processed together by one thread: the innermost loop runs over
+ * them so it vectorises without reassociating any single channel's sum. */
+#define FIO_CBLK 16
+
+/* Round a double to the nearest bf16 value (8 significant bits), ties to
+ * even.  Exact: scaling by a power of two and rint() (round-half-even under
+ * the default rounding mode) introduce no other rounding. */
+double fio_round_bf16(double v)
+{
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e2;
+    frexp(v, &e2);                 /* |v| in [2^(e2-1), 2^e2) */
+    int e = e2 - 1;
+    if (e < -126) e = -126;        /* bf16 subnormal range: fixed quantum */
+    double q = ldexp(1.0, e - 7);  /* weight of the last kept bit */
+#if FIO_MUTANT == 6
+    return floor(v / q) * q;       /* mutant 6: truncation instead of nearest-even */
+#else
+    return rint(v / q) * q;
+#endif
+}
+
+/* One batch element, channels [c0, c0+cn), all positions.
+ * closed == 0: x is read for every position.
+ * closed != 0: x[0][.] is read, x[t+1][.] is written from tanh(y[t][.]). */
+static void conv_block(int64_t D, int64_t L, int64_t c0, int64_t cn,
+                       const double *h, double *x, double *y,
+                       int closed, int round_bf16)
+{
+    double acc[FIO_CBLK];
+    for (int64_t t = 0; t < L; ++t) {
+        for (int64_t k = 0; k < cn; ++k) acc[k] = 0.0;
+#if FIO_MUTANT == 1
+        for (int64_t s = 0; s < t; ++s) {          /* mutant 1: lag-0 term dropped */
+#else
+        for (int64_t s = 0; s <= t; ++s) {
+#endif
+#if FIO_MUTANT == 2
+            const double *hr = h + (t - s + (t > s ? 1 : 0)) % L * D + c0;  /* mutant 2: lag off by one */
+#elif FIO_MUTANT == 3
+            const double *hr = h + s * D + c0;    /* mutant 3: filter index s instead of t-s */
+#else
+            const double *hr = h + (t - s) * D + c0;
+#endif
+            const double *xr = x + s * D + c0;
+            for (int64_t k = 0; k < cn; ++k) {
+#if FIO_MUTANT == 4
+                acc[k] += hr[(k + 1) % cn] * xr[k];  /* mutant 4: neighbouring channel's filter */
+#else
+                acc[k] += hr[k] * xr[k];
+#endif
+            }
+        }
+        double *yr = y + t * D + c0;
+        for (int64_t k = 0; k < cn; ++k) yr[k] = acc[k];
+        if (closed && t + 1 < L) {
+            double *xn = x + (t + 1) * D + c0;
+            for (int64_t k = 0; k < cn; ++k) {
+#if FIO_MUTANT == 5
+                double f = tanh(acc[k]) * 0.5;     /* mutant 5: wrong feedback */
+#else
+                double f = tanh(acc[k]);
+#endif
+                xn[k] = round_bf16 ? fio_round_bf16(f) : f;
+            }
+        }
+    }
+}
+
+static void run(int64_t B, int64_t D, int64_t L, const double *h, double *x,
+                double *y, int closed, int round_bf16, int nthreads)
+{
+    int64_t nblk = (D + FIO_CBLK - 1) / FIO_CBLK;
+    int64_t jobs = B * nblk;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t j = 0; j < jobs; ++j) {
+        int64_t b = j / nblk, c0 = (j % nblk) * FIO_CBLK;
+        int64_t cn = D - c0 < FIO_CBLK ? D - c0 : FIO_CBLK;
+        conv_block(D, L, c0, cn, h, x + b * L * D, y + b * L * D,
+                   closed, round_bf16);
+    }
+    (void)nthreads;
+}
+
+/* Open loop: y = causal convolution of x with h, every channel, every position. */
+void fio_open(int64_t B, int64_t D, int64_t L, const double *h,
+              const double *x, double *y, int nthreads)
+{
+    run(B, D, L, h, (double *)x, y, 0, 0, nthreads);
+}
+
+/* Closed loop, free-running.  x_io[B][L][D]: on entry x_io[b][0][c] holds x0;
+ * on return every x_io[b][t][c] holds the input that produced y[b][t][c]. */
+void fio_closed(int64_t B, int64_t D, int64_t L, const double *h, double *x_io,
+                double *y, int round_bf16, int nthreads)
+{
+    run(B, D, L, h, x_io, y, 1, round_bf16, nthreads);
+}
+
+/* One channel, selected positions: y_k = sum_{s=0}^{t_k} h[t_k - s] x[s],
+ * with h and x given as that channel's series of length L. */
+void fio_points(int64_t L, const double *h, const double *x, int64_t n,
+                const int64_t *t, double *y)
+{
+    for (int64_t k = 0; k < n; ++k) {
+        int64_t tk = t[k];
+        double acc = 0.0;
+        if (tk >= 0 && tk < L)
+            for (int64_t s = 0; s <= tk; ++s) acc += h[tk - s] * x[s];
+        y[k] = acc;
+    }
+}
+
+int fio_mutant(void) { return FIO_MUTANT; }
