@@ -1,0 +1,197 @@
+#!/usr/bin/env python
+"""Benchmark: mixer tokens/s of the exact online causal long convolution.
+
+One step = one full pass of the hot path over one batch: fi_run_closed_loop
+on the Hyena-like mixer workload (B=1, D=1024, L=16384, fp32, closed-loop tanh
+feedback, decaying-Gaussian filters with log-uniform tau in [64, 8192]) with
+the inputs already resident in HBM.  Protocol of the pages: warm-ups, then
+the mean over timed runs.  Prints ONE JSON line.
+
+Also reported:
+  roofline      the persistent kernel (k_run, the only kernel of a step):
+                algorithmic bytes of the method (per-tile x block read, accumulator
+                read+write, filter taps or spectrum, per-step reads/writes) divided
+                by its mean duration from HIP events on its stream, against
+                MI355X's 8 TB/s HBM peak; ``traffic`` comes from the committed
+                rocprofv3 counter summary when it was taken on the current kernel
+                source, else null.
+  cpu_baseline  the CPU oracle (fp64 brute force) timed on a channel subset of
+                the same workload, scaled to the whole workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "mixer tokens/sec (B·L/s) at D=1024, L=16K; % HBM roofline"
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_run_hyena-d1024-l16k_traffic.json")
+KERNEL_SOURCES = ["exact_online_amd/csrc/fi_kernels.hip", "exact_online_amd/csrc/fi_device.hpp",
+                  "exact_online_amd/csrc/fi_internal.h"]
+
+
+def progress(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(B, D, L, s_x, s_h, T, closed) -> int:
+    """Bytes the method moves: every tile of side U reads its x block (U s_x)
+    and reads+writes U accumulators (2U*4) per channel, plus the filter data
+    per filter channel (taps h[1..2U) for direct tiles, the (U+1)-point complex
+    spectrum for FFT tiles); every step reads the accumulator and x, writes y
+    (and x in closed loop)."""
+    P = (L - 1).bit_length()
+    tot = 0
+    for q in range(P):
+        U = 1 << q
+        n = L // (2 * U)
+        Fq = (2 * U - 1) * s_h if U <= T else (U + 1) * 8
+        tot += n * (B * D * (U * s_x + 2 * U * 4) + D * Fq)
+    tot += B * D * L * (4 + s_x + 4 + (s_x if closed else 0))
+    return tot
+
+
+def load_traffic(sha: str, launches_per_step: int = 1):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, h, x0, nch: int):
+    import oracle
+    orc = oracle.default()
+    nch = min(nch, w.D)
+    t0 = time.perf_counter()
+    orc.conv_closed(h[:, :nch], x0[:, :nch])
+    dt = time.perf_counter() - t0
+    scale = (w.B * w.D) / (x0.shape[0] * nch)
+    return {"value": w.B * w.L / (dt * scale), "unit": "tokens/s", "cores": orc.threads,
+            "kind": "oracle",
+            "sample": f"{nch} of {w.D} channels, all {w.L} positions, closed loop, fp64; "
+                      f"{dt:.2f} s measured, scaled x{scale:g} (channels are independent)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="hyena-d1024-l16k")
+    ap.add_argument("--small-tile-max", type=int, default=0)
+    ap.add_argument("--cpu-channels", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): the path shards "
+              "over channels with no per-step communication, so a multi-GPU figure is not produced here.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import exact_online_amd as fi
+    import workloads
+
+    w = workloads.get(args.workload)
+    T = args.small_tile_max or 128
+    closed = "closed" in w.modes[0]
+    progress(f"bench: workload {w.name} B={w.B} D={w.D} L={w.L} {w.dtype} closed={closed}")
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    h = workloads.make_filter(w)
+    x0 = workloads.make_x0(w)
+    io = fi.FI_BF16 if w.dtype == "bf16" else fi.FI_F32
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(workloads.to_bf16_bits(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    hd = dev(h)
+    xin = dev(x0) if closed else dev(workloads.make_x(w))
+    y = torch.empty((w.B, w.L, w.D), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    m = fi.Mixer(w.B, w.D, w.L, hd, io, args.small_tile_max, stream)
+    create_ms = (time.perf_counter() - t0) * 1e3
+    fb = fi.FI_FEEDBACK_TANH if closed else fi.FI_FEEDBACK_NONE
+
+    def one():
+        m.reset()
+        m.run(xin, fb, y)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    progress(f"bench: create {create_ms:.1f} ms, {args.warmup} warm-up passes done")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        one()
+        evs[k][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per = [a.elapsed_time(b) for a, b in evs]
+    ms_step = total_ms / args.steps
+    kern_ms = sum(per) / len(per)
+    assert torch.isfinite(y).all().item(), "non-finite output"
+    progress(f"bench: {args.steps} timed passes, {ms_step:.4f} ms/pass, per-pass {['%.4f' % p for p in per]}")
+
+    s_x = 2 if w.dtype == "bf16" else 4
+    ab = algorithmic_bytes(w.B, w.D, w.L, s_x, s_x, 128, closed)
+    achieved = ab / (kern_ms * 1e-3) / 1e9
+    sha = kernel_source_sha()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(sha),
+                "kernel": "k_run", "algorithmic_bytes": ab, "kernel_ms": round(kern_ms, 4),
+                "kernel_source_sha": sha}
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress(f"bench: timing the CPU oracle on {args.cpu_channels} channels")
+        cpu = cpu_baseline(w, h, x0, args.cpu_channels)
+    m.close()
+    value = w.B * w.L / (ms_step * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "D": w.D, "L": w.L,
+                   "mode": "closed-loop tanh" if closed else "open loop", "small_tile_max": T,
+                   "create_ms": round(create_ms, 1)},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,61 @@
+// fi_internal.h -- declarations shared by the host API (fi_api.cpp) and the
+// kernel launchers (fi_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fi {
+
+constexpr int kMaxLevels = 40;
+constexpr int kLdsFftMax = 4096;  // largest complex FFT held in LDS (32 KiB in fp32)
+
+// Device state of one handle.  Layouts (rows padded to LS = L rounded up to 64):
+//   hT[D][LS]      filter, one contiguous row per channel c, fp32
+//   state[C][LS]   per channel (b, c), ch = b*D + c: positions below the
+//                  current one hold x (the input history), the others hold the
+//                  accumulated tile contributions (the two share one slot per
+//                  position, as the activation buffer is reused for the mixer
+//                  output in the pages' memory optimisation)
+//   spec           per FFT level q (U = 2^q): [D][U] float4 = (alpha, beta) of
+//                  the packed real circular convolution of length 2U, stored in
+//                  the position order of the forward FFT, scaled by 1/U
+//   twf            twiddles, twf[S + m] = exp(-2 pi i m / S), S = 1 .. 2^smax
+//   scratch        [slots][sc_stride] complex fp32 for FFTs larger than LDS
+struct DevState {
+    int64_t B, D, L, C, LS;
+    int T;                 // largest tile side done directly
+    int W;                 // LDS accumulator window (positions) of the run kernel
+    int XR;                // LDS ring of recent inputs (positions)
+    int F;                 // LDS FFT buffer (complex points) of the run kernel
+    int io_bf16;
+    float *hT;
+    float *state;
+    void *spec;            // float4
+    int64_t spec_off[kMaxLevels];  // element (float4) offset of level q, -1 if none
+    void *twf;             // Cx<float>
+    void *scratch;         // Cx<float>
+    int64_t sc_stride;     // complex elements per scratch slot
+    int64_t sc_slots;
+    int umax_fft;          // largest FFT tile side (0 if none)
+};
+
+// fi_create helpers (synchronous work on `st`)
+hipError_t launch_transpose(const DevState &d, const void *h, hipStream_t st);
+hipError_t launch_twiddles(void *twd, void *twf, int smax, hipStream_t st);
+hipError_t launch_spectra(const DevState &d, int q, void *scd, int64_t scd_stride, int64_t slots,
+                          const void *twd, hipStream_t st);
+hipError_t launch_zero(float *p, int64_t n, hipStream_t st);
+
+// online pieces
+hipError_t launch_step(const DevState &d, int64_t t, const void *x_t, float *y_t, hipStream_t st);
+hipError_t launch_tile(const DevState &d, int64_t i, hipStream_t st);
+
+// the persistent pass over all positions
+hipError_t launch_run(const DevState &d, const void *x_in, int closed, float *y, void *x_out,
+                      int grid, hipStream_t st);
+int run_lds_bytes(const DevState &d);
+int run_max_blocks_per_cu(const DevState &d, int closed);
+int tile_fft_lds_bytes();
+
+}  // namespace fi

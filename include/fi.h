@@ -1,0 +1,139 @@
+/*
+ * fi.h -- exact online causal long convolution on AMD MI355X (gfx950).
+ *
+ * Citations name the web page "Flash Inference: Inferenza in Tempo
+ * Quasi-Lineare per Modelli di Sequenza a Convoluzione Lunga e Oltre"
+ * (lowest.today summary of arXiv 2410.12982), written [FI], and its sections.
+ *
+ * The operation ([FI] "Definizione del Compito", "Definizione Specifica di
+ * LCSM"), 0-indexed: for every channel (b, c), b in [0,B), c in [0,D),
+ *
+ *     y[b][t][c] = sum_{s=0}^{t} h[t-s][c] * x[b][s][c],     t in [0, L),
+ *
+ * where x[b][t+1][.] may only be supplied after y[b][t][.] has been returned
+ * (online constraint).  The filter h[L][D] is shared by the B batch rows.  The
+ * library evaluates it with the relaxed power-of-two tiling of [FI]
+ * "Strategia di Tiling (Algoritmo 1)": once position i-1 is complete, with
+ * U = largest power of two dividing i, the tile tau(x, [i-U, i), h, [i, i+U))
+ * of [FI] "Definizione di Aggregazione di Contribuzione" adds the contribution
+ * of x[i-U, i) to y[i, i+U) (clipped to < L).  Tiles of side U <= T (the
+ * config's small_tile_max) are direct Toeplitz products; larger ones are FFT
+ * circular convolutions of length 2U with precomputed filter spectra ([FI]
+ * "Ottimizzazione della Memoria", "Trucco di Convoluzione Circolare").
+ *
+ * Layouts: row-major, channels innermost: h[L][D], x[B][L][D], y[B][L][D],
+ * per-step vectors [B][D].  Storage dtype of x and h is the config's io_dtype
+ * (fp32 or bf16); y is always fp32 and all arithmetic is fp32.
+ *
+ * Pointers: every array argument is a DEVICE pointer (hipMalloc'ed or a
+ * torch CUDA tensor's data_ptr()) unless stated.  Calls other than
+ * fi_create / fi_destroy are asynchronous on the config's stream: the caller
+ * owns its arrays and must keep them valid until that stream is synchronised.
+ *
+ * Errors: functions return FI_OK (0) or a negative FI_ERR_* code and never
+ * throw.  Arguments are validated before any device work; a rejected call
+ * changes nothing.  FI_ERR_HIP records the HIP error, readable through
+ * fi_strerror(FI_ERR_HIP) on the same thread.  A handle is not thread-safe;
+ * distinct handles are independent.
+ */
+#ifndef FI_H_
+#define FI_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fi_handle fi_handle;  /* opaque; owns all the device memory it allocates */
+
+/* Storage type of x and h. */
+enum { FI_F32 = 0, FI_BF16 = 1 };
+
+/* Feedback of fi_run_closed_loop. */
+enum {
+    FI_FEEDBACK_NONE = 0,   /* open loop: x[b][t][c] read from x_in[B][L][D] */
+    FI_FEEDBACK_TANH = 1    /* closed loop: x[b][t+1][c] = tanh(y[b][t][c]) */
+};
+
+enum {
+    FI_OK = 0,
+    FI_ERR_INVALID = -1,      /* bad argument: NULL, size <= 0, overflow, unknown enum */
+    FI_ERR_NOMEM = -2,        /* device allocation failed */
+    FI_ERR_HIP = -3,          /* HIP runtime error (see fi_strerror) */
+    FI_ERR_STATE = -4,        /* call not allowed at the handle's current position */
+    FI_ERR_UNSUPPORTED = -5   /* valid but not supported (e.g. no gfx950 device) */
+};
+
+typedef struct {
+    int64_t B;               /* batch rows, >= 1 */
+    int64_t D;               /* channels per row, >= 1 */
+    int64_t L;               /* positions = filter length, >= 1 (any value; tiles clip to < L) */
+    int32_t io_dtype;        /* FI_F32 or FI_BF16 */
+    int32_t small_tile_max;  /* T: largest tile side done as a direct product; 0 = default (128);
+                                otherwise a power of two in [64, 4096] */
+    void *stream;            /* hipStream_t the handle works on; NULL = the null stream */
+} fi_config;
+
+/*
+ * fi_create: validate cfg, allocate the handle's device state, copy the
+ * filter h[L][D] (device pointer, io_dtype) and precompute, on the device,
+ * the filter spectra of every FFT tile level ([FI] "Ottimizzazione della
+ * Memoria": the filter DFT is computed ahead for each block size) and the
+ * twiddle tables.  Synchronous: returns after the device work finished, so
+ * the caller may free h at once.  On success *out receives the handle at
+ * position 0; on failure *out is set to NULL and nothing stays allocated.
+ */
+int fi_create(const fi_config *cfg, const void *h, fi_handle **out);
+
+/*
+ * fi_step: one online step at the handle's position t ([FI] "Strategia di
+ * Tiling (Algoritmo 1)", one loop iteration): reads x_t[B][D] (io_dtype),
+ * writes y_t[B][D] (fp32) = accumulated tiles + h[0] * x_t (the red cell),
+ * then, if t+1 < L, applies the tile of side lowbit(t+1).  Position becomes
+ * t+1.  FI_ERR_STATE when the position already is L.
+ */
+int fi_step(fi_handle *s, const void *x_t, float *y_t);
+
+/*
+ * fi_run_closed_loop: all L steps in one call, from position 0 (else
+ * FI_ERR_STATE); leaves the position at L.  One persistent device pass.
+ *   fb = FI_FEEDBACK_TANH: x_in is x_0[B][D]; x[t+1] = tanh(y[t]) (rounded to
+ *        bf16, nearest-even, when io_dtype is FI_BF16).
+ *   fb = FI_FEEDBACK_NONE: x_in is x[B][L][D] (the open-loop inputs, consumed
+ *        in order through the same online schedule).
+ *   y[B][L][D] (fp32) receives every output; x_out[B][L][D] (io_dtype), if not
+ *   NULL, receives the inputs that produced them.
+ */
+int fi_run_closed_loop(fi_handle *s, const void *x_in, int32_t fb, float *y, void *x_out);
+
+/* fi_reset: position := 0; the accumulators are cleared on the stream before
+ * the next fi_step (fi_run_closed_loop clears the rows it uses itself). */
+int fi_reset(fi_handle *s);
+
+/* fi_destroy: synchronise the stream and free everything; NULL is a no-op. */
+void fi_destroy(fi_handle *s);
+
+/* fi_position: the handle's current position (host value), or -1 for NULL. */
+int64_t fi_position(const fi_handle *s);
+
+/* fi_strerror: static description of a status code (host; thread-local text
+ * for FI_ERR_HIP includes the last HIP error seen on this thread). */
+const char *fi_strerror(int status);
+
+/*
+ * Schedule helper (host, integer only): the tile applied once position i-1
+ * is complete, for 1 <= i < L ([FI] "Strategia di Tiling (Algoritmo 1)",
+ * "Analisi di Complessita (Proposizione 1)"): U = largest power of two dividing
+ * i, inputs [in_lo, in_hi) = [i-U, i), outputs [out_lo, out_hi) =
+ * [i, min(i+U, L)).  FI_ERR_INVALID for i outside [1, L) or a NULL out.
+ */
+typedef struct {
+    int64_t U, in_lo, in_hi, out_lo, out_hi;
+} fi_tile;
+int fi_tile_at(int64_t L, int64_t i, fi_tile *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FI_H_ */

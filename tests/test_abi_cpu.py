@@ -1,0 +1,114 @@
+"""CPU-only checks of the C ABI: the library loads and exports every symbol
+include/fi.h declares, arguments are validated before any device work, and the
+schedule helper reproduces the relaxed tiling of the page "Flash Inference:
+Inferenza in Tempo Quasi-Lineare per Modelli di Sequenza a Convoluzione Lunga
+e Oltre", section "Strategia di Tiling (Algoritmo 1)"."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import exact_online_amd as fi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "fi.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fi_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(fi.EXPORTS), names
+    for n in names:
+        assert hasattr(fi.lib, n), n
+
+
+def test_strerror_and_null_handles():
+    for code in (fi.FI_OK, fi.FI_ERR_INVALID, fi.FI_ERR_NOMEM, fi.FI_ERR_HIP,
+                 fi.FI_ERR_STATE, fi.FI_ERR_UNSUPPORTED, -99):
+        assert isinstance(fi.fi_strerror(code), str) and fi.fi_strerror(code)
+    assert fi.fi_position(None) == -1
+    fi.fi_destroy(None)  # no-op
+    assert fi.lib.fi_step(None, 1, 1) == fi.FI_ERR_INVALID
+    assert fi.lib.fi_run_closed_loop(None, 1, 1, 1, None) == fi.FI_ERR_INVALID
+    assert fi.lib.fi_reset(None) == fi.FI_ERR_INVALID
+
+
+def _create_status(cfg, h=0x1000):
+    out = ctypes.c_void_p(123)
+    st = fi.lib.fi_create(ctypes.byref(cfg) if cfg is not None else None, h, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=0, D=4, L=16), dict(B=1, D=0, L=16), dict(B=1, D=4, L=0), dict(B=-1, D=4, L=16),
+    dict(B=1, D=4, L=16, io_dtype=2), dict(B=1, D=4, L=16, small_tile_max=96),
+    dict(B=1, D=4, L=16, small_tile_max=32), dict(B=1, D=4, L=16, small_tile_max=8192),
+    dict(B=1 << 31, D=4, L=16), dict(B=1 << 20, D=1 << 20, L=1 << 20),
+])
+def test_create_rejects_invalid(kw):
+    st, out = _create_status(fi.make_config(**kw))
+    assert st == fi.FI_ERR_INVALID
+    assert out is None
+
+
+def test_create_rejects_null():
+    assert _create_status(None)[0] == fi.FI_ERR_INVALID
+    assert _create_status(fi.make_config(1, 4, 16), h=0)[0] == fi.FI_ERR_INVALID
+    cfg = fi.make_config(1, 4, 16)
+    assert fi.lib.fi_create(ctypes.byref(cfg), 0x1000, None) == fi.FI_ERR_INVALID
+
+
+def test_create_without_gpu_is_unsupported():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, out = _create_status(fi.make_config(1, 4, 16))
+    assert st == fi.FI_ERR_UNSUPPORTED and out is None
+
+
+# --------------------------------------------------------------- schedule
+def _tiles(L):
+    return [fi.fi_tile_at(L, i) for i in range(1, L)]
+
+
+@pytest.mark.parametrize("L", [2, 3, 8, 16, 64, 100, 1000, 1024])
+def test_schedule_exact_cover(L):
+    """Every pair s < t is added by exactly one tile, and a tile only reads
+    completed positions and writes positions not yet produced."""
+    cover = {}
+    for i, t in enumerate(_tiles(L), start=1):
+        assert t.in_hi == i and t.out_lo == i and t.U == (i & -i)
+        assert t.in_lo == i - t.U and t.out_hi == min(i + t.U, L)
+        for s in range(t.in_lo, t.in_hi):
+            for o in range(t.out_lo, t.out_hi):
+                cover[(s, o)] = cover.get((s, o), 0) + 1
+    want = {(s, o) for o in range(L) for s in range(o)}
+    assert set(cover) == want
+    assert all(v == 1 for v in cover.values())
+
+
+def test_schedule_counts_match_the_page():
+    facts = json.load(open(os.path.join(ROOT, "tests", "golden", "schedule_facts.json")))["facts"]
+    P = 14
+    L = 1 << P
+    tiles = _tiles(L)
+    assert len(tiles) == L - 1                                   # L-1 invocations
+    for q in range(P):
+        assert sum(t.U == (1 << q) for t in tiles) == 1 << (P - 1 - q)   # 2^(P-1-q)
+    f4 = sum(t.U <= 4 for t in tiles) / len(tiles)
+    f8 = sum(t.U <= 8 for t in tiles) / len(tiles)
+    assert abs(f4 - facts[2]["value"]) < 1e-3
+    assert abs(f8 - facts[3]["value"]) < 1e-3
+
+
+def test_tile_at_rejects_out_of_range():
+    t = fi.fi_tile()
+    for L, i in [(1, 1), (16, 0), (16, 16), (16, -1)]:
+        assert fi.lib.fi_tile_at(L, i, ctypes.byref(t)) == fi.FI_ERR_INVALID
+    assert fi.lib.fi_tile_at(16, 3, None) == fi.FI_ERR_INVALID

@@ -1,0 +1,216 @@
+"""GPU parity at small sizes: the HIP library (through its C ABI) against the
+CPU oracle on the same seeded inputs, element by element.
+
+Tolerances (BASELINE north-star, fp32 arithmetic): open loop relative L2
+error <= 1e-5; closed loop max abs error <= 1e-3 on y; closed-loop feedback
+consistency |x[t+1] - tanh(y[t])| <= 1e-6 (fp64 tanh of the GPU's own y; for
+bf16 storage half a bf16 ulp more).  Cases with only direct tiles and integer
+data are compared bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from fi_harness import (boundary_positions, chaos_horizon, columns, gpu_run, gpu_steps, host,
+                        log, rel_l2, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import exact_online_amd as fi  # noqa: E402  (fails loudly if libfi.so is missing)
+
+ORC = None
+
+
+def orc():
+    global ORC
+    if ORC is None:
+        ORC = oracle.default()
+    return ORC
+
+
+def small(name="mixer-d16-l1k", **kw):
+    return workloads.get(name).with_(**kw)
+
+
+def _open_case(w, T=0, via_steps=False):
+    h = workloads.make_filter(w)
+    x = workloads.make_x(w)
+    hd, xd = to_dev(h, w.dtype), to_dev(x, w.dtype)
+    if via_steps:
+        y = gpu_steps(hd, w.B, w.D, w.L, w.dtype, xd, T)
+    else:
+        y, xo = gpu_run(hd, w.B, w.D, w.L, w.dtype, xd, closed=False, T=T)
+        assert torch.equal(xo, xd)
+    ref = orc().conv_open(h, x)
+    return host(y), ref
+
+
+# ---------------------------------------------------------------- open loop
+@pytest.mark.parametrize("T", [0, 64, 256])
+def test_small_mixer_open_run(T):
+    w = small()
+    log("case small mixer open run T", T)
+    y, ref = _open_case(w, T)
+    err = rel_l2(y, ref)
+    log("rel l2", err)
+    assert err <= 1e-5
+
+
+def test_small_mixer_open_steps():
+    w = small()
+    log("case small mixer open via fi_step")
+    y, ref = _open_case(w, 0, via_steps=True)
+    assert rel_l2(y, ref) <= 1e-5
+
+
+@pytest.mark.parametrize("L,T", [(1, 64), (2, 64), (5, 64), (63, 64), (64, 64), (65, 64), (100, 64),
+                                 (129, 64), (1000, 64), (3000, 128), (5000, 64)])
+def test_ragged_lengths_open(L, T):
+    w = small(B=2, D=3, L=L, seed=L)
+    log("case ragged open L", L, "T", T)
+    y, ref = _open_case(w, T)
+    assert rel_l2(y, ref) <= 1e-5
+    if L <= 300:
+        ys, _ = _open_case(w, T, via_steps=True)
+        assert rel_l2(ys, ref) <= 1e-5
+
+
+@pytest.mark.parametrize("T", [64, 128, 512])
+def test_delta_filters_hit_every_level(T):
+    """h = delta_k gives y[t] = x[t-k]; one k per channel, chosen on and
+    around every tile side, so every level's kernel moves data exactly once."""
+    L = 16384
+    ks = [1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 1023, 1024,
+          2047, 2048, 4095, 4096, 4097, 8191, 8192, 12345, 16383]
+    D = len(ks)
+    h = np.zeros((L, D), np.float32)
+    for c, k in enumerate(ks):
+        h[k, c] = 1.0
+    x = np.random.default_rng(5).standard_normal((1, L, D)).astype(np.float32)
+    log("case delta filters T", T)
+    y, _ = gpu_run(to_dev(h, "f32"), 1, D, L, "f32", to_dev(x, "f32"), closed=False, T=T, want_x=False)
+    y = host(y)
+    for c, k in enumerate(ks):
+        ref = np.zeros(L)
+        ref[k:] = x[0, :L - k, c]
+        err = np.abs(y[0, :, c] - ref).max()
+        assert err <= 2e-5, (k, err)
+        # positions before the first FFT tile see only direct and in-register
+        # tiles of a single nonzero tap: exact
+        first_fft = 2 * T if T >= 64 else 128
+        assert np.array_equal(y[0, :first_fft, c], ref[:first_fft].astype(np.float32)), k
+
+
+@pytest.mark.parametrize("T", [128, 4096])
+def test_integer_data(T):
+    """x, h in {-3..3}: direct tiles are exact; FFT tiles round to the exact
+    integer (|y| < 2^24)."""
+    L, D, B = 8192, 4, 2
+    r = np.random.default_rng(9)
+    h = r.integers(-3, 4, size=(L, D)).astype(np.float32)
+    x = r.integers(-3, 4, size=(B, L, D)).astype(np.float32)
+    log("case integer data T", T)
+    y, _ = gpu_run(to_dev(h, "f32"), B, D, L, "f32", to_dev(x, "f32"), closed=False, T=T, want_x=False)
+    y = host(y).astype(np.float64)
+    ref = orc().conv_open(h, x)
+    assert np.array_equal(np.rint(y), ref)
+    assert np.abs(y - ref).max() < 0.05
+    if T == 4096:   # every tile direct (largest tile side is 4096)
+        assert np.array_equal(y, ref)
+
+
+def test_large_fft_tiles_global_path():
+    """L = 2^15: tiles of side 8192 and 16384 exceed LDS and run through the
+    global-scratch passes."""
+    w = workloads.get("hyena-d1024-l16k").with_(D=6, L=1 << 15, B=2)
+    log("case global-path fft L=32768")
+    y, ref = _open_case(w)
+    assert rel_l2(y, ref) <= 1e-5
+
+
+# -------------------------------------------------------------- closed loop
+def _closed_case(w, T=0):
+    h = workloads.make_filter(w)
+    x0 = workloads.make_x0(w)
+    y, xo = gpu_run(to_dev(h, w.dtype), w.B, w.D, w.L, w.dtype, to_dev(x0, w.dtype), closed=True, T=T)
+    return h, x0, host(y).astype(np.float64), host(xo).astype(np.float64)
+
+
+def _check_feedback(y, xo, x0, bf16):
+    assert np.array_equal(xo[:, 0, :], x0.astype(np.float64))
+    want = np.tanh(y[:, :-1, :])
+    tol = 1e-6
+    if bf16:
+        tol = tol + 2.0 ** -8 * np.abs(want)   # half a bf16 ulp is at most 2^-8 of the value
+    assert np.all(np.abs(xo[:, 1:, :] - want) <= tol)
+
+
+@pytest.mark.parametrize("T", [0, 64])
+def test_small_mixer_closed(T):
+    w = small()
+    log("case small mixer closed T", T)
+    h, x0, y, xo = _closed_case(w, T)
+    _check_feedback(y, xo, x0, False)
+    assert chaos_horizon(h, x0, w.L) == w.L        # well-posed over the whole run
+    yr, _ = orc().conv_closed(h, x0)
+    assert np.abs(y - yr).max() <= 1e-3
+    ytf = orc().conv_open(h, xo)                    # step-wise validity
+    assert np.abs(y - ytf).max() <= 1e-4
+
+
+@pytest.mark.parametrize("L", [1, 3, 64, 65, 700, 3000])
+def test_ragged_closed(L):
+    w = small(B=2, D=3, L=L, seed=L + 1)
+    log("case ragged closed L", L)
+    h, x0, y, xo = _closed_case(w, 64)
+    _check_feedback(y, xo, x0, False)
+    yr, _ = orc().conv_closed(h, x0)
+    assert np.abs(y - yr).max() <= 1e-3
+
+
+def test_bf16_open_and_closed():
+    w = small(dtype="bf16", B=2, D=8, L=4096)
+    log("case bf16 open")
+    y, ref = _open_case(w)
+    assert rel_l2(y, ref) <= 1e-5
+    log("case bf16 closed")
+    h, x0, y, xo = _closed_case(w)
+    _check_feedback(y, xo, x0, True)
+    assert np.array_equal(orc().round_bf16(xo), xo)     # stored on the bf16 grid
+    ytf = orc().conv_open(h, xo)
+    assert np.abs(y - ytf).max() <= 1e-4
+
+
+# ------------------------------------------------------------------- state
+def test_state_machine_and_determinism():
+    w = small(D=4, L=256)
+    h = to_dev(workloads.make_filter(w), "f32")
+    x = to_dev(workloads.make_x(w), "f32")
+    y1 = torch.empty((1, 256, 4), device="cuda")
+    y2 = torch.empty_like(y1)
+    xt = torch.zeros((1, 4), device="cuda")
+    yt = torch.zeros((1, 4), device="cuda")
+    with fi.Mixer(1, 4, 256, h, stream=torch.cuda.current_stream()) as m:
+        m.run(x, fi.FI_FEEDBACK_NONE, y1)
+        with pytest.raises(fi.FiError) as e:
+            m.step(xt, yt)
+        assert e.value.status == fi.FI_ERR_STATE
+        with pytest.raises(fi.FiError) as e:
+            m.run(x, fi.FI_FEEDBACK_NONE, y2)
+        assert e.value.status == fi.FI_ERR_STATE
+        m.reset()
+        m.step(xt, yt)
+        with pytest.raises(fi.FiError) as e:
+            m.run(x, fi.FI_FEEDBACK_NONE, y2)
+        assert e.value.status == fi.FI_ERR_STATE
+        m.reset()
+        m.run(x, fi.FI_FEEDBACK_NONE, y2)
+        torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
