@@ -52,6 +52,8 @@ void free_state(DevState &d) {
     if (d.spec) (void)hipFree(d.spec);
     if (d.twf) (void)hipFree(d.twf);
     if (d.scratch) (void)hipFree(d.scratch);
+    if (d.lvl) (void)hipFree(d.lvl);
+    d.lvl = nullptr;
     d.hT = nullptr;
     d.state = nullptr;
     d.spec = nullptr;
@@ -85,6 +87,18 @@ int build(fi_handle *s, const void *h) {
         smax = q;
     }
     d.F = d.umax_fft > 0 ? (d.umax_fft < fi::kLdsFftMax ? d.umax_fft : fi::kLdsFftMax) : 1;
+    // FFT region of the persistent pass: the largest LDS transform, or the
+    // staging of a tile's input (4U bytes) and, for U <= 1024, its spectrum
+    // (16U bytes) behind that tile's own transform buffer
+    d.fftreg = fi::lds_fft_elems(d.F) * 8;
+    for (int q = 0; q < fi::kMaxLevels; ++q) {
+        if (d.spec_off[q] < 0) continue;
+        const int U = 1 << q;
+        int need = 0;
+        if (U <= 1024) need = fi::lds_fft_elems(U) * 8 + 4 * U + 16 * U;
+        else if (U <= 2048) need = fi::lds_fft_elems(U) * 8 + 4 * U;
+        if (need > d.fftreg) d.fftreg = need;
+    }
 
     FI_HIP(dalloc(&d.hT, (size_t)(d.D * d.LS) * sizeof(float)));
     FI_HIP(dalloc(&d.state, (size_t)(d.C * d.LS) * sizeof(float)));
@@ -108,6 +122,22 @@ int build(fi_handle *s, const void *h) {
     d.sc_slots = slots;
     d.sc_stride = d.umax_fft > fi::kLdsFftMax ? d.umax_fft : 0;
     if (d.sc_stride > 0) FI_HIP(dalloc(&d.scratch, (size_t)(slots * d.sc_stride) * 8));
+    // level buffers (persistent pass): FFT levels whose tiles reach past the
+    // LDS window, L/2 + U floats per channel each (positions with bit q set)
+    d.lvl_qlo = fi::kMaxLevels;
+    d.lvl_qhi = -1;
+    int64_t lvl_per_ch = 0;
+    for (int q = 0; q < fi::kMaxLevels; ++q) {
+        d.lvl_off[q] = -1;
+        const int64_t U = (int64_t)1 << q;
+        if (d.spec_off[q] < 0 || U <= d.W) continue;
+        d.lvl_off[q] = lvl_per_ch;
+        lvl_per_ch += (d.LS / 2 + U + 63) / 64 * 64;
+        if (q < d.lvl_qlo) d.lvl_qlo = q;
+        d.lvl_qhi = q;
+    }
+    d.lvl_stride = lvl_per_ch;
+    if (lvl_per_ch > 0) FI_HIP(dalloc(&d.lvl, (size_t)(d.C * lvl_per_ch) * sizeof(float)));
 
     FI_HIP(fi::launch_transpose(d, h, st));
     void *twd = nullptr;
@@ -136,8 +166,8 @@ int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
     if (!cfg || !h || !out) return FI_ERR_INVALID;
     if (cfg->B < 1 || cfg->D < 1 || cfg->L < 1) return FI_ERR_INVALID;
     if (cfg->io_dtype != FI_F32 && cfg->io_dtype != FI_BF16) return FI_ERR_INVALID;
-    int T = cfg->small_tile_max == 0 ? 128 : cfg->small_tile_max;
-    if (!is_pow2(T) || T < 64 || T > 4096) return FI_ERR_INVALID;
+    int T = cfg->small_tile_max == 0 ? 64 : cfg->small_tile_max;
+    if (!is_pow2(T) || T < 64 || T > 256) return FI_ERR_INVALID;
     // sizes: every element count must fit comfortably in int64 and the
     // per-channel position index in int32 kernels' loop bounds
     const int64_t lim = (int64_t)1 << 31;
@@ -167,8 +197,8 @@ int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
     d.C = C;
     d.LS = LS;
     d.T = T;
-    d.W = T > 512 ? T : 512;
-    d.XR = T;
+    d.W = 256;                  // LDS accumulator ring: >= T and >= the 128-position block
+    d.XR = T >= 128 ? T : 0;    // LDS ring of recent inputs, only for direct tiles (T >= 128)
     d.io_bf16 = cfg->io_dtype == FI_BF16;
     s->stream = static_cast<hipStream_t>(cfg->stream);
     s->pos = 0;

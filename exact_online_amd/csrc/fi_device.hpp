@@ -1,17 +1,20 @@
 // fi_device.hpp -- device building blocks for the gfx950 kernels: complex
-// arithmetic, small in-register DFTs, wave-level Stockham FFTs in LDS and
-// radix-2 passes over a global scratch buffer.
+// arithmetic, small in-register DFTs, wave-level in-place FFT stages in LDS
+// and radix-2 passes over a global scratch buffer.
 //
 // Citations name the page "Flash Inference: Inferenza in Tempo Quasi-Lineare
 // per Modelli di Sequenza a Convoluzione Lunga e Oltre" (lowest.today summary
 // of arXiv 2410.12982), written [FI].  The FFT is the tool of [FI] "Definizione
 // di Aggregazione di Contribuzione" (Lemma 1: an FFT evaluates a tile's
-// contribution in O(n log n)); the algorithms below are the textbook ones:
-// Stockham autosort (natural order in and out, twiddle before the butterfly)
-// and decimation in frequency / in time for the passes outside LDS.
+// contribution in O(n log n)); the algorithms are the textbook in-place
+// Cooley-Tukey ones: decimation in frequency for the forward transform
+// (natural order in, bit-reversed order out) and decimation in time for the
+// inverse (bit-reversed in, natural out), so a convolution never permutes.
 //
 // Every routine here is executed by ONE wavefront (64 lanes) that owns the
-// buffers it touches; workgroups are one wavefront wide.
+// buffers it touches; workgroups are one wavefront wide.  Pointers carry their
+// address space (global or LDS) so loads and stores compile to global_* and
+// ds_* instructions rather than flat ones.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,15 +22,27 @@
 
 #include "fi_internal.h"
 
+#define FI_GLOBAL __attribute__((address_space(1)))
+#define FI_SHARED __attribute__((address_space(3)))
+
 namespace fi {
 
 constexpr int kWave = 64;
 
+template <typename T>
+__device__ __forceinline__ FI_GLOBAL T* gmem(T* p) { return (FI_GLOBAL T*)p; }
+template <typename T>
+__device__ __forceinline__ const FI_GLOBAL T* gmem(const T* p) { return (const FI_GLOBAL T*)p; }
+template <typename T>
+__device__ __forceinline__ FI_SHARED T* smem_ptr(T* p) { return (FI_SHARED T*)p; }
+
 // ------------------------------------------------------------------ complex
+// A complex number as a two-lane clang vector (x = real, y = imaginary); the
+// vector type can be loaded and stored through pointers of any address space.
 template <typename R>
-struct alignas(2 * sizeof(R)) Cx {
-    R x, y;
-};
+using Cx = R __attribute__((ext_vector_type(2)));
+using V2 = float __attribute__((ext_vector_type(2)));
+using V4 = float __attribute__((ext_vector_type(4)));
 
 template <typename R>
 __device__ __forceinline__ Cx<R> cadd(Cx<R> a, Cx<R> b) { return {a.x + b.x, a.y + b.y}; }
@@ -36,11 +51,6 @@ __device__ __forceinline__ Cx<R> csub(Cx<R> a, Cx<R> b) { return {a.x - b.x, a.y
 template <typename R>
 __device__ __forceinline__ Cx<R> cmul(Cx<R> a, Cx<R> b) {
     return {a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x};
-}
-// a * conj(b)
-template <typename R>
-__device__ __forceinline__ Cx<R> cmulc(Cx<R> a, Cx<R> b) {
-    return {a.x * b.x + a.y * b.y, a.y * b.x - a.x * b.y};
 }
 template <typename R>
 __device__ __forceinline__ Cx<R> cconj(Cx<R> a) { return {a.x, -a.y}; }
@@ -53,8 +63,11 @@ __device__ __forceinline__ Cx<R> cmul_mi(Cx<R> a) {
 
 // Twiddle tables: tw[S + m] = exp(-2*pi*i*m/S) for every power of two S and
 // m in [0, S); the inverse transforms use the conjugate.
+template <typename R>
+using TwPtr = const FI_GLOBAL Cx<R>*;
+
 template <bool INV, typename R>
-__device__ __forceinline__ Cx<R> twiddle(const Cx<R>* tw, int S, int m) {
+__device__ __forceinline__ Cx<R> twiddle(TwPtr<R> tw, int S, int m) {
     Cx<R> w = tw[S + m];
     if constexpr (INV) w.y = -w.y;
     return w;
@@ -98,136 +111,319 @@ __device__ __forceinline__ void dft(Cx<T>* v) {
     }
 }
 
-// ------------------------------------------------ Stockham FFT in LDS
-// One radix-R pass over M points held in LDS, current sub-transform length LS:
-// butterfly j takes v_r = buf[j + r*M/R], multiplies by w_{LS*R}^{r*k}
-// (k = j mod LS), applies DFT_R and stores at (j-k)*R + k + r*LS.  All reads of
-// a pass complete before its writes (register staging), so it runs in place.
-template <int M, int R, int LS, bool INV, typename T>
-__device__ __forceinline__ void stockham_pass(Cx<T>* buf, const Cx<T>* tw) {
-    constexpr int NBF = M / R;
-    constexpr int PER = (NBF + kWave - 1) / kWave;
+// ------------------------------------------------------------ wave sync
+// Workgroups are one wavefront wide.  A wavefront's LDS and global memory
+// operations are performed in program order and see each other across lanes,
+// so ordering between lanes only needs the compiler kept from moving memory
+// operations across this point.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------- in-place FFT stages in LDS
+// LDS FFT buffers keep one spare slot per 8 points, which spreads the
+// strided butterfly accesses over the banks.
+__device__ __forceinline__ int lp(int p) { return p + (p >> 3); }
+
+// Twiddle sources: powers(S, k, w) sets w[r] = exp(-2 pi i r k / S), r < R.
+template <typename T>
+struct GlobalTw {  // every power read from the global table tw[S + t]
+    TwPtr<T> tw;
+    template <int R>
+    __device__ __forceinline__ void powers(int S, int k, Cx<T>* w) const {
+#pragma unroll
+        for (int r = 1; r < R; ++r) w[r] = tw[S + r * k];
+    }
+};
+// Two-level LDS table for S <= 4096: with u = t * 4096 / S,
+// exp(-2 pi i u / 4096) = A[u >> 6] * B[u & 63], A[a] = w_64^a, B[b] = w_4096^b.
+// One lookup per butterfly; the other powers are products (depth <= 3).
+struct LdsTw {
+    const FI_SHARED Cx<float>* A;  // [64], B follows at A + 64
+    template <int R>
+    __device__ __forceinline__ void powers(int S, int k, Cx<float>* w) const {
+        const int u = k * (kLdsFftMax / S);
+        w[1] = cmul(A[u >> 6], A[64 + (u & 63)]);
+        if constexpr (R >= 4) {
+            w[2] = cmul(w[1], w[1]);
+            w[3] = cmul(w[2], w[1]);
+        }
+        if constexpr (R == 8) {
+            w[4] = cmul(w[2], w[2]);
+            w[5] = cmul(w[4], w[1]);
+            w[6] = cmul(w[4], w[2]);
+            w[7] = cmul(w[4], w[3]);
+        }
+    }
+};
+
+// v_r *= w_S^{r k} for r = 1..R-1 (conjugated for the inverse).
+template <int R, bool INV, typename T, typename Tw>
+__device__ __forceinline__ void twiddle_apply(Cx<T>* v, const Tw& tw, int S, int k) {
+    Cx<T> w[R];
+    tw.template powers<R>(S, k, w);
+#pragma unroll
+    for (int r = 1; r < R; ++r) {
+        if constexpr (INV) w[r].y = -w[r].y;
+        v[r] = cmul(v[r], w[r]);
+    }
+}
+
+// Radix of the stage that splits a sub-problem of size S.
+__host__ __device__ constexpr int ct_radix(int S) { return S >= 8 ? 8 : S; }
+
+// Size of the last (smallest) sub-problem stage of an M-point transform.
+__host__ __device__ constexpr int ct_smallest(int M) {
+    int S = M;
+    while (S / ct_radix(S) > 1) S /= ct_radix(S);
+    return S;
+}
+
+template <typename T>
+struct LdsIn {
+    const FI_SHARED Cx<T>* b;
+    __device__ __forceinline__ Cx<T> operator()(int p) const { return b[lp(p)]; }
+};
+template <typename T>
+struct LdsOut {
+    FI_SHARED Cx<T>* b;
+    __device__ __forceinline__ void operator()(int p, Cx<T> v) const { b[lp(p)] = v; }
+};
+
+// Bit reversal of r over log2(R) bits, R in {2, 4, 8}.
+template <int R>
+__device__ __forceinline__ constexpr int rev_r(int r) {
+    if constexpr (R == 8) return ((r & 1) << 2) | (r & 2) | ((r >> 2) & 1);
+    else if constexpr (R == 4) return ((r & 1) << 1) | ((r >> 1) & 1);
+    else return r;
+}
+
+// One in-place Cooley-Tukey stage on every sub-problem of size S of an
+// M-point sequence (sub-problems contiguous), radix R = ct_radix(S), Q = S/R.
+// Butterfly (base, j) owns the slots base + j + r*Q, r < R:
+//   forward (decimation in frequency): v_r from slot r; u = DFT_R(v),
+//     u_rho *= w_S^{j rho}, u_rho to slot rev(rho);
+//   inverse (decimation in time): v_rho from slot rev(rho),
+//     v_rho *= conj(w_S^{j rho}), u = IDFT_R(v), u_r to slot r.
+// Storing each radix-R output in bit-reversed slot order makes the whole
+// forward transform end in plain bit-reversed order.
+// Each butterfly reads and writes the same slots, so no staging is needed;
+// a lane processes its butterflies GRP at a time to overlap memory latency.
+template <int M, int S, bool INV, typename T, typename Src, typename Dst, typename Tw>
+__device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const Tw& tw) {
+    constexpr int R = ct_radix(S);
+    constexpr int Q = S / R;
+    constexpr int NB = M / R;
+    constexpr int PER = (NB + kWave - 1) / kWave;
+    constexpr int GRP = PER < 2 ? PER : 2;
     const int lane = threadIdx.x & (kWave - 1);
-    Cx<T> v[PER][R];
+#pragma unroll 1
+    for (int u0 = 0; u0 < PER; u0 += GRP) {
+        Cx<T> v[GRP][R];
+        int off[GRP], jj[GRP];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int j = lane + kWave * u;
-        if (NBF % kWave == 0 || j < NBF) {
-            const int k = j & (LS - 1);
+        for (int g = 0; g < GRP; ++g) {
+            const int n = lane + kWave * (u0 + g);
+            jj[g] = n % Q;
+            off[g] = (n / Q) * S + jj[g];
+            if (NB % kWave == 0 || n < NB) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) v[u][r] = buf[j + r * NBF];
-            if constexpr (LS > 1) {
-#pragma unroll
-                for (int r = 1; r < R; ++r) v[u][r] = cmul(v[u][r], twiddle<INV>(tw, LS * R, r * k));
+                for (int r = 0; r < R; ++r) v[g][r] = src(off[g] + (INV ? rev_r<R>(r) : r) * Q);
             }
-            dft<R, INV>(v[u]);
+        }
+#pragma unroll
+        for (int g = 0; g < GRP; ++g) {
+            const int n = lane + kWave * (u0 + g);
+            if (NB % kWave == 0 || n < NB) {
+                if constexpr (INV) {
+                    if constexpr (S > R) twiddle_apply<R, true>(v[g], tw, S, jj[g]);
+                    dft<R, true>(v[g]);
+                } else {
+                    dft<R, false>(v[g]);
+                    if constexpr (S > R) twiddle_apply<R, false>(v[g], tw, S, jj[g]);
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) dst(off[g] + (INV ? r : rev_r<R>(r)) * Q, v[g][r]);
+            }
         }
     }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int j = lane + kWave * u;
-        if (NBF % kWave == 0 || j < NBF) {
-            const int k = j & (LS - 1);
-            const int i0 = (j - k) * R + k;
-#pragma unroll
-            for (int r = 0; r < R; ++r) buf[i0 + r * LS] = v[u][r];
-        }
-    }
-    __syncthreads();
+    wave_sync();
 }
 
-template <int M, int LS, bool INV, typename T>
-__device__ __forceinline__ void stockham_from(Cx<T>* buf, const Cx<T>* tw) {
-    if constexpr (LS < M) {
-        constexpr int R = (M / LS >= 8) ? 8 : ((M / LS >= 4) ? 4 : 2);
-        stockham_pass<M, R, LS, INV>(buf, tw);
-        stockham_from<M, LS * R, INV>(buf, tw);
+// Forward M-point FFT (unnormalised), natural order in, bit-reversed order
+// out (position brev(k) holds frequency k): the first stage reads src,
+// the others work in place on the LDS buffer.
+template <int M, int S, typename T, typename Src, typename Tw>
+__device__ __forceinline__ void dif_lds(const Src& src, FI_SHARED Cx<T>* lds, const Tw& tw) {
+    if constexpr (S > 1) {
+        if constexpr (S == M) ct_stage<M, S, false, T>(src, LdsOut<T>{lds}, tw);
+        else ct_stage<M, S, false, T>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
+        dif_lds<M, S / ct_radix(S), T>(src, lds, tw);
     }
 }
 
-// Unnormalised M-point FFT of buf (LDS), natural order in and out.
-template <int M, bool INV, typename T>
-__device__ __forceinline__ void fft_lds(Cx<T>* buf, const Cx<T>* tw) {
-    stockham_from<M, 1, INV>(buf, tw);
+// Inverse of dif_lds (unnormalised, times M): bit-reversed order in, natural
+// order out, in place on the LDS buffer.  Every stage but the smallest has
+// radix 8, so the sizes run ct_smallest(M), 8x that, ..., M.
+template <int M, int S, typename T, typename Tw>
+__device__ __forceinline__ void dit_lds(FI_SHARED Cx<T>* lds, const Tw& tw) {
+    if constexpr (S <= M) {
+        ct_stage<M, S, true, T>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
+        if constexpr (S < M) dit_lds<M, S * 8, T>(lds, tw);
+    }
 }
 
-// Runtime-size dispatch for 2 <= M <= kLdsFftMax.
-template <bool INV, typename T>
-__device__ __noinline__ void fft_lds_any(int M, Cx<T>* buf, const Cx<T>* tw) {
+// Runtime-size dispatch (64 <= M <= kLdsFftMax), in place on the LDS buffer.
+template <typename T, typename Tw>
+__device__ __noinline__ void dif_lds_any(int M, FI_SHARED Cx<T>* lds, const Tw& tw) {
+    const LdsIn<T> in{lds};
     switch (M) {
-        case 2: fft_lds<2, INV>(buf, tw); break;
-        case 4: fft_lds<4, INV>(buf, tw); break;
-        case 8: fft_lds<8, INV>(buf, tw); break;
-        case 16: fft_lds<16, INV>(buf, tw); break;
-        case 32: fft_lds<32, INV>(buf, tw); break;
-        case 64: fft_lds<64, INV>(buf, tw); break;
-        case 128: fft_lds<128, INV>(buf, tw); break;
-        case 256: fft_lds<256, INV>(buf, tw); break;
-        case 512: fft_lds<512, INV>(buf, tw); break;
-        case 1024: fft_lds<1024, INV>(buf, tw); break;
-        case 2048: fft_lds<2048, INV>(buf, tw); break;
-        case 4096: fft_lds<4096, INV>(buf, tw); break;
+        case 64: dif_lds<64, 64, T>(in, lds, tw); break;
+        case 128: dif_lds<128, 128, T>(in, lds, tw); break;
+        case 256: dif_lds<256, 256, T>(in, lds, tw); break;
+        case 512: dif_lds<512, 512, T>(in, lds, tw); break;
+        case 1024: dif_lds<1024, 1024, T>(in, lds, tw); break;
+        case 2048: dif_lds<2048, 2048, T>(in, lds, tw); break;
+        case 4096: dif_lds<4096, 4096, T>(in, lds, tw); break;
         default: break;
     }
 }
-
+template <typename T, typename Tw>
+__device__ __noinline__ void dit_lds_any(int M, FI_SHARED Cx<T>* lds, const Tw& tw) {
+    switch (M) {
+        case 64: dit_lds<64, ct_smallest(64), T>(lds, tw); break;
+        case 128: dit_lds<128, ct_smallest(128), T>(lds, tw); break;
+        case 256: dit_lds<256, ct_smallest(256), T>(lds, tw); break;
+        case 512: dit_lds<512, ct_smallest(512), T>(lds, tw); break;
+        case 1024: dit_lds<1024, ct_smallest(1024), T>(lds, tw); break;
+        case 2048: dit_lds<2048, ct_smallest(2048), T>(lds, tw); break;
+        case 4096: dit_lds<4096, ct_smallest(4096), T>(lds, tw); break;
+        default: break;
+    }
+}
 // ---------------------------------------------- passes over global scratch
 // Radix-2 decimation in frequency on every sub-problem of size S of sc[0..M):
 // (v0, v1) = (sc[b+j], sc[b+j+S/2]) -> (v0+v1, (v0-v1) w_S^j).  After the
-// passes down to size F, the block of F points at p*F holds the DFT inputs of
-// frequencies k = brev(p) + (M/F)*q (bit reversal over log2(M/F) bits).
+// passes down to size F, the block of F points at p*F holds the transform of
+// the frequencies k = brev(p) + (M/F)*kq (bit reversal over log2(M/F) bits);
+// after the F-point transforms of the blocks, position q of every frequency k
+// is brev(k) over log2(M) bits.
+// Global-memory loops handle kBatch iterations per lane at a time, all loads
+// of a batch issued before its first store, so one memory latency covers the
+// batch.  Iterations of a batch touch disjoint elements.
+constexpr int kBatch = 8;
+
 template <typename T>
-__device__ __forceinline__ void dif_pass(Cx<T>* sc, int M, int S, const Cx<T>* tw) {
+__device__ __forceinline__ void dif_pass(FI_GLOBAL Cx<T>* sc, int M, int S, TwPtr<T> tw) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int half = S >> 1;
-    for (int n = lane; n < (M >> 1); n += kWave) {
-        const int b = (n / half) * S, j = n % half;
-        Cx<T> v0 = sc[b + j], v1 = sc[b + j + half];
-        sc[b + j] = cadd(v0, v1);
-        sc[b + j + half] = cmul(csub(v0, v1), twiddle<false>(tw, S, j));
+    const int half = S >> 1, nbf = M >> 1;
+#pragma unroll 1
+    for (int n0 = 0; n0 < nbf; n0 += kWave * kBatch) {
+        Cx<T> v0[kBatch], v1[kBatch], w[kBatch];
+        int o[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int n = n0 + lane + kWave * u;
+            const int b = (n / half) * S, j = n % half;
+            o[u] = b + j;
+            if (n < nbf) {
+                v0[u] = sc[o[u]];
+                v1[u] = sc[o[u] + half];
+                w[u] = tw[S + j];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (n0 + lane + kWave * u < nbf) {
+                sc[o[u]] = cadd(v0[u], v1[u]);
+                sc[o[u] + half] = cmul(csub(v0[u], v1[u]), w[u]);
+            }
+        }
     }
-    __syncthreads();
+    wave_sync();
 }
 
 // Inverse of dif_pass (unnormalised): (v0, v1 w_S^-j) -> (v0+., v0-.).
 template <typename T>
-__device__ __forceinline__ void dit_pass(Cx<T>* sc, int M, int S, const Cx<T>* tw) {
+__device__ __forceinline__ void dit_pass(FI_GLOBAL Cx<T>* sc, int M, int S, TwPtr<T> tw) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int half = S >> 1;
-    for (int n = lane; n < (M >> 1); n += kWave) {
-        const int b = (n / half) * S, j = n % half;
-        Cx<T> v0 = sc[b + j];
-        Cx<T> v1 = cmul(sc[b + j + half], twiddle<true>(tw, S, j));
-        sc[b + j] = cadd(v0, v1);
-        sc[b + j + half] = csub(v0, v1);
+    const int half = S >> 1, nbf = M >> 1;
+#pragma unroll 1
+    for (int n0 = 0; n0 < nbf; n0 += kWave * kBatch) {
+        Cx<T> v0[kBatch], v1[kBatch], w[kBatch];
+        int o[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int n = n0 + lane + kWave * u;
+            const int b = (n / half) * S, j = n % half;
+            o[u] = b + j;
+            if (n < nbf) {
+                v0[u] = sc[o[u]];
+                v1[u] = sc[o[u] + half];
+                w[u] = tw[S + j];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (n0 + lane + kWave * u < nbf) {
+                const Cx<T> t = cmul(v1[u], cconj(w[u]));
+                sc[o[u]] = cadd(v0[u], t);
+                sc[o[u] + half] = csub(v0[u], t);
+            }
+        }
     }
-    __syncthreads();
+    wave_sync();
 }
 
-// FFT of each F-point block of sc[0..M) through the LDS buffer.
-template <bool INV, typename T>
-__device__ __forceinline__ void blocks_via_lds(Cx<T>* sc, int M, int F, Cx<T>* lbuf, const Cx<T>* tw) {
+// Copies n elements between global and LDS (padded) buffers in batches.
+template <typename T>
+__device__ __forceinline__ void copy_to_lds(FI_SHARED Cx<T>* lds, const FI_GLOBAL Cx<T>* g, int n) {
     const int lane = threadIdx.x & (kWave - 1);
-    for (int base = 0; base < M; base += F) {
-        for (int q = lane; q < F; q += kWave) lbuf[q] = sc[base + q];
-        __syncthreads();
-        fft_lds_any<INV>(F, lbuf, tw);
-        for (int q = lane; q < F; q += kWave) sc[base + q] = lbuf[q];
-        __syncthreads();
+#pragma unroll 1
+    for (int q0 = 0; q0 < n; q0 += kWave * kBatch) {
+        Cx<T> v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int q = q0 + lane + kWave * u;
+            if (q < n) v[u] = g[q];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int q = q0 + lane + kWave * u;
+            if (q < n) lds[lp(q)] = v[u];
+        }
     }
+    wave_sync();
+}
+template <typename T>
+__device__ __forceinline__ void copy_from_lds(FI_GLOBAL Cx<T>* g, const FI_SHARED Cx<T>* lds, int n) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll 4
+    for (int q = lane; q < n; q += kWave) g[q] = lds[lp(q)];
+    wave_sync();
 }
 
 __device__ __forceinline__ int brev_bits(int v, int nb) {
     return nb == 0 ? 0 : (int)(__brev((unsigned)v) >> (32 - nb));
 }
 
-// Position of the partner frequency M-k for the layout above
-// (P = M/F blocks, nb = log2 P): block p with klow = brev(p) pairs with block
-// brev(P - klow) reversed; block 0 pairs with itself as q -> (F-q) mod F.
-__device__ __forceinline__ int partner_block(int p, int P, int nb) {
-    const int kl = brev_bits(p, nb);
-    return kl == 0 ? 0 : brev_bits(P - kl, nb);
+// Frequency pairs (k, M-k) in bit-reversed position order: position p holds
+// k = brev(p); its partner sits at the mirror of p within its octave,
+// p' = 3*2^j - 1 - p for 2^j <= p < 2^(j+1), and p' = p for p < 2.
+__device__ __forceinline__ int mirror_pos(int p) {
+    if (p < 2) return p;
+    const int j = 31 - __builtin_clz(p);
+    return 3 * (1 << j) - 1 - p;
+}
+// The n-th position of a pair's first member, n in [0, M/2]: 0, 1, then the
+// lower halves [2^j, 2^j + 2^(j-1)) of the octaves j >= 1, in order.
+__device__ __forceinline__ int pair_first(int n) {
+    if (n < 2) return n;
+    const int m = n - 1;
+    const int j = 32 - __builtin_clz(m);  // bit length of m
+    return (1 << j) + (m - (1 << (j - 1)));
 }
 
 // ------------------------------------------------------------- scalar math
@@ -237,6 +433,11 @@ __device__ __forceinline__ float tanh_fast(float y) {
     const float e = __builtin_amdgcn_exp2f(y * 2.8853900817779268f);  // 2*log2(e)
     return __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
 }
+
+// The same with the argument already multiplied by 2*log2(e):
+// r = 1 / (1 + 2^a); tanh = 1 - 2r.
+__device__ __forceinline__ float tanh_rcp_scaled(float a) { return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a)); }
+constexpr float kTanhScale = 2.8853900817779268f;  // 2*log2(e)
 
 // fp32 -> nearest bf16 value (ties to even), kept in an fp32 register.
 __device__ __forceinline__ float round_bf16(float v) {

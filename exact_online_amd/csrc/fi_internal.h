@@ -9,6 +9,8 @@ namespace fi {
 
 constexpr int kMaxLevels = 40;
 constexpr int kLdsFftMax = 4096;  // largest complex FFT held in LDS (32 KiB in fp32)
+// LDS FFT buffers hold one spare slot per 8 points (bank spreading).
+constexpr int lds_fft_elems(int M) { return M + M / 8; }
 
 // Device state of one handle.  Layouts (rows padded to LS = L rounded up to 64):
 //   hT[D][LS]      filter, one contiguous row per channel c, fp32
@@ -19,8 +21,10 @@ constexpr int kLdsFftMax = 4096;  // largest complex FFT held in LDS (32 KiB in 
 //                  output in the pages' memory optimisation)
 //   spec           per FFT level q (U = 2^q): [D][U] float4 = (alpha, beta) of
 //                  the packed real circular convolution of length 2U, stored in
-//                  the position order of the forward FFT, scaled by 1/U
+//                  the bit-reversed position order of the forward FFT, 1/U folded
 //   twf            twiddles, twf[S + m] = exp(-2 pi i m / S), S = 1 .. 2^smax
+//                  (spectra in bit-reversed frequency order: entry p is
+//                  frequency brev(p))
 //   scratch        [slots][sc_stride] complex fp32 for FFTs larger than LDS
 struct DevState {
     int64_t B, D, L, C, LS;
@@ -28,6 +32,7 @@ struct DevState {
     int W;                 // LDS accumulator window (positions) of the run kernel
     int XR;                // LDS ring of recent inputs (positions)
     int F;                 // LDS FFT buffer (complex points) of the run kernel
+    int fftreg;            // bytes of the run kernel's LDS FFT / staging region
     int io_bf16;
     float *hT;
     float *state;
@@ -38,6 +43,13 @@ struct DevState {
     int64_t sc_stride;     // complex elements per scratch slot
     int64_t sc_slots;
     int umax_fft;          // largest FFT tile side (0 if none)
+    // level buffers of the persistent pass: for each FFT level q with U > W,
+    // per channel ch the floats lvl[ch*lvl_stride + lvl_off[q] + (p >> (q+1))*U
+    // + (p & (U-1))] hold the output of that level's tile for position p
+    float *lvl;
+    int64_t lvl_stride;           // floats per channel (all levels)
+    int64_t lvl_off[kMaxLevels];  // float offset of level q within a channel, -1 if none
+    int lvl_qlo, lvl_qhi;         // range of levels with buffers (qlo > qhi: none)
 };
 
 // fi_create helpers (synchronous work on `st`)

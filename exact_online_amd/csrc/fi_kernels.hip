@@ -26,13 +26,13 @@ namespace fi {
 // ------------------------------------------------------------------ io
 template <bool BF16>
 __device__ __forceinline__ float load_io(const void* p, int64_t idx) {
-    if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[idx]);
-    else return static_cast<const float*>(p)[idx];
+    if constexpr (BF16) return bf16_to_f32(gmem(static_cast<const uint16_t*>(p))[idx]);
+    else return gmem(static_cast<const float*>(p))[idx];
 }
 template <bool BF16>
 __device__ __forceinline__ void store_io(void* p, int64_t idx, float v) {
-    if constexpr (BF16) static_cast<uint16_t*>(p)[idx] = f32_to_bf16_bits(v);
-    else static_cast<float*>(p)[idx] = v;
+    if constexpr (BF16) gmem(static_cast<uint16_t*>(p))[idx] = f32_to_bf16_bits(v);
+    else gmem(static_cast<float*>(p))[idx] = v;
 }
 
 __device__ __forceinline__ int ilog2(int64_t v) { return 63 - __builtin_clzll((unsigned long long)v); }
@@ -78,55 +78,56 @@ __global__ void k_twiddles(Cx<double>* twd, Cx<float>* twf, int smax) {
 // Filter spectra of level q (U = 2^q = M complex points): with the tile's
 // length-2U filter segment g[n] = h[n] for 1 <= n < 2U (g[0] = 0: lag 0 never
 // reaches the outputs [U, 2U) that are kept, [FI] "Trucco di Convoluzione
-// Circolare"), z[n] = g[2n] + i g[2n+1], Z = DFT_M(z) in fp64, and per
-// position p (frequency k, partner frequency M-k at p'):
-//   E = (Z[p] + conj Z[p'])/2,  d = Z[p] - conj Z[p'],  w = exp(-2 pi i k/M)
+// Circolare"), z[n] = g[2n] + i g[2n+1] and Z = DFT_M(z) in fp64, per
+// frequency k (partner frequency M-k):
+//   E = (Z[k] + conj Z[M-k])/2,  d = Z[k] - conj Z[M-k],  w = exp(-2 pi i k/M)
 //   alpha = (E + d/4 (1 - w)) / M,   beta = d/4 (1 + w) / M
-// so that the tile's packed output spectrum is W = alpha Z_x + beta conj(Z_x').
+// so that the tile's packed output spectrum is W = alpha Z_x + beta conj(Z_x')
+// (Z_x' at frequency M-k).  The FFT is the tile's own (in-place, bit-reversed
+// output); alpha/beta are stored in that position order: entry p belongs to
+// frequency brev(p), its partner to the octave mirror of p.
 __global__ __launch_bounds__(64) void k_spectra(const float* hT, int64_t LS, int64_t L, int64_t D, int M,
-                                                float4* spec, Cx<double>* scd, int64_t scd_stride,
-                                                const Cx<double>* twd) {
+                                                V4* spec, Cx<double>* scd, int64_t scd_stride,
+                                                const Cx<double>* twd_) {
     extern __shared__ __align__(16) unsigned char smem[];
-    Cx<double>* lbuf = reinterpret_cast<Cx<double>*>(smem);
+    FI_SHARED Cx<double>* lbuf = smem_ptr(reinterpret_cast<Cx<double>*>(smem));
+    TwPtr<double> twd = gmem(twd_);
+    const GlobalTw<double> gtw{twd};
     const int lane = threadIdx.x;
     const int F = M < kLdsFftMax ? M : kLdsFftMax;
-    const int P = M / F, nb = ilog2(P);
+    const int P = M / F, lm = ilog2(M);
     for (int64_t c = blockIdx.x; c < D; c += gridDim.x) {
-        const float* hr = hT + c * LS;
+        const FI_GLOBAL float* hr = gmem(hT + c * LS);
         auto g = [&](int64_t n) -> double { return (n >= 1 && n < L) ? (double)hr[n] : 0.0; };
-        Cx<double>* Z;
+        FI_GLOBAL Cx<double>* sc = gmem(scd + (int64_t)blockIdx.x * scd_stride);
         if (P == 1) {
-            for (int n = lane; n < M; n += kWave) lbuf[n] = {g(2 * n), g(2 * n + 1)};
-            __syncthreads();
-            fft_lds_any<false>(M, lbuf, twd);
-            Z = lbuf;
+            for (int n = lane; n < M; n += kWave) lbuf[lp(n)] = Cx<double>{g(2 * n), g(2 * n + 1)};
+            wave_sync();
+            dif_lds_any<double>(M, lbuf, gtw);
         } else {
-            Cx<double>* sc = scd + (int64_t)blockIdx.x * scd_stride;
-            for (int n = lane; n < M; n += kWave) sc[n] = {g(2 * n), g(2 * n + 1)};
-            __syncthreads();
+            for (int n = lane; n < M; n += kWave) sc[n] = Cx<double>{g(2 * n), g(2 * n + 1)};
+            wave_sync();
             for (int S = M; S > F; S >>= 1) dif_pass(sc, M, S, twd);
-            blocks_via_lds<false>(sc, M, F, lbuf, twd);
-            Z = sc;
+            for (int p = 0; p < P; ++p) {
+                copy_to_lds(lbuf, sc + p * F, F);
+                dif_lds_any<double>(F, lbuf, gtw);
+                copy_from_lds(sc + p * F, lbuf, F);
+            }
         }
-        float4* out = spec + c * (int64_t)M;
+        auto zat = [&](int p) -> Cx<double> { return P == 1 ? lbuf[lp(p)] : sc[p]; };
+        FI_GLOBAL V4* out = gmem(spec + c * (int64_t)M);
         const double inv = 1.0 / (double)M;
         for (int p = lane; p < M; p += kWave) {
-            const int blk = p / F, q = p % F;
-            const int kl = brev_bits(blk, nb);
-            const int k = kl + P * q;
-            int pp;
-            if (P == 1) pp = (M - p) & (M - 1);
-            else if (kl == 0) pp = (F - q) & (F - 1);
-            else pp = brev_bits(P - kl, nb) * F + (F - 1 - q);
-            const Cx<double> z1 = Z[p], z2c = cconj(Z[pp]);
+            const int k = brev_bits(p, lm);
+            const Cx<double> z1 = zat(p), z2c = cconj(zat(mirror_pos(p)));
             const Cx<double> E = {(z1.x + z2c.x) * 0.5, (z1.y + z2c.y) * 0.5};
             const Cx<double> d4 = {(z1.x - z2c.x) * 0.25, (z1.y - z2c.y) * 0.25};
             const Cx<double> w = twd[M + k];
             const Cx<double> a = cadd(E, cmul(d4, Cx<double>{1.0 - w.x, -w.y}));
             const Cx<double> bb = cmul(d4, Cx<double>{1.0 + w.x, w.y});
-            out[p] = make_float4((float)(a.x * inv), (float)(a.y * inv), (float)(bb.x * inv), (float)(bb.y * inv));
+            out[p] = V4{(float)(a.x * inv), (float)(a.y * inv), (float)(bb.x * inv), (float)(bb.y * inv)};
         }
-        __syncthreads();
+        wave_sync();
     }
 }
 
@@ -136,41 +137,178 @@ __global__ void k_zero(float* p, int64_t n) {
 }
 
 // ============================================================== FFT tile
-// Where a tile's outputs go: positions below `wend` into the LDS ring `accw`
-// (slot = position & wmask), the others into the channel's global row.
+// Where the outputs of the tile at i go: positions below `wend` into the LDS
+// ring `accw` (slot = position & wmask; none when accw is null).  The others
+// either go with plain stores to the tile's level buffer `lvl` (entry o - i;
+// each position receives at most one tile per level, so nothing accumulates
+// there), or, without a level buffer, are added into the channel's global
+// row.  wend - i is a multiple of 128.
 struct TileSink {
-    float* row;
-    float* accw;
+    FI_GLOBAL float* row;
+    FI_SHARED float* accw;
     int64_t wend;
     int wmask;
     int64_t L;
+    FI_GLOBAL float* lvl;
 };
 
-// Adds (a, b) to positions (o, o+1); o is even and wend is even.
-__device__ __forceinline__ void sink_pair(const TileSink& s, int64_t o, float a, float b) {
-    if (o >= s.L) return;
-    if (o < s.wend) {
-        s.accw[o & s.wmask] += a;
-        if (o + 1 < s.L) s.accw[(o + 1) & s.wmask] += b;
-    } else if (o + 1 < s.L) {
-        float2* pp = reinterpret_cast<float2*>(s.row + o);
-        float2 v = *pp;
-        v.x += a;
-        v.y += b;
-        *pp = v;
-    } else {
-        s.row[o] += a;
+// Adds w[m] = (a, b) to positions (i + 2m, i + 2m + 1) for m in [0, n):
+// lane-strided chunks of 64 pairs, each chunk wholly in the LDS ring or wholly
+// global; global read-modify-writes go kBatch chunks at a time.
+template <typename Get>
+__device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n, const Get& get) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int m0 = 0;
+    if (s.accw) {
+        const int nl = (int)((s.wend - i) / 2) < n ? (int)((s.wend - i) / 2) : n;
+#pragma unroll 1
+        for (; m0 < nl; m0 += kWave) {
+            const int m = m0 + lane;
+            const int64_t o = i + 2 * (int64_t)m;
+            if (m < n && o < s.L) {
+                const Cx<float> w = get(m);
+                s.accw[o & s.wmask] += w.x;
+                if (o + 1 < s.L) s.accw[(o + 1) & s.wmask] += w.y;
+            }
+        }
+    }
+    if (s.lvl) {
+#pragma unroll 4
+        for (int m = m0 + lane; m < n; m += kWave) {
+            if (i + 2 * (int64_t)m < s.L) {
+                const Cx<float> w = get(m);
+                *reinterpret_cast<FI_GLOBAL V2*>(s.lvl + 2 * m) = V2{w.x, w.y};
+            }
+        }
+        return;
+    }
+#pragma unroll 1
+    for (; m0 < n; m0 += kWave * kBatch) {
+        V2 v[kBatch];
+        Cx<float> w[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int m = m0 + lane + kWave * u;
+            const int64_t o = i + 2 * (int64_t)m;
+            if (m < n && o + 1 < s.L) v[u] = *reinterpret_cast<const FI_GLOBAL V2*>(s.row + o);
+            if (m < n) w[u] = get(m);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int m = m0 + lane + kWave * u;
+            const int64_t o = i + 2 * (int64_t)m;
+            if (m < n && o + 1 < s.L) {
+                *reinterpret_cast<FI_GLOBAL V2*>(s.row + o) = V2{v[u].x + w[u].x, v[u].y + w[u].y};
+            } else if (m < n && o < s.L) {
+                s.row[o] += w[u].x;
+            }
+        }
     }
 }
 
-__device__ __forceinline__ void untangle_pair(Cx<float>* Z, const float4* spec, int pa, int pb) {
-    const Cx<float> z1 = Z[pa], z2 = Z[pb];
-    const float4 s1 = spec[pa], s2 = spec[pb];
-    // W = alpha Z + beta conj(Z_partner)
-    const Cx<float> w1 = cadd(cmul(Cx<float>{s1.x, s1.y}, z1), cmul(Cx<float>{s1.z, s1.w}, cconj(z2)));
-    const Cx<float> w2 = cadd(cmul(Cx<float>{s2.x, s2.y}, z2), cmul(Cx<float>{s2.z, s2.w}, cconj(z1)));
-    Z[pa] = w1;
-    Z[pb] = w2;
+// W = alpha Z + beta conj(Z') for a partner pair of frequencies (k, M-k):
+// za/zb are the buffer slots holding them, sa/sb their alpha/beta entries.
+template <typename Acc>
+__device__ __forceinline__ void untangle_pair(const Acc& Z, int za, int zb, V4 sa, V4 sb) {
+    const Cx<float> z1 = Z.get(za), z2 = Z.get(zb);
+    const Cx<float> w1 = cadd(cmul(Cx<float>{sa.x, sa.y}, z1), cmul(Cx<float>{sa.z, sa.w}, cconj(z2)));
+    const Cx<float> w2 = cadd(cmul(Cx<float>{sb.x, sb.y}, z2), cmul(Cx<float>{sb.z, sb.w}, cconj(z1)));
+    Z.set(za, w1);
+    Z.set(zb, w2);
+}
+struct PadAcc {  // LDS FFT buffer, padded
+    FI_SHARED Cx<float>* b;
+    __device__ __forceinline__ Cx<float> get(int p) const { return b[lp(p)]; }
+    __device__ __forceinline__ void set(int p, Cx<float> v) const { b[lp(p)] = v; }
+};
+struct FlatAcc {  // global scratch
+    FI_GLOBAL Cx<float>* b;
+    __device__ __forceinline__ Cx<float> get(int p) const { return b[p]; }
+    __device__ __forceinline__ void set(int p, Cx<float> v) const { b[p] = v; }
+};
+
+// Forward-FFT input of the tile: z[n] = x[2n] + i x[2n+1] for n < M/2, zero
+// beyond (the input block padded on the right).
+struct TileIn {
+    const FI_GLOBAL V2* xs;
+    int half;
+    __device__ __forceinline__ Cx<float> operator()(int n) const {
+        if (n < half) {
+            const V2 v = xs[n];
+            return {v.x, v.y};
+        }
+        return {0.f, 0.f};
+    }
+};
+
+// Untangle W = alpha Z + beta conj(Z') over nitems partner pairs held in the
+// LDS buffer; pos(n) gives the (buffer-relative) positions of pair n and
+// spec index = sbase + position.  All spectrum loads of a lane's batch are
+// issued before the first use.
+template <int NB, typename SpecP, typename Pos>
+__device__ __forceinline__ void untangle_lds(FI_SHARED Cx<float>* lds, SpecP spec, int nitems, const Pos& pos) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const PadAcc Z{lds};
+#pragma unroll 1
+    for (int n0 = 0; n0 < nitems; n0 += kWave * NB) {
+        V4 sa[NB], sb[NB];
+        int pa[NB], pb[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int n = n0 + lane + kWave * u;
+            pos(n < nitems ? n : 0, pa[u], pb[u]);
+            if (n < nitems) {
+                sa[u] = spec[pa[u]];
+                sb[u] = spec[pb[u]];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            if (n0 + lane + kWave * u < nitems) untangle_pair(Z, pa[u], pb[u], sa[u], sb[u]);
+        }
+    }
+    wave_sync();
+}
+
+// pairs of a whole bit-reversed transform (or of a block holding its octaves)
+struct PairsAll {
+    __device__ __forceinline__ void operator()(int n, int& a, int& b) const {
+        a = pair_first(n);
+        b = mirror_pos(a);
+    }
+};
+// pairs (q, F-1-q) of one octave-block of size F
+struct PairsMirror {
+    int F;
+    __device__ __forceinline__ void operator()(int n, int& a, int& b) const {
+        a = n;
+        b = F - 1 - n;
+    }
+};
+
+// The same input staged in LDS.
+struct TileInLds {
+    const FI_SHARED V2* xs;
+    int half;
+    __device__ __forceinline__ Cx<float> operator()(int n) const {
+        if (n < half) {
+            const V2 v = xs[n];
+            return {v.x, v.y};
+        }
+        return {0.f, 0.f};
+    }
+};
+
+template <int M, typename XIn, typename SpecP>
+__device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP spec, FI_SHARED Cx<float>* lds,
+                                             const LdsTw& tw, const TileSink& out) {
+    dif_lds<M, M, float>(xin, lds, tw);
+    constexpr int NB = (M / 2 / kWave + 1) < 8 ? (M / 2 / kWave + 1) : 8;
+    untangle_lds<NB>(lds, spec, M / 2 + 1, PairsAll{});
+    dit_lds<M, ct_smallest(M), float>(lds, tw);
+    // point M/2 + m carries outputs 2m, 2m + 1 of the tile
+    tile_output(out, i, M / 2, [lds](int m) { return lds[lp(M / 2 + m)]; });
+    wave_sync();
 }
 
 // The tile tau(x, [i-U, i), h, [i, i+U)) as the circular convolution of
@@ -180,70 +318,111 @@ __device__ __forceinline__ void untangle_pair(Cx<float>* Z, const float4* spec, 
 // sequences are packed in pairs into M = U complex points; the per-level
 // (alpha, beta) fold the packing, the filter spectrum and the 1/M scale.
 // `row` holds the channel's input history (row[s] = x[s] for s < i).
-__device__ __noinline__ void fft_tile(int U, int64_t i, const float* row, const float4* spec,
-                                      Cx<float>* lbuf, Cx<float>* sc, const Cx<float>* tw,
-                                      TileSink out) {
+// xst, when not null, holds the input block x[i-U, i) in LDS (staged by the
+// caller), and spec_lds the tile's alpha/beta entries.
+__device__ __noinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row, const FI_GLOBAL V4* spec,
+                                      FI_SHARED Cx<float>* lbuf, FI_GLOBAL Cx<float>* sc, TwPtr<float> tw,
+                                      const FI_SHARED Cx<float>* twl, TileSink out, const FI_SHARED float* xst,
+                                      const FI_SHARED V4* spec_lds) {
+    const LdsTw ltw{twl};
     const int M = U;
-    const int lane = threadIdx.x & (kWave - 1);
-    const float2* xs = reinterpret_cast<const float2*>(row + (i - U));
-    if (M <= kLdsFftMax) {
-        for (int n = lane; n < M; n += kWave) {
-            Cx<float> z = {0.f, 0.f};
-            if (n < (M >> 1)) {
-                const float2 v = xs[n];
-                z = {v.x, v.y};
+    const FI_GLOBAL float* xblock = row + (i - U);
+    if (xst) {
+        const TileInLds xin{reinterpret_cast<const FI_SHARED V2*>(xst), M / 2};
+        if (spec_lds) {
+            switch (M) {
+                case 128: fft_tile_lds<128>(i, xin, spec_lds, lbuf, ltw, out); return;
+                case 256: fft_tile_lds<256>(i, xin, spec_lds, lbuf, ltw, out); return;
+                case 512: fft_tile_lds<512>(i, xin, spec_lds, lbuf, ltw, out); return;
+                case 1024: fft_tile_lds<1024>(i, xin, spec_lds, lbuf, ltw, out); return;
+                default: break;
             }
-            lbuf[n] = z;
+        } else if (M == 2048) {
+            fft_tile_lds<2048>(i, xin, spec, lbuf, ltw, out);
+            return;
         }
-        __syncthreads();
-        fft_lds_any<false>(M, lbuf, tw);
-        for (int q = lane; q <= (M >> 1); q += kWave) untangle_pair(lbuf, spec, q, (M - q) & (M - 1));
-        __syncthreads();
-        fft_lds_any<true>(M, lbuf, tw);
-        for (int m = lane; m < (M >> 1); m += kWave) {
-            const Cx<float> w = lbuf[(M >> 1) + m];
-            sink_pair(out, i + 2 * m, w.x, w.y);
-        }
-        __syncthreads();
-        return;
     }
-    const int F = kLdsFftMax, P = M / F, nb = ilog2(P);
+    const TileIn xg{reinterpret_cast<const FI_GLOBAL V2*>(xblock), M / 2};
+    switch (M) {
+        case 64: fft_tile_lds<64>(i, xg, spec, lbuf, ltw, out); return;
+        case 128: fft_tile_lds<128>(i, xg, spec, lbuf, ltw, out); return;
+        case 256: fft_tile_lds<256>(i, xg, spec, lbuf, ltw, out); return;
+        case 512: fft_tile_lds<512>(i, xg, spec, lbuf, ltw, out); return;
+        case 1024: fft_tile_lds<1024>(i, xg, spec, lbuf, ltw, out); return;
+        case 2048: fft_tile_lds<2048>(i, xg, spec, lbuf, ltw, out); return;
+        case 4096: fft_tile_lds<4096>(i, xg, spec, lbuf, ltw, out); return;
+        default: break;
+    }
+    // M > 4096: radix-2 decimation-in-frequency passes over the scratch slot
+    // until F = 4096-point blocks remain; after the blocks' own transforms,
+    // position p (block p / F) holds frequency brev(p) over log2(M) bits.
+    // Block 0 holds octaves 0 .. log2(F)-1 and block 1 octave log2(F): both
+    // hold their own partner frequencies and are transformed, multiplied and
+    // transformed back in one LDS visit.  Blocks b >= 2 pair with the mirror
+    // block of their octave through the scratch slot.
+    const int lane = threadIdx.x & (kWave - 1);
+    const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
+    constexpr int F = kLdsFftMax;
+    const int P = M / F;
     const int half = M >> 1;
-    // first decimation-in-frequency pass fused with the load (upper half is 0)
-    for (int j = lane; j < half; j += kWave) {
-        const float2 v = xs[j];
+    for (int j = lane; j < half; j += kWave) {   // first pass fused with the load (upper half is 0)
+        const V2 v = xs[j];
         const Cx<float> z = {v.x, v.y};
         sc[j] = z;
         sc[j + half] = cmul(z, twiddle<false>(tw, M, j));
     }
-    __syncthreads();
+    wave_sync();
     for (int S = half; S > F; S >>= 1) dif_pass(sc, M, S, tw);
-    blocks_via_lds<false>(sc, M, F, lbuf, tw);
     for (int p = 0; p < P; ++p) {
-        const int pp = partner_block(p, P, nb);
-        if (pp < p) continue;
-        if (pp == p) {
-            const int kl = brev_bits(p, nb);
-            for (int q = lane; q < F; q += kWave) {
-                const int q2 = kl == 0 ? ((F - q) & (F - 1)) : (F - 1 - q);
-                if (q2 >= q) untangle_pair(sc, spec, p * F + q, p * F + q2);
+        FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
+        copy_to_lds(lbuf, blk, F);
+        dif_lds<F, F, float>(LdsIn<float>{lbuf}, lbuf, ltw);
+        if (p <= 1) {
+            if (p == 0) untangle_lds<8>(lbuf, spec, F / 2 + 1, PairsAll{});
+            else untangle_lds<8>(lbuf, spec + F, F / 2, PairsMirror{F});
+            dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        }
+        copy_from_lds(blk, lbuf, F);
+    }
+    if (P > 2) {
+        const FlatAcc Zg{sc};
+        for (int p = 2; p < P; ++p) {
+            const int a = 31 - __builtin_clz(p);   // octave of block p: blocks [2^a, 2^(a+1))
+            const int pp = 3 * (1 << a) - 1 - p;
+            if (pp < p) continue;
+#pragma unroll 1
+            for (int k0 = 0; k0 < F; k0 += kWave * kBatch) {
+                V4 sa[kBatch], sb[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int k = k0 + lane + kWave * u;
+                    sa[u] = spec[(int64_t)p * F + k];
+                    sb[u] = spec[(int64_t)pp * F + (F - 1 - k)];
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int k = k0 + lane + kWave * u;
+                    untangle_pair(Zg, p * F + k, pp * F + (F - 1 - k), sa[u], sb[u]);
+                }
             }
-        } else {
-            for (int q = lane; q < F; q += kWave) untangle_pair(sc, spec, p * F + q, pp * F + (F - 1 - q));
+        }
+        wave_sync();
+        for (int p = 2; p < P; ++p) {
+            FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
+            copy_to_lds(lbuf, blk, F);
+            dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+            copy_from_lds(blk, lbuf, F);
         }
     }
-    __syncthreads();
-    blocks_via_lds<true>(sc, M, F, lbuf, tw);
     for (int S = 2 * F; S < M; S <<= 1) dit_pass(sc, M, S, tw);
     // last inverse pass (size M) fused with the output; only the upper half
     // (outputs U..2U-1 of the circular convolution) is needed
-    for (int j = lane; j < half; j += kWave) {
+    tile_output(out, i, half, [sc, tw, half](int j) {
         const Cx<float> v0 = sc[j];
-        const Cx<float> v1 = cmul(sc[j + half], twiddle<true>(tw, M, j));
-        const Cx<float> w = csub(v0, v1);
-        sink_pair(out, i + 2 * j, w.x, w.y);
-    }
-    __syncthreads();
+        const Cx<float> v1 = cmul(sc[j + half], twiddle<true>(tw, 2 * half, j));
+        return csub(v0, v1);
+    });
+    wave_sync();
 }
 
 // ================================================================ fi_step
@@ -276,33 +455,58 @@ __global__ void k_tile_direct(float* state, const float* hT, int64_t LS, int64_t
     }
 }
 
+// Fills the two-level twiddle table A[64] = w_64^a, B[64] = w_4096^b (fp64
+// sincospi of exact dyadic arguments, rounded to fp32).
+__device__ __forceinline__ void fill_lds_twiddles(FI_SHARED Cx<float>* t) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double sn, cs;
+    sincospi(2.0 * lane / 64.0, &sn, &cs);
+    t[lane] = Cx<float>{(float)cs, (float)-sn};
+    sincospi(2.0 * lane / 4096.0, &sn, &cs);
+    t[64 + lane] = Cx<float>{(float)cs, (float)-sn};
+}
+
 __global__ __launch_bounds__(64) void k_tile_fft(DevState d, int64_t i, int U) {
     extern __shared__ __align__(16) unsigned char smem[];
-    Cx<float>* lbuf = reinterpret_cast<Cx<float>*>(smem);
-    const int q = ilog2(U);
-    const float4* spec = static_cast<const float4*>(d.spec) + d.spec_off[q];
+    FI_SHARED Cx<float>* twl = smem_ptr(reinterpret_cast<Cx<float>*>(smem));
+    FI_SHARED Cx<float>* lbuf = twl + 128;
+    fill_lds_twiddles(twl);
+    wave_sync();
+    const int q = ilog2(U);  // level
+    const FI_GLOBAL V4* spec = gmem(static_cast<const V4*>(d.spec)) + d.spec_off[q];
     for (int64_t ch = blockIdx.x; ch < d.C; ch += gridDim.x) {
-        float* row = d.state + ch * d.LS;
-        Cx<float>* sc = static_cast<Cx<float>*>(d.scratch) + (int64_t)blockIdx.x * d.sc_stride;
-        TileSink s{row, nullptr, i, 0, d.L};
-        fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)U, lbuf, sc, static_cast<const Cx<float>*>(d.twf), s);
+        FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
+        FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)blockIdx.x * d.sc_stride;
+        TileSink s{row, nullptr, i, 0, d.L, nullptr};
+        fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)U, lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl, s,
+                 nullptr, nullptr);
     }
 }
 
 // ============================================================ persistent run
-// One wavefront per channel runs all L positions.  Positions are processed in
-// blocks of 64, lane m holding position t0+m:
-//  * the red cells and the tiles of side < 64 -- which all lie inside one
-//    64-position block and together cover its lower triangle -- run in
-//    registers: each new x is pushed into the accumulators of the later
-//    positions of its block (a DPP lane shift slides the filter taps), so the
-//    same products reach the same outputs as those tiles;
-//  * at each block boundary i = t0+64 the tile of side U = lowbit(i) >= 64
+// One wavefront per channel runs all L positions, in blocks of kBlk = 128
+// positions; lane r holds positions t0+r and t0+64+r in two registers.
+//  * Within a block, the red cells and every tile of side < 128 -- these lie
+//    inside one 128-position block and together cover its lower triangle --
+//    run in registers: once x[t] is known it is pushed, times the filter tap
+//    of each lag, into the accumulators of t and of every later position of
+//    the block (lag 0 is the red cell), so the register of position t holds
+//    y[t] when it is read.  The same products reach the same outputs as those
+//    tiles.  Taps come from LDS: hz[128 + j] = h[j], zeros below.
+//  * At each block boundary i = t0+128 the tile of side U = lowbit(i) >= 128
 //    runs: a direct Toeplitz product from LDS when U <= T, else the FFT tile.
-// Accumulators of positions [t0, t0+W) live in an LDS ring; tiles add their
-// outputs beyond it to the channel's global row, which is read back when the
-// position enters the ring.  The global row holds x below the current
-// position, so the FFT tiles read their input blocks from it.
+// Accumulators of positions [t0, t0+W) live in an LDS ring.  A tile's outputs
+// beyond it are stored, without accumulation, in its level's buffer: position
+// p gets a tile of side U = 2^q exactly when bit q of p is set, so when p
+// enters the ring its value is the sum of the buffered levels whose bit is set
+// (and whose tile left p outside the ring).  The channel's global row holds
+// the input history x, from which the FFT tiles read their input blocks.
+constexpr int kBlk = 128;
+constexpr int kMaxBufLevels = 16;    // level buffers summed per position (levels 9 .. 24)
+constexpr int kStageSpecMax = 1024;  // tiles up to this side get spectrum and input staged in LDS
+// (FFT buffer 9M bytes + input 4U + spectrum 16U fits the 36 KiB region for
+// U <= 1024; U = 2048 stages the input only)
+
 struct RunArgs {
     DevState d;
     const void* x_in;
@@ -310,26 +514,40 @@ struct RunArgs {
     void* x_out;
 };
 
-__device__ __forceinline__ void direct_tile_lds(int64_t i, int U, const float* xring, int xmask,
-                                                const float* htap, float* accw, int wmask, int64_t L) {
+__device__ __forceinline__ void direct_tile_lds(int64_t i, int U, const FI_SHARED float* xring, int xmask,
+                                                const FI_SHARED float* htap, FI_SHARED float* accw, int wmask,
+                                                int64_t L) {
     const int lane = threadIdx.x & (kWave - 1);
     for (int r = lane; r < U; r += kWave) {
         float acc = 0.f;
-        const float* hp = htap + U + r;
+        const FI_SHARED float* hp = htap + U + r;
 #pragma unroll 8
         for (int j = 0; j < U; ++j) acc = __builtin_fmaf(xring[(i - U + j) & xmask], hp[-j], acc);
         if (i + r < L) accw[(i + r) & wmask] += acc;
     }
 }
 
+// LDS of k_run: static arrays for the tap table, the twiddle table and the
+// accumulator ring (separate objects, so the compiler sees that the direct-to-
+// LDS staging loads into the dynamic region never touch them), and a dynamic
+// region: FFT / staging area [fftreg bytes] | (T >= 128 only) xring[XR] | htap[2T].
+constexpr int kRing = 256;   // accumulator ring W (small_tile_max <= 256)
+inline int run_lds_floats(const DevState& d) { return d.fftreg / 4 + (d.T >= kBlk ? d.XR + 2 * d.T : 0); }
+
 template <bool CLOSED, bool BF16>
 __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ Cx<float> s_tw[128];     // twiddles A[64] = w_64^a, B[64] = w_4096^b
+    __shared__ float s_ring[kRing];     // accumulators of positions [t0, t0+W)
+    __shared__ float s_taps[2 * kBlk];  // zeros, then the chain's taps
     const DevState& d = a.d;
-    Cx<float>* lbuf = reinterpret_cast<Cx<float>*>(smem);
-    float* accw = reinterpret_cast<float*>(smem + (size_t)d.F * sizeof(Cx<float>));
-    float* xring = accw + d.W;
-    float* htap = xring + d.XR;  // h[0 .. 2T)
+    FI_SHARED Cx<float>* lbuf = smem_ptr(reinterpret_cast<Cx<float>*>(smem));
+    FI_SHARED Cx<float>* twl = smem_ptr(s_tw);
+    FI_SHARED float* accw = smem_ptr(s_ring);
+    FI_SHARED float* hz = smem_ptr(s_taps);
+    FI_SHARED float* xring = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.fftreg);  // direct tiles only
+    FI_SHARED float* htap = xring + d.XR;    // h[0 .. 2T), direct tiles only
+    const bool direct = d.T >= kBlk;
     const int lane = threadIdx.x;
     const int wmask = d.W - 1, xmask = d.XR - 1;
     const int64_t L = d.L, D = d.D;
@@ -337,92 +555,179 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     // consecutive channels on the same XCD (workgroups go round-robin over
     // the 8 XCDs), so their strided y / x_out rows meet in one L2
     const int64_t ch0 = (G % 8 == 0) ? (int64_t)(bid % 8) * (G / 8) + bid / 8 : bid;
-    const Cx<float>* tw = static_cast<const Cx<float>*>(d.twf);
-    Cx<float>* sc = static_cast<Cx<float>*>(d.scratch) + (int64_t)bid * d.sc_stride;
+    TwPtr<float> tw = gmem(static_cast<const Cx<float>*>(d.twf));
+    FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)bid * d.sc_stride;
+    FI_GLOBAL float* yout = gmem(a.y);
+    fill_lds_twiddles(twl);
 
     for (int64_t ch = ch0; ch < d.C; ch += G) {
         const int64_t b = ch / D, c = ch % D;
-        float* row = d.state + ch * d.LS;
-        const float* hrow = d.hT + c * d.LS;
-        for (int64_t q = 4 * lane; q < d.LS; q += 4 * kWave) *reinterpret_cast<float4*>(row + q) = make_float4(0.f, 0.f, 0.f, 0.f);
+        FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
+        const FI_GLOBAL float* hrow = gmem(d.hT + c * d.LS);
+        FI_GLOBAL float* lvl = gmem(d.lvl) + ch * d.lvl_stride;
         for (int q = lane; q < d.W; q += kWave) accw[q] = 0.f;
-        for (int q = lane; q < 2 * d.T; q += kWave) htap[q] = q < L ? hrow[q] : 0.f;
-        const float h0 = hrow[0];
-        const float hlane = (lane >= 1 && lane < L) ? hrow[lane] : 0.f;  // taps h[1..63] for the in-block push
-        __syncthreads();
+        for (int q = lane; q < 2 * kBlk; q += kWave)
+            hz[q] = (q >= kBlk && q - kBlk < L) ? (CLOSED ? kTanhScale * hrow[q - kBlk] : hrow[q - kBlk]) : 0.f;
+        if (direct)
+            for (int q = lane; q < 2 * d.T; q += kWave) htap[q] = q < L ? hrow[q] : 0.f;
+        wave_sync();
 
         float xcur = 0.f;   // closed loop: x at the next position (uniform)
-        float xb_next = 0.f;  // open loop: inputs of the next block, lane m -> position t0+64+m
+        float xb0n = 0.f, xb1n = 0.f;      // open loop: inputs of the next block
         if constexpr (CLOSED) {
             xcur = load_io<BF16>(a.x_in, b * D + c);
         } else {
-            xb_next = lane < L ? load_io<BF16>(a.x_in, (b * L + lane) * D + c) : 0.f;
+            xb0n = lane < L ? load_io<BF16>(a.x_in, (b * L + lane) * D + c) : 0.f;
+            xb1n = lane + kWave < L ? load_io<BF16>(a.x_in, (b * L + lane + kWave) * D + c) : 0.f;
         }
-        for (int64_t t0 = 0; t0 < L; t0 += kWave) {
-            const int64_t tl = t0 + lane;
-            const float xb = xb_next;
+        // nothing in flight when the block loop starts, so the waits inside it
+        // only cover what each block issues
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        for (int64_t t0 = 0; t0 < L; t0 += kBlk) {
+            const int64_t tl0 = t0 + lane, tl1 = t0 + kWave + lane;
+            const float xb0 = xb0n, xb1 = xb1n;
             if constexpr (!CLOSED) {
-                const int64_t tn = tl + kWave;
-                xb_next = tn < L ? load_io<BF16>(a.x_in, (b * L + tn) * D + c) : 0.f;
+                const int64_t n0 = tl0 + kBlk, n1 = tl1 + kBlk;
+                xb0n = n0 < L ? load_io<BF16>(a.x_in, (b * L + n0) * D + c) : 0.f;
+                xb1n = n1 < L ? load_io<BF16>(a.x_in, (b * L + n1) * D + c) : 0.f;
             }
-            const int64_t pin = t0 + d.W + lane;  // position entering the LDS window at this block's end
-            const float in_acc = pin < L ? row[pin] : 0.f;
-            float pend = accw[tl & wmask];
-            float hs = hlane;
-            float ykeep = 0.f;
-            const float xfirst = xcur;
+            float p0 = accw[tl0 & wmask];
+            float p1 = accw[tl1 & wmask];
+            // accumulators of the positions entering the LDS window at this
+            // block's end: independent loads now, summed after the chain
+            const int64_t in0 = t0 + d.W + lane, in1 = in0 + kWave;
+            float lv0[kMaxBufLevels], lv1[kMaxBufLevels];
 #pragma unroll
-            for (int m = 0; m < kWave; ++m) {
-                if constexpr (CLOSED) {
-                    const float ya = __builtin_fmaf(h0, xcur, pend);  // red cell: acc[t] + h[0] x[t]
-                    ykeep = (lane == m) ? ya : ykeep;
-                    const float ym = readlane(ya, m);
-                    pend = __builtin_fmaf(hs, xcur, pend);           // push x[t0+m] into later positions
-                    hs = wave_shr1(hs);
-                    float xn = tanh_fast(ym);
-                    if constexpr (BF16) xn = round_bf16(xn);
-                    xcur = xn;
-                } else {
-                    const float xm = readlane(xb, m);
-                    pend = __builtin_fmaf(hs, xm, pend);
-                    hs = wave_shr1(hs);
+            for (int k = 0; k < kMaxBufLevels; ++k) {
+                const int q = d.lvl_qlo + k;
+                lv0[k] = lv1[k] = 0.f;
+                if (q <= d.lvl_qhi) {
+                    const int64_t U = (int64_t)1 << q;
+                    const FI_GLOBAL float* lq = lvl + d.lvl_off[q];
+                    if (in0 < L && ((in0 >> q) & 1) && (in0 & (U - 1)) >= d.W) lv0[k] = lq[(in0 >> (q + 1)) * U + (in0 & (U - 1))];
+                    if (in1 < L && ((in1 >> q) & 1) && (in1 & (U - 1)) >= d.W) lv1[k] = lq[(in1 >> (q + 1)) * U + (in1 & (U - 1))];
                 }
             }
-            // Lane m's accumulator stopped changing at step m (later pushes
-            // carry a zero tap there), so pend now holds what step m saw.
-            float xkeep;
+            // the next tile's spectrum and older input block go straight to the
+            // idle LDS FFT region while the chain runs
+            const int64_t inext = t0 + kBlk;
+            const int Un = inext < L ? (int)(inext & -inext) : 0;
+            const bool stage_x = Un > d.T && Un <= 2 * kStageSpecMax;
+            const bool stage_spec = Un > d.T && Un <= kStageSpecMax;
+            FI_SHARED float* xst = reinterpret_cast<FI_SHARED float*>(lbuf + lds_fft_elems(Un));
+            FI_SHARED V4* sst = reinterpret_cast<FI_SHARED V4*>(xst + Un);
+            if (stage_spec) {
+                const FI_GLOBAL V4* sp =
+                    gmem(static_cast<const V4*>(d.spec)) + d.spec_off[ilog2(Un)] + c * (int64_t)Un;
+                for (int k = 0; k < Un; k += kWave)
+                    __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(sp + k + lane), (FI_SHARED void*)(sst + k), 16, 0, 0);
+            }
+            if (stage_x) {
+                for (int k = 0; k < Un - kBlk; k += kWave)
+                    __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(row + (inext - Un) + k + lane),
+                                                     (FI_SHARED void*)(xst + k), 4, 0, 0);
+            }
+            const FI_SHARED float* hz0 = hz + kBlk + lane;   // hz0[-m]: tap of lag lane-m
+            float xk0, xk1;
             if constexpr (CLOSED) {
-                // x[t0+m] for m >= 1 is the feedback of y[t0+m-1]: the same
-                // instructions on the same values as in the chain above
-                float tx = tanh_fast(ykeep);
-                if constexpr (BF16) tx = round_bf16(tx);
-                xkeep = wave_shr1(tx);
-                if (lane == 0) xkeep = xfirst;
+                // The accumulators run in units of 2 log2(e) (the taps hz are
+                // c h, c = 2 log2 e), so the feedback of position t is
+                // x = 1 - 2 r with r = 1 / (1 + 2^q[t]); pushing x = 1 - 2r as
+                // q += c h - 2 c h r leaves one fma after r on the serial path:
+                // push -> read lane -> exp2 -> add -> rcp.
+                float q0 = p0 * kTanhScale, q1 = p1 * kTanhScale;
+                xk0 = xcur;   // lane 0: x[t0]
+                xk1 = 0.f;
+                float r = 0.f;
+#pragma unroll
+                for (int m = 0; m < kBlk; ++m) {
+                    if (m == 0 || BF16) {   // push the stored x itself
+                        if (m < kWave) {
+                            q0 = __builtin_fmaf(hz0[-m], xcur, q0);
+                            q1 = __builtin_fmaf(hz0[kWave - m], xcur, q1);
+                        } else {
+                            q1 = __builtin_fmaf(hz0[kWave - m], xcur, q1);
+                        }
+                    } else {                // x = 1 - 2r
+                        if (m < kWave) {
+                            const float t0v = hz0[-m], t1v = hz0[kWave - m];
+                            q0 = __builtin_fmaf(-2.0f * t0v, r, q0 + t0v);
+                            q1 = __builtin_fmaf(-2.0f * t1v, r, q1 + t1v);
+                        } else {
+                            const float t1v = hz0[kWave - m];
+                            q1 = __builtin_fmaf(-2.0f * t1v, r, q1 + t1v);
+                        }
+                    }
+                    r = tanh_rcp_scaled(m < kWave ? readlane(q0, m) : readlane(q1, m - kWave));
+                    xcur = __builtin_fmaf(-2.0f, r, 1.0f);
+                    if constexpr (BF16) xcur = round_bf16(xcur);
+                    if (m + 1 < kWave) xk0 = (lane == m + 1) ? xcur : xk0;
+                    else if (m + 1 < kBlk) xk1 = (lane == m + 1 - kWave) ? xcur : xk1;
+                }
+                p0 = q0 * (1.0f / kTanhScale);
+                p1 = q1 * (1.0f / kTanhScale);
             } else {
-                xkeep = xb;
-                ykeep = __builtin_fmaf(h0, xb, pend);
+#pragma unroll
+                for (int m = 0; m < kBlk; ++m) {
+                    const float xm = m < kWave ? readlane(xb0, m) : readlane(xb1, m - kWave);
+                    if (m < kWave) {
+                        p0 = __builtin_fmaf(hz0[-m], xm, p0);
+                        p1 = __builtin_fmaf(hz0[kWave - m], xm, p1);
+                    } else {
+                        p1 = __builtin_fmaf(hz0[kWave - m], xm, p1);
+                    }
+                }
+                xk0 = xb0;
+                xk1 = xb1;
             }
-            if (tl < L) {
-                const int64_t o = (b * L + tl) * D + c;
-                a.y[o] = ykeep;
-                if (a.x_out) store_io<BF16>(a.x_out, o, xkeep);
-                row[tl] = xkeep;  // the slot of a consumed accumulator now holds x
+            float acc_in0 = 0.f, acc_in1 = 0.f;
+#pragma unroll
+            for (int k = 0; k < kMaxBufLevels; ++k) {
+                acc_in0 += lv0[k];
+                acc_in1 += lv1[k];
             }
-            xring[tl & xmask] = xkeep;
-            accw[tl & wmask] = in_acc;  // slot of position tl now holds position tl + W
-            __syncthreads();
-            const int64_t i = t0 + kWave;
+            // p0, p1 now hold y of the block (lane m's accumulator stopped
+            // changing at step m: later pushes carry a zero tap there)
+            if (tl0 < L) {
+                const int64_t o = (b * L + tl0) * D + c;
+                yout[o] = p0;
+                if (a.x_out) store_io<BF16>(a.x_out, o, xk0);
+                row[tl0] = xk0;  // the slot of a consumed accumulator now holds x
+            }
+            if (tl1 < L) {
+                const int64_t o = (b * L + tl1) * D + c;
+                yout[o] = p1;
+                if (a.x_out) store_io<BF16>(a.x_out, o, xk1);
+                row[tl1] = xk1;
+            }
+            if (direct) {
+                xring[tl0 & xmask] = xk0;
+                xring[tl1 & xmask] = xk1;
+            }
+            if (stage_x) {   // this block's x completes the staged input block
+                xst[Un - kBlk + lane] = xk0;
+                xst[Un - kWave + lane] = xk1;
+            }
+            accw[tl0 & wmask] = acc_in0;  // slot of position t now holds position t + W
+            accw[tl1 & wmask] = acc_in1;
+            wave_sync();
+            const int64_t i = t0 + kBlk;
             if (i < L) {
                 const int U = (int)(i & -i);
                 if (U <= d.T) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
                 } else {
-                    TileSink s{row, accw, i + d.W, wmask, L};
-                    const float4* spec = static_cast<const float4*>(d.spec) + d.spec_off[ilog2(U)] + c * (int64_t)U;
-                    fft_tile(U, i, row, spec, lbuf, sc, tw, s);
+                    const int q = ilog2(U);
+                    TileSink s{row, accw, i + d.W, wmask, L,
+                               d.lvl_off[q] >= 0 ? lvl + d.lvl_off[q] + (i >> (q + 1)) * U : nullptr};
+                    const FI_GLOBAL V4* spec =
+                        gmem(static_cast<const V4*>(d.spec)) + d.spec_off[q] + c * (int64_t)U;
+                    if (stage_x) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged loads landed
+                    fft_tile(U, i, row, spec, lbuf, sc, tw, twl, s, stage_x ? xst : nullptr,
+                             stage_spec ? sst : nullptr);
                 }
+                wave_sync();
             }
-            __syncthreads();
         }
     }
 }
@@ -452,9 +757,10 @@ hipError_t launch_spectra(const DevState& d, int q, void* scd, int64_t scd_strid
                           const void* twd, hipStream_t st) {
     const int M = 1 << q;
     const int F = M < kLdsFftMax ? M : kLdsFftMax;
-    const size_t lds = (size_t)F * sizeof(Cx<double>);
+    const size_t lds = (size_t)lds_fft_elems(F) * sizeof(Cx<double>);
+    if (lds > 65536) (void)hipFuncSetAttribute((const void*)k_spectra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     const int grid = (int)(d.D < slots ? d.D : slots);
-    float4* spec = static_cast<float4*>(d.spec) + d.spec_off[q];
+    V4* spec = static_cast<V4*>(d.spec) + d.spec_off[q];
     hipLaunchKernelGGL(k_spectra, dim3(grid), dim3(64), lds, st, d.hT, d.LS, d.L, d.D, M, spec,
                        static_cast<Cx<double>*>(scd), scd_stride, static_cast<const Cx<double>*>(twd));
     return hipGetLastError();
@@ -472,7 +778,7 @@ hipError_t launch_step(const DevState& d, int64_t t, const void* x_t, float* y_t
     return hipGetLastError();
 }
 
-int tile_fft_lds_bytes() { return kLdsFftMax * (int)sizeof(Cx<float>); }
+int tile_fft_lds_bytes() { return (lds_fft_elems(kLdsFftMax) + 128) * (int)sizeof(Cx<float>); }
 
 hipError_t launch_tile(const DevState& d, int64_t i, hipStream_t st) {
     const int U = (int)(i & -i);
@@ -482,14 +788,12 @@ hipError_t launch_tile(const DevState& d, int64_t i, hipStream_t st) {
     } else {
         const int F = U < kLdsFftMax ? U : kLdsFftMax;
         const int grid = (int)(d.C < d.sc_slots ? d.C : d.sc_slots);
-        hipLaunchKernelGGL(k_tile_fft, dim3(grid), dim3(64), (size_t)F * sizeof(Cx<float>), st, d, i, U);
+        hipLaunchKernelGGL(k_tile_fft, dim3(grid), dim3(64), (size_t)(lds_fft_elems(F) + 128) * sizeof(Cx<float>), st, d, i, U);
     }
     return hipGetLastError();
 }
 
-int run_lds_bytes(const DevState& d) {
-    return d.F * (int)sizeof(Cx<float>) + (d.W + d.XR + 2 * d.T) * (int)sizeof(float);
-}
+int run_lds_bytes(const DevState& d) { return run_lds_floats(d) * (int)sizeof(float); }
 
 int run_max_blocks_per_cu(const DevState& d, int closed) {
     int nb = 0;

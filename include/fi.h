@@ -70,8 +70,9 @@ typedef struct {
     int64_t D;               /* channels per row, >= 1 */
     int64_t L;               /* positions = filter length, >= 1 (any value; tiles clip to < L) */
     int32_t io_dtype;        /* FI_F32 or FI_BF16 */
-    int32_t small_tile_max;  /* T: largest tile side done as a direct product; 0 = default (128);
-                                otherwise a power of two in [64, 4096] */
+    int32_t small_tile_max;  /* T: largest tile side done as a direct product; 0 = default (64:
+                                every tile of side >= 128 is an FFT tile); otherwise 64, 128
+                                or 256 */
     void *stream;            /* hipStream_t the handle works on; NULL = the null stream */
 } fi_config;
 

@@ -48,7 +48,7 @@ def _create_status(cfg, h=0x1000):
 @pytest.mark.parametrize("kw", [
     dict(B=0, D=4, L=16), dict(B=1, D=0, L=16), dict(B=1, D=4, L=0), dict(B=-1, D=4, L=16),
     dict(B=1, D=4, L=16, io_dtype=2), dict(B=1, D=4, L=16, small_tile_max=96),
-    dict(B=1, D=4, L=16, small_tile_max=32), dict(B=1, D=4, L=16, small_tile_max=8192),
+    dict(B=1, D=4, L=16, small_tile_max=32), dict(B=1, D=4, L=16, small_tile_max=512),
     dict(B=1 << 31, D=4, L=16), dict(B=1 << 20, D=1 << 20, L=1 << 20),
 ])
 def test_create_rejects_invalid(kw):

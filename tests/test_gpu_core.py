@@ -82,7 +82,7 @@ def test_ragged_lengths_open(L, T):
         assert rel_l2(ys, ref) <= 1e-5
 
 
-@pytest.mark.parametrize("T", [64, 128, 512])
+@pytest.mark.parametrize("T", [64, 128, 256])
 def test_delta_filters_hit_every_level(T):
     """h = delta_k gives y[t] = x[t-k]; one k per channel, chosen on and
     around every tile side, so every level's kernel moves data exactly once."""
@@ -108,11 +108,11 @@ def test_delta_filters_hit_every_level(T):
         assert np.array_equal(y[0, :first_fft, c], ref[:first_fft].astype(np.float32)), k
 
 
-@pytest.mark.parametrize("T", [128, 4096])
-def test_integer_data(T):
+@pytest.mark.parametrize("L,T", [(8192, 128), (512, 256)])
+def test_integer_data(L, T):
     """x, h in {-3..3}: direct tiles are exact; FFT tiles round to the exact
     integer (|y| < 2^24)."""
-    L, D, B = 8192, 4, 2
+    D, B = 4, 2
     r = np.random.default_rng(9)
     h = r.integers(-3, 4, size=(L, D)).astype(np.float32)
     x = r.integers(-3, 4, size=(B, L, D)).astype(np.float32)
@@ -122,7 +122,7 @@ def test_integer_data(T):
     ref = orc().conv_open(h, x)
     assert np.array_equal(np.rint(y), ref)
     assert np.abs(y - ref).max() < 0.05
-    if T == 4096:   # every tile direct (largest tile side is 4096)
+    if L <= 2 * T:   # every tile direct (the largest tile side is L/2)
         assert np.array_equal(y, ref)
 
 
