@@ -78,6 +78,71 @@ def load_traffic(sha: str, launches_per_step: int = 1):
     return t.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(path: str, kernel_regex: str):
+    """Per-dispatch counter values (summed over counters named in the file) of
+    the kernels whose name matches kernel_regex, from a rocprofv3 --pmc csv
+    output directory (or one *counter_collection.csv file)."""
+    import csv
+    import glob
+    import re
+    files = [path] if path.endswith(".csv") else \
+        sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    per = {}
+    pat = re.compile(kernel_regex)
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                if pat.search(r["Kernel_Name"]):
+                    key = (fn, r.get("Dispatch_Id") or r.get("Correlation_Id"))
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch of a kernel matching {kernel_regex!r} in {path}")
+    return list(per.values())
+
+
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, command):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, in KiB per
+    dispatch, of k_run and of a plain copy of copy_mib MiB) into HBM bytes per
+    k_run launch, each counter scaled by what it reads for the copy."""
+    mean = lambda v: sum(v) / len(v)
+    nbytes = copy_mib * (1 << 20)
+    kf = mean(_counter_rows(fetch_dir, r"k_run"))
+    kw = mean(_counter_rows(write_dir, r"k_run"))
+    cf = mean(_counter_rows(copy_fetch_dir, r"neg"))
+    cw = mean(_counter_rows(copy_write_dir, r"neg"))
+    f_scale = nbytes / (cf * 1024.0)
+    w_scale = nbytes / (cw * 1024.0)
+    out = {"kernel": "k_run", "workload": "hyena-d1024-l16k", "kernel_source_sha": kernel_source_sha(),
+           "fetch_kib_per_launch": kf, "write_kib_per_launch": kw,
+           "copy_bytes": nbytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_read_bytes_per_launch": round(kf * 1024.0 * f_scale),
+           "hbm_write_bytes_per_launch": round(kw * 1024.0 * w_scale),
+           "command": command}
+    out["hbm_bytes_per_launch"] = out["hbm_read_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+    return 0
+
+
+def copy_probe(mib: int, reps: int = 5) -> int:
+    """A plain elementwise copy (y = -x) of mib MiB: the known-size kernel the
+    counter runs are calibrated against."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "reps": reps}), flush=True)
+    return 0
+
+
 def cpu_baseline(w, h, x0, nch: int):
     import oracle
     orc = oracle.default()
@@ -101,13 +166,24 @@ def main() -> int:
     ap.add_argument("--small-tile-max", type=int, default=0)
     ap.add_argument("--cpu-channels", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=5,
+                    metavar=("K_FETCH", "K_WRITE", "COPY_FETCH", "COPY_WRITE", "COPY_MIB"),
+                    help="host only: rocprofv3 --pmc output dirs -> the traffic summary")
+    ap.add_argument("--traffic-command", default="", help="recorded with --write-traffic")
     args = ap.parse_args()
+    if args.write_traffic:
+        a = args.write_traffic
+        return write_traffic(a[0], a[1], a[2], a[3], int(a[4]), args.traffic_command)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): the path shards "
               "over channels with no per-step communication, so a multi-GPU figure is not produced here.",
               file=sys.stderr)
         return 2
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
 
     import numpy as np
     import torch
@@ -116,7 +192,7 @@ def main() -> int:
     import workloads
 
     w = workloads.get(args.workload)
-    T = args.small_tile_max or 128
+    T = args.small_tile_max or fi.FI_DEFAULT_SMALL_TILE_MAX
     closed = "closed" in w.modes[0]
     progress(f"bench: workload {w.name} B={w.B} D={w.D} L={w.L} {w.dtype} closed={closed}")
     torch.cuda.set_device(0)
@@ -182,9 +258,9 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "D": w.D, "L": w.L,
+        "config": {"workload": w.name, "B": w.B, "D": w.D, "L": w.L, "io_dtype": w.dtype,
                    "mode": "closed-loop tanh" if closed else "open loop", "small_tile_max": T,
                    "create_ms": round(create_ms, 1)},
         "roofline": roofline, "cpu_baseline": cpu,

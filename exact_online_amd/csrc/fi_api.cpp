@@ -166,7 +166,7 @@ int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
     if (!cfg || !h || !out) return FI_ERR_INVALID;
     if (cfg->B < 1 || cfg->D < 1 || cfg->L < 1) return FI_ERR_INVALID;
     if (cfg->io_dtype != FI_F32 && cfg->io_dtype != FI_BF16) return FI_ERR_INVALID;
-    int T = cfg->small_tile_max == 0 ? 64 : cfg->small_tile_max;
+    int T = cfg->small_tile_max == 0 ? FI_DEFAULT_SMALL_TILE_MAX : cfg->small_tile_max;
     if (!is_pow2(T) || T < 64 || T > 256) return FI_ERR_INVALID;
     // sizes: every element count must fit comfortably in int64 and the
     // per-channel position index in int32 kernels' loop bounds

@@ -65,14 +65,17 @@ enum {
     FI_ERR_UNSUPPORTED = -5   /* valid but not supported (e.g. no gfx950 device) */
 };
 
+/* small_tile_max used when the config leaves it 0 */
+#define FI_DEFAULT_SMALL_TILE_MAX 64
+
 typedef struct {
     int64_t B;               /* batch rows, >= 1 */
     int64_t D;               /* channels per row, >= 1 */
     int64_t L;               /* positions = filter length, >= 1 (any value; tiles clip to < L) */
     int32_t io_dtype;        /* FI_F32 or FI_BF16 */
-    int32_t small_tile_max;  /* T: largest tile side done as a direct product; 0 = default (64:
-                                every tile of side >= 128 is an FFT tile); otherwise 64, 128
-                                or 256 */
+    int32_t small_tile_max;  /* T: largest tile side done as a direct product; 0 = FI_DEFAULT_SMALL_TILE_MAX
+                                (every tile of side >= 128 is then an FFT tile);
+                                otherwise 64, 128 or 256 */
     void *stream;            /* hipStream_t the handle works on; NULL = the null stream */
 } fi_config;
 
