@@ -23,6 +23,7 @@ __all__ = [
 FI_F32, FI_BF16 = 0, 1
 FI_FEEDBACK_NONE, FI_FEEDBACK_TANH = 0, 1
 FI_DEFAULT_SMALL_TILE_MAX = 64
+FI_MAX_L = 1 << 25
 FI_OK, FI_ERR_INVALID, FI_ERR_NOMEM, FI_ERR_HIP, FI_ERR_STATE, FI_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 
 LIB_PATH = Path(__file__).resolve().parent / "libfi.so"

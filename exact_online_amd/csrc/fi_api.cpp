@@ -122,22 +122,23 @@ int build(fi_handle *s, const void *h) {
     d.sc_slots = slots;
     d.sc_stride = d.umax_fft > fi::kLdsFftMax ? d.umax_fft : 0;
     if (d.sc_stride > 0) FI_HIP(dalloc(&d.scratch, (size_t)(slots * d.sc_stride) * 8));
-    // level buffers (persistent pass): FFT levels whose tiles reach past the
-    // LDS window, L/2 + U floats per channel each (positions with bit q set)
+    // level buffers (persistent pass): U floats per FFT level whose tiles
+    // reach past the LDS window, per resident wavefront
     d.lvl_qlo = fi::kMaxLevels;
     d.lvl_qhi = -1;
-    int64_t lvl_per_ch = 0;
+    int64_t lvl_per_slot = 0;
     for (int q = 0; q < fi::kMaxLevels; ++q) {
         d.lvl_off[q] = -1;
         const int64_t U = (int64_t)1 << q;
         if (d.spec_off[q] < 0 || U <= d.W) continue;
-        d.lvl_off[q] = lvl_per_ch;
-        lvl_per_ch += (d.LS / 2 + U + 63) / 64 * 64;
+        d.lvl_off[q] = lvl_per_slot;
+        lvl_per_slot += (U + 63) / 64 * 64;
         if (q < d.lvl_qlo) d.lvl_qlo = q;
         d.lvl_qhi = q;
     }
-    d.lvl_stride = lvl_per_ch;
-    if (lvl_per_ch > 0) FI_HIP(dalloc(&d.lvl, (size_t)(d.C * lvl_per_ch) * sizeof(float)));
+    if (d.lvl_qhi - d.lvl_qlo + 1 > fi::kMaxBufLevels) return FI_ERR_UNSUPPORTED;
+    d.lvl_stride = lvl_per_slot;
+    if (lvl_per_slot > 0) FI_HIP(dalloc(&d.lvl, (size_t)(slots * lvl_per_slot) * sizeof(float)));
 
     FI_HIP(fi::launch_transpose(d, h, st));
     void *twd = nullptr;
@@ -172,6 +173,7 @@ int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
     // per-channel position index in int32 kernels' loop bounds
     const int64_t lim = (int64_t)1 << 31;
     if (cfg->B >= lim || cfg->D >= lim || cfg->L >= lim) return FI_ERR_INVALID;
+    if (cfg->L > FI_MAX_L) return FI_ERR_UNSUPPORTED;
     const int64_t LS = (cfg->L + 63) / 64 * 64;
     const int64_t C = cfg->B * cfg->D;
     if (C >= lim || (C > 0 && LS > ((int64_t)1 << 46) / C)) return FI_ERR_INVALID;

@@ -42,16 +42,19 @@ __device__ __forceinline__ int ilog2(int64_t v) { return 63 - __builtin_clzll((u
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_transpose(const void* h, float* hT, int64_t L, int64_t D, int64_t LS) {
     __shared__ float tile[64][65];
-    const int64_t c0 = (int64_t)blockIdx.x * 64, j0 = (int64_t)blockIdx.y * 64;
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
-    for (int r = ty; r < 64; r += 4) {
-        const int64_t j = j0 + r, c = c0 + tx;
-        tile[r][tx] = (j < L && c < D) ? load_io<BF16>(h, j * D + c) : 0.f;
-    }
-    __syncthreads();
-    for (int r = ty; r < 64; r += 4) {
-        const int64_t c = c0 + r, j = j0 + tx;
-        if (c < D && j < LS) hT[c * LS + j] = tile[tx][r];
+    for (int64_t j0 = (int64_t)blockIdx.y * 64; j0 < LS; j0 += (int64_t)gridDim.y * 64) {
+        for (int r = ty; r < 64; r += 4) {
+            const int64_t j = j0 + r, c = c0 + tx;
+            tile[r][tx] = (j < L && c < D) ? load_io<BF16>(h, j * D + c) : 0.f;
+        }
+        __syncthreads();
+        for (int r = ty; r < 64; r += 4) {
+            const int64_t c = c0 + r, j = j0 + tx;
+            if (c < D && j < LS) hT[c * LS + j] = tile[tx][r];
+        }
+        __syncthreads();
     }
 }
 
@@ -502,7 +505,6 @@ __global__ __launch_bounds__(64) void k_tile_fft(DevState d, int64_t i, int U) {
 // (and whose tile left p outside the ring).  The channel's global row holds
 // the input history x, from which the FFT tiles read their input blocks.
 constexpr int kBlk = 128;
-constexpr int kMaxBufLevels = 16;    // level buffers summed per position (levels 9 .. 24)
 constexpr int kStageSpecMax = 1024;  // tiles up to this side get spectrum and input staged in LDS
 // (FFT buffer 9M bytes + input 4U + spectrum 16U fits the 36 KiB region for
 // U <= 1024; U = 2048 stages the input only)
@@ -558,13 +560,13 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     TwPtr<float> tw = gmem(static_cast<const Cx<float>*>(d.twf));
     FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)bid * d.sc_stride;
     FI_GLOBAL float* yout = gmem(a.y);
+    FI_GLOBAL float* lvl = gmem(d.lvl) + (int64_t)bid * d.lvl_stride;
     fill_lds_twiddles(twl);
 
     for (int64_t ch = ch0; ch < d.C; ch += G) {
         const int64_t b = ch / D, c = ch % D;
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         const FI_GLOBAL float* hrow = gmem(d.hT + c * d.LS);
-        FI_GLOBAL float* lvl = gmem(d.lvl) + ch * d.lvl_stride;
         for (int q = lane; q < d.W; q += kWave) accw[q] = 0.f;
         for (int q = lane; q < 2 * kBlk; q += kWave)
             hz[q] = (q >= kBlk && q - kBlk < L) ? (CLOSED ? kTanhScale * hrow[q - kBlk] : hrow[q - kBlk]) : 0.f;
@@ -604,8 +606,8 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                 if (q <= d.lvl_qhi) {
                     const int64_t U = (int64_t)1 << q;
                     const FI_GLOBAL float* lq = lvl + d.lvl_off[q];
-                    if (in0 < L && ((in0 >> q) & 1) && (in0 & (U - 1)) >= d.W) lv0[k] = lq[(in0 >> (q + 1)) * U + (in0 & (U - 1))];
-                    if (in1 < L && ((in1 >> q) & 1) && (in1 & (U - 1)) >= d.W) lv1[k] = lq[(in1 >> (q + 1)) * U + (in1 & (U - 1))];
+                    if (in0 < L && ((in0 >> q) & 1) && (in0 & (U - 1)) >= d.W) lv0[k] = lq[in0 & (U - 1)];
+                    if (in1 < L && ((in1 >> q) & 1) && (in1 & (U - 1)) >= d.W) lv1[k] = lq[in1 & (U - 1)];
                 }
             }
             // the next tile's spectrum and older input block go straight to the
@@ -719,7 +721,7 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                 } else {
                     const int q = ilog2(U);
                     TileSink s{row, accw, i + d.W, wmask, L,
-                               d.lvl_off[q] >= 0 ? lvl + d.lvl_off[q] + (i >> (q + 1)) * U : nullptr};
+                               d.lvl_off[q] >= 0 ? lvl + d.lvl_off[q] : nullptr};
                     const FI_GLOBAL V4* spec =
                         gmem(static_cast<const V4*>(d.spec)) + d.spec_off[q] + c * (int64_t)U;
                     if (stage_x) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged loads landed
@@ -740,7 +742,8 @@ static int grid_for(int64_t n, int block, int cap = 65536) {
 }
 
 hipError_t launch_transpose(const DevState& d, const void* h, hipStream_t st) {
-    dim3 grid((unsigned)((d.D + 63) / 64), (unsigned)((d.LS + 63) / 64));
+    const int64_t gy = (d.LS + 63) / 64;
+    dim3 grid((unsigned)((d.D + 63) / 64), (unsigned)(gy < 32768 ? gy : 32768));
     if (d.io_bf16) hipLaunchKernelGGL((k_transpose<true>), grid, dim3(256), 0, st, h, d.hT, d.L, d.D, d.LS);
     else hipLaunchKernelGGL((k_transpose<false>), grid, dim3(256), 0, st, h, d.hT, d.L, d.D, d.LS);
     return hipGetLastError();

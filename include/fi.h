@@ -65,6 +65,9 @@ enum {
     FI_ERR_UNSUPPORTED = -5   /* valid but not supported (e.g. no gfx950 device) */
 };
 
+/* largest supported L (fi_create returns FI_ERR_UNSUPPORTED beyond it) */
+#define FI_MAX_L (1LL << 25)
+
 /* small_tile_max used when the config leaves it 0 */
 #define FI_DEFAULT_SMALL_TILE_MAX 64
 
@@ -87,6 +90,10 @@ typedef struct {
  * twiddle tables.  Synchronous: returns after the device work finished, so
  * the caller may free h at once.  On success *out receives the handle at
  * position 0; on failure *out is set to NULL and nothing stays allocated.
+ * Errors: FI_ERR_INVALID for a NULL pointer, B, D or L < 1, an unknown dtype
+ * or small_tile_max, or sizes whose element counts overflow; FI_ERR_UNSUPPORTED
+ * for L > FI_MAX_L or when the current device is not gfx950; FI_ERR_NOMEM /
+ * FI_ERR_HIP from the device.
  */
 int fi_create(const fi_config *cfg, const void *h, fi_handle **out);
 

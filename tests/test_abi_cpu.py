@@ -64,6 +64,12 @@ def test_create_rejects_null():
     assert fi.lib.fi_create(ctypes.byref(cfg), 0x1000, None) == fi.FI_ERR_INVALID
 
 
+def test_create_rejects_too_long_filter():
+    # valid sizes beyond the supported length: unsupported, with or without a GPU
+    st, out = _create_status(fi.make_config(1, 4, fi.FI_MAX_L + 1))
+    assert st == fi.FI_ERR_UNSUPPORTED and out is None
+
+
 def test_create_without_gpu_is_unsupported():
     import torch
     if torch.cuda.is_available():
