@@ -89,14 +89,17 @@ int build(fi_handle *s, const void *h) {
     d.F = d.umax_fft > 0 ? (d.umax_fft < fi::kLdsFftMax ? d.umax_fft : fi::kLdsFftMax) : 1;
     // FFT region of the persistent pass: the largest LDS transform, or the
     // staging of a tile's input (4U bytes) and, for U <= 1024, its spectrum
-    // (16U bytes) behind that tile's own transform buffer
+    // (16U bytes) behind that tile's own transform buffer, and in its last
+    // kLvlStageBytes the level-buffer rows being summed while the chain runs
     d.fftreg = fi::lds_fft_elems(d.F) * 8;
+    if (d.fftreg < fi::kLvlStageBytes) d.fftreg = fi::kLvlStageBytes;
     for (int q = 0; q < fi::kMaxLevels; ++q) {
         if (d.spec_off[q] < 0) continue;
         const int U = 1 << q;
         int need = 0;
         if (U <= 1024) need = fi::lds_fft_elems(U) * 8 + 4 * U + 16 * U;
         else if (U <= 2048) need = fi::lds_fft_elems(U) * 8 + 4 * U;
+        need += fi::kLvlStageBytes;
         if (need > d.fftreg) d.fftreg = need;
     }
 
@@ -131,12 +134,14 @@ int build(fi_handle *s, const void *h) {
         d.lvl_off[q] = -1;
         const int64_t U = (int64_t)1 << q;
         if (d.spec_off[q] < 0 || U <= d.W) continue;
-        d.lvl_off[q] = lvl_per_slot;
-        lvl_per_slot += (U + 63) / 64 * 64;
+        d.lvl_off[q] = lvl_per_slot;   // = 2^q - 2^qlo (the kernels rely on it)
+        lvl_per_slot += U;
         if (q < d.lvl_qlo) d.lvl_qlo = q;
         d.lvl_qhi = q;
     }
     if (d.lvl_qhi - d.lvl_qlo + 1 > fi::kMaxBufLevels) return FI_ERR_UNSUPPORTED;
+    for (int q = d.lvl_qlo; q <= d.lvl_qhi; ++q)
+        if (d.lvl_off[q] != ((int64_t)1 << q) - ((int64_t)1 << d.lvl_qlo)) return FI_ERR_HIP;
     d.lvl_stride = lvl_per_slot;
     if (lvl_per_slot > 0) FI_HIP(dalloc(&d.lvl, (size_t)(slots * lvl_per_slot) * sizeof(float)));
 
@@ -199,8 +204,8 @@ int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
     d.C = C;
     d.LS = LS;
     d.T = T;
-    d.W = 256;                  // LDS accumulator ring: >= T and >= the 128-position block
-    d.XR = T >= 128 ? T : 0;    // LDS ring of recent inputs, only for direct tiles (T >= 128)
+    d.W = fi::kRunBlock;        // LDS accumulator ring of the persistent pass: one block
+    d.XR = T >= fi::kRunBlock ? T : 0;   // LDS ring of recent inputs, only for its direct tiles
     d.io_bf16 = cfg->io_dtype == FI_BF16;
     s->stream = static_cast<hipStream_t>(cfg->stream);
     s->pos = 0;

@@ -457,6 +457,10 @@ __device__ __forceinline__ float wave_shr1(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, true));
 }
 
+// Empty asm that takes v in a VGPR and gives it back: the computation of v
+// stays ahead of this point (no instruction is emitted).
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ float readlane(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }

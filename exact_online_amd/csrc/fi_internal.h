@@ -8,7 +8,9 @@
 namespace fi {
 
 constexpr int kMaxLevels = 40;
+constexpr int kRunBlock = 256;     // positions per block of the persistent pass (= its LDS ring W)
 constexpr int kMaxBufLevels = 16;  // level buffers the persistent pass sums per position
+constexpr int kLvlStageBytes = kMaxBufLevels * 64 * 4;  // their LDS rows (end of the FFT region)
 constexpr int kLdsFftMax = 4096;  // largest complex FFT held in LDS (32 KiB in fp32)
 // LDS FFT buffers hold one spare slot per 8 points (bank spreading).
 constexpr int lds_fft_elems(int M) { return M + M / 8; }

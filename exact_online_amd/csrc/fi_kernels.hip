@@ -18,6 +18,8 @@
 //       one wavefront per channel; no grid-wide synchronisation is ever needed
 //       because channels are independent ([FI] "Definizione Specifica di
 //       LCSM": the mixer is a per-channel Hadamard convolution).
+#include <type_traits>
+
 #include "fi_device.hpp"
 #include "fi_internal.h"
 
@@ -487,24 +489,29 @@ __global__ __launch_bounds__(64) void k_tile_fft(DevState d, int64_t i, int U) {
 }
 
 // ============================================================ persistent run
-// One wavefront per channel runs all L positions, in blocks of kBlk = 128
-// positions; lane r holds positions t0+r and t0+64+r in two registers.
-//  * Within a block, the red cells and every tile of side < 128 -- these lie
-//    inside one 128-position block and together cover its lower triangle --
+// One wavefront per channel runs all L positions, in blocks of kBlk = 256
+// positions; lane r holds positions t0 + 64k + r (k < kRegs) in registers.
+//  * Within a block, the red cells and every tile of side < 256 -- these lie
+//    inside one 256-position block and together cover its lower triangle --
 //    run in registers: once x[t] is known it is pushed, times the filter tap
 //    of each lag, into the accumulators of t and of every later position of
 //    the block (lag 0 is the red cell), so the register of position t holds
 //    y[t] when it is read.  The same products reach the same outputs as those
-//    tiles.  Taps come from LDS: hz[128 + j] = h[j], zeros below.
-//  * At each block boundary i = t0+128 the tile of side U = lowbit(i) >= 128
-//    runs: a direct Toeplitz product from LDS when U <= T, else the FFT tile.
-// Accumulators of positions [t0, t0+W) live in an LDS ring.  A tile's outputs
-// beyond it are stored, without accumulation, in its level's buffer: position
-// p gets a tile of side U = 2^q exactly when bit q of p is set, so when p
-// enters the ring its value is the sum of the buffered levels whose bit is set
-// (and whose tile left p outside the ring).  The channel's global row holds
-// the input history x, from which the FFT tiles read their input blocks.
-constexpr int kBlk = 128;
+//    tiles.  Taps come from LDS: hz[kWave + j] = h[j], zeros below (a lane's
+//    lag is never below -63).
+//  * At each block boundary i = t0 + kBlk the tile of side U = lowbit(i) >=
+//    kBlk runs: a direct Toeplitz product from LDS when U <= T, else the FFT
+//    tile.
+// Accumulators of positions [t0, t0+W) (W = kBlk) live in an LDS ring.  A
+// tile's outputs beyond it are stored, without accumulation, in its level's
+// buffer: position p gets a tile of side U = 2^q exactly when bit q of p is
+// set, so when p enters the ring its value is the sum of the buffered levels
+// whose bit is set (and whose tile left p outside the ring).  The channel's
+// global row holds the input history x, from which the FFT tiles read their
+// input blocks.
+constexpr int kRegs = kRunBlock / kWave;   // accumulator registers per lane
+constexpr int kBlk = kRunBlock;
+constexpr int kTapBatch = 4;         // chain: taps loaded per batch, one batch ahead
 constexpr int kStageSpecMax = 1024;  // tiles up to this side get spectrum and input staged in LDS
 // (FFT buffer 9M bytes + input 4U + spectrum 16U fits the 36 KiB region for
 // U <= 1024; U = 2048 stages the input only)
@@ -532,16 +539,45 @@ __device__ __forceinline__ void direct_tile_lds(int64_t i, int U, const FI_SHARE
 // LDS of k_run: static arrays for the tap table, the twiddle table and the
 // accumulator ring (separate objects, so the compiler sees that the direct-to-
 // LDS staging loads into the dynamic region never touch them), and a dynamic
-// region: FFT / staging area [fftreg bytes] | (T >= 128 only) xring[XR] | htap[2T].
-constexpr int kRing = 256;   // accumulator ring W (small_tile_max <= 256)
+// region: FFT / staging area [fftreg bytes] | (T >= kBlk only) xring[XR] | htap[2T].
 inline int run_lds_floats(const DevState& d) { return d.fftreg / 4 + (d.T >= kBlk ? d.XR + 2 * d.T : 0); }
+
+// Level-buffer values of the positions base + 64k + lane entering the ring.
+// Which levels hold a value is the same for the whole block: bits >= 9 of a
+// position are those of the block-aligned base, and level q holds one unless
+// q is base's lowest set bit (that level's tile runs at base itself and puts
+// the block in the ring), so `present` (bit j: level qlo + j) is uniform.
+// Level q's buffer sits at 2^q - 2^qlo in the slot (buffers of U floats,
+// ascending levels).  The values go straight to LDS rows lvst[j][lane]: no
+// register waits on them until they are summed.
+__device__ __forceinline__ void level_loads(const FI_GLOBAL float* lvl, int qlo, uint32_t present, int64_t p,
+                                            FI_SHARED float* lvst) {
+#pragma unroll
+    for (int j = 0; j < kMaxBufLevels; ++j) {
+        if ((present >> j) & 1) {
+            const int64_t U = (int64_t)1 << (qlo + j);
+            __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(lvl + (U - ((int64_t)1 << qlo)) + (p & (U - 1))),
+                                             (FI_SHARED void*)(lvst + kWave * j), 4, 0, 0);
+        }
+    }
+}
+// Sum of the present rows (every row is read; absent ones are masked).
+__device__ __forceinline__ float level_sum(uint32_t present, const FI_SHARED float* lvst, int lane) {
+    float v[kMaxBufLevels];
+#pragma unroll
+    for (int j = 0; j < kMaxBufLevels; ++j) v[j] = lvst[kWave * j + lane];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxBufLevels; ++j) s += ((present >> j) & 1) ? v[j] : 0.f;
+    return s;
+}
 
 template <bool CLOSED, bool BF16>
 __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ Cx<float> s_tw[128];     // twiddles A[64] = w_64^a, B[64] = w_4096^b
-    __shared__ float s_ring[kRing];     // accumulators of positions [t0, t0+W)
-    __shared__ float s_taps[2 * kBlk];  // zeros, then the chain's taps
+    __shared__ float s_ring[kBlk];      // accumulators of positions [t0, t0+W)
+    __shared__ float s_taps[kWave + kBlk];  // 64 zeros, then the chain's taps
     const DevState& d = a.d;
     FI_SHARED Cx<float>* lbuf = smem_ptr(reinterpret_cast<Cx<float>*>(smem));
     FI_SHARED Cx<float>* twl = smem_ptr(s_tw);
@@ -549,9 +585,11 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     FI_SHARED float* hz = smem_ptr(s_taps);
     FI_SHARED float* xring = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.fftreg);  // direct tiles only
     FI_SHARED float* htap = xring + d.XR;    // h[0 .. 2T), direct tiles only
+    // level rows, at the end of the FFT region (idle while the chain runs)
+    FI_SHARED float* lvst = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.fftreg - kLvlStageBytes);
     const bool direct = d.T >= kBlk;
     const int lane = threadIdx.x;
-    const int wmask = d.W - 1, xmask = d.XR - 1;
+    const int wmask = kBlk - 1, xmask = d.XR - 1;
     const int64_t L = d.L, D = d.D;
     const int G = gridDim.x, bid = blockIdx.x;
     // consecutive channels on the same XCD (workgroups go round-robin over
@@ -560,54 +598,51 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     TwPtr<float> tw = gmem(static_cast<const Cx<float>*>(d.twf));
     FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)bid * d.sc_stride;
     FI_GLOBAL float* yout = gmem(a.y);
-    FI_GLOBAL float* lvl = gmem(d.lvl) + (int64_t)bid * d.lvl_stride;
+    const FI_GLOBAL float* lvl = gmem(d.lvl) + (int64_t)bid * d.lvl_stride;
+    FI_GLOBAL float* lvlw = gmem(d.lvl) + (int64_t)bid * d.lvl_stride;
     fill_lds_twiddles(twl);
 
     for (int64_t ch = ch0; ch < d.C; ch += G) {
         const int64_t b = ch / D, c = ch % D;
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         const FI_GLOBAL float* hrow = gmem(d.hT + c * d.LS);
-        for (int q = lane; q < d.W; q += kWave) accw[q] = 0.f;
-        for (int q = lane; q < 2 * kBlk; q += kWave)
-            hz[q] = (q >= kBlk && q - kBlk < L) ? (CLOSED ? kTanhScale * hrow[q - kBlk] : hrow[q - kBlk]) : 0.f;
+        for (int q = lane; q < kBlk; q += kWave) accw[q] = 0.f;
+        for (int q = lane; q < kWave + kBlk; q += kWave)
+            hz[q] = (q >= kWave && q - kWave < L) ? (CLOSED ? kTanhScale * hrow[q - kWave] : hrow[q - kWave]) : 0.f;
         if (direct)
             for (int q = lane; q < 2 * d.T; q += kWave) htap[q] = q < L ? hrow[q] : 0.f;
         wave_sync();
+        const float ch0v = hz[kWave];   // closed loop: c h[0]
 
-        float xcur = 0.f;   // closed loop: x at the next position (uniform)
-        float xb0n = 0.f, xb1n = 0.f;      // open loop: inputs of the next block
+        float xcur = 0.f;        // closed loop: x at the next position (uniform)
+        float xbn[kRegs];        // open loop: inputs of the next block
+#pragma unroll
+        for (int k = 0; k < kRegs; ++k) xbn[k] = 0.f;
         if constexpr (CLOSED) {
             xcur = load_io<BF16>(a.x_in, b * D + c);
         } else {
-            xb0n = lane < L ? load_io<BF16>(a.x_in, (b * L + lane) * D + c) : 0.f;
-            xb1n = lane + kWave < L ? load_io<BF16>(a.x_in, (b * L + lane + kWave) * D + c) : 0.f;
+#pragma unroll
+            for (int k = 0; k < kRegs; ++k) {
+                const int64_t n = kWave * k + lane;
+                if (n < L) xbn[k] = load_io<BF16>(a.x_in, (b * L + n) * D + c);
+            }
         }
         // nothing in flight when the block loop starts, so the waits inside it
         // only cover what each block issues
         __builtin_amdgcn_s_waitcnt(0x0F70);
         for (int64_t t0 = 0; t0 < L; t0 += kBlk) {
-            const int64_t tl0 = t0 + lane, tl1 = t0 + kWave + lane;
-            const float xb0 = xb0n, xb1 = xb1n;
-            if constexpr (!CLOSED) {
-                const int64_t n0 = tl0 + kBlk, n1 = tl1 + kBlk;
-                xb0n = n0 < L ? load_io<BF16>(a.x_in, (b * L + n0) * D + c) : 0.f;
-                xb1n = n1 < L ? load_io<BF16>(a.x_in, (b * L + n1) * D + c) : 0.f;
-            }
-            float p0 = accw[tl0 & wmask];
-            float p1 = accw[tl1 & wmask];
-            // accumulators of the positions entering the LDS window at this
-            // block's end: independent loads now, summed after the chain
-            const int64_t in0 = t0 + d.W + lane, in1 = in0 + kWave;
-            float lv0[kMaxBufLevels], lv1[kMaxBufLevels];
+            float xb[kRegs], p[kRegs], xk[kRegs], acc_in[kRegs];
 #pragma unroll
-            for (int k = 0; k < kMaxBufLevels; ++k) {
-                const int q = d.lvl_qlo + k;
-                lv0[k] = lv1[k] = 0.f;
-                if (q <= d.lvl_qhi) {
-                    const int64_t U = (int64_t)1 << q;
-                    const FI_GLOBAL float* lq = lvl + d.lvl_off[q];
-                    if (in0 < L && ((in0 >> q) & 1) && (in0 & (U - 1)) >= d.W) lv0[k] = lq[in0 & (U - 1)];
-                    if (in1 < L && ((in1 >> q) & 1) && (in1 & (U - 1)) >= d.W) lv1[k] = lq[in1 & (U - 1)];
+            for (int k = 0; k < kRegs; ++k) {
+                xb[k] = xbn[k];
+                p[k] = accw[(kWave * k + lane) & wmask];   // t0 is a multiple of the ring size
+                acc_in[k] = 0.f;
+            }
+            if constexpr (!CLOSED) {
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) {
+                    const int64_t n = t0 + kBlk + kWave * k + lane;
+                    xbn[k] = n < L ? load_io<BF16>(a.x_in, (b * L + n) * D + c) : 0.f;
                 }
             }
             // the next tile's spectrum and older input block go straight to the
@@ -629,89 +664,118 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(row + (inext - Un) + k + lane),
                                                      (FI_SHARED void*)(xst + k), 4, 0, 0);
             }
-            const FI_SHARED float* hz0 = hz + kBlk + lane;   // hz0[-m]: tap of lag lane-m
-            float xk0, xk1;
-            if constexpr (CLOSED) {
-                // The accumulators run in units of 2 log2(e) (the taps hz are
-                // c h, c = 2 log2 e), so the feedback of position t is
-                // x = 1 - 2 r with r = 1 / (1 + 2^q[t]); pushing x = 1 - 2r as
-                // q += c h - 2 c h r leaves one fma after r on the serial path:
-                // push -> read lane -> exp2 -> add -> rcp.
-                float q0 = p0 * kTanhScale, q1 = p1 * kTanhScale;
-                xk0 = xcur;   // lane 0: x[t0]
-                xk1 = 0.f;
-                float r = 0.f;
+            // Chain over the block.  The level-buffer values of the positions
+            // entering the ring at the block's end are loaded one register row
+            // at a time (row k at step 64k, summed 64 steps later), so they
+            // arrive while the chain runs.
+            const int64_t base = t0 + kBlk;
+            uint32_t present = 0;   // level qlo + j holds values for this block
+            if (d.lvl_qhi >= d.lvl_qlo) {
+                const int nq = d.lvl_qhi - d.lvl_qlo + 1;
+                const uint64_t bits = ((uint64_t)base & ~((uint64_t)base & (0 - (uint64_t)base))) >> d.lvl_qlo;
+                present = (uint32_t)(bits & ((1ull << nq) - 1));
+            }
+            const FI_SHARED float* hz0 = hz + kWave + lane;   // hz0[64k - m]: tap of position 64k + lane, input m
+            float ta[kRegs][2 * kTapBatch];
 #pragma unroll
-                for (int m = 0; m < kBlk; ++m) {
-                    if (m == 0 || BF16) {   // push the stored x itself
-                        if (m < kWave) {
-                            q0 = __builtin_fmaf(hz0[-m], xcur, q0);
-                            q1 = __builtin_fmaf(hz0[kWave - m], xcur, q1);
-                        } else {
-                            q1 = __builtin_fmaf(hz0[kWave - m], xcur, q1);
-                        }
-                    } else {                // x = 1 - 2r
-                        if (m < kWave) {
-                            const float t0v = hz0[-m], t1v = hz0[kWave - m];
-                            q0 = __builtin_fmaf(-2.0f * t0v, r, q0 + t0v);
-                            q1 = __builtin_fmaf(-2.0f * t1v, r, q1 + t1v);
-                        } else {
-                            const float t1v = hz0[kWave - m];
-                            q1 = __builtin_fmaf(-2.0f * t1v, r, q1 + t1v);
+            for (int n = 0; n < kTapBatch; ++n)
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) ta[k][n] = hz0[kWave * k - n];
+            float v = 0.f;
+            float xstart = 0.f;
+            if constexpr (CLOSED) {
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) p[k] *= kTanhScale;
+                v = readlane(p[0], 0);
+                xstart = xcur;
+            }
+            // one 64-step segment of the chain (steps 64K .. 64K+63)
+            auto segment = [&](auto kc) {
+                constexpr int K = decltype(kc)::value;
+                level_loads(lvl, d.lvl_qlo, present, base + kWave * K + lane, lvst);
+#pragma unroll
+                for (int m2 = 0; m2 < kWave; ++m2) {
+                    const int m = kWave * K + m2;
+                    float tv[kRegs];
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) tv[k] = ta[k][m % (2 * kTapBatch)];
+                    // closed loop: the accumulators run in units of c = 2 log2(e)
+                    // (the taps hz are c h), so tanh(y) = 1 - 2 r with
+                    // r = 1 / (1 + 2^(c y)); v holds position t0+m's accumulator
+                    // with every input but its own pushed (read one step ahead,
+                    // off the serial path), and the serial path of a position is
+                    // c y = v + c h[0] x, exp2, add, rcp, x = 1 - 2 r.  Position
+                    // m's own lag-0 push is the same fma as c y, so its register
+                    // ends equal to it.
+                    const float xm = CLOSED ? xcur : readlane(xb[K], m2);
+                    const float cy = __builtin_fmaf(ch0v, xm, v);
+#pragma unroll
+                    for (int k = K; k < kRegs; ++k) {
+                        p[k] = __builtin_fmaf(tv[k], xm, p[k]);
+                        pin(p[k]);   // push now: x[t] is then dead after this step
+                    }
+                    if (m % kTapBatch == 0 && m + kTapBatch < kBlk) {
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int n2 = 0; n2 < kTapBatch; ++n2) {
+                            const int n = m + kTapBatch + n2;
+#pragma unroll
+                            for (int k = 0; k < kRegs; ++k)
+                                if (n < kWave * (k + 1)) ta[k][n % (2 * kTapBatch)] = hz0[kWave * k - n];
                         }
                     }
-                    r = tanh_rcp_scaled(m < kWave ? readlane(q0, m) : readlane(q1, m - kWave));
-                    xcur = __builtin_fmaf(-2.0f, r, 1.0f);
-                    if constexpr (BF16) xcur = round_bf16(xcur);
-                    if (m + 1 < kWave) xk0 = (lane == m + 1) ? xcur : xk0;
-                    else if (m + 1 < kBlk) xk1 = (lane == m + 1 - kWave) ? xcur : xk1;
+                    if constexpr (CLOSED) {
+                        if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
+                        xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
+                        if constexpr (BF16) xcur = round_bf16(xcur);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                p0 = q0 * (1.0f / kTanhScale);
-                p1 = q1 * (1.0f / kTanhScale);
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this segment's level rows landed
+                acc_in[K] = base + kWave * K + lane < L ? level_sum(present, lvst, lane) : 0.f;
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): rows read before the next segment refills them
+            };
+            static_assert(kRegs == 4, "the chain below runs four segments");
+            segment(std::integral_constant<int, 0>{});
+            segment(std::integral_constant<int, 1>{});
+            segment(std::integral_constant<int, 2>{});
+            segment(std::integral_constant<int, 3>{});
+            if constexpr (CLOSED) {
+                // The inputs of the block, one per lane: the register of
+                // position t ended as the same fma as the chain's c y[t], so
+                // the same exp2 / rcp / fma on it gives back x[t+1] exactly.
+                float f[kRegs];
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) {
+                    f[k] = __builtin_fmaf(-2.0f, tanh_rcp_scaled(p[k]), 1.0f);
+                    if constexpr (BF16) f[k] = round_bf16(f[k]);
+                }
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) {
+                    const float prev = k == 0 ? xstart : readlane(f[k - 1], kWave - 1);
+                    const float sh = __shfl_up(f[k], 1);
+                    xk[k] = lane == 0 ? prev : sh;
+                    p[k] *= 1.0f / kTanhScale;
+                }
             } else {
 #pragma unroll
-                for (int m = 0; m < kBlk; ++m) {
-                    const float xm = m < kWave ? readlane(xb0, m) : readlane(xb1, m - kWave);
-                    if (m < kWave) {
-                        p0 = __builtin_fmaf(hz0[-m], xm, p0);
-                        p1 = __builtin_fmaf(hz0[kWave - m], xm, p1);
-                    } else {
-                        p1 = __builtin_fmaf(hz0[kWave - m], xm, p1);
-                    }
-                }
-                xk0 = xb0;
-                xk1 = xb1;
+                for (int k = 0; k < kRegs; ++k) xk[k] = xb[k];
             }
-            float acc_in0 = 0.f, acc_in1 = 0.f;
-#pragma unroll
-            for (int k = 0; k < kMaxBufLevels; ++k) {
-                acc_in0 += lv0[k];
-                acc_in1 += lv1[k];
-            }
-            // p0, p1 now hold y of the block (lane m's accumulator stopped
+            // p now holds y of the block (lane m's accumulator stopped
             // changing at step m: later pushes carry a zero tap there)
-            if (tl0 < L) {
-                const int64_t o = (b * L + tl0) * D + c;
-                yout[o] = p0;
-                if (a.x_out) store_io<BF16>(a.x_out, o, xk0);
-                row[tl0] = xk0;  // the slot of a consumed accumulator now holds x
+#pragma unroll
+            for (int k = 0; k < kRegs; ++k) {
+                const int64_t tl = t0 + kWave * k + lane;
+                if (tl < L) {
+                    const int64_t o = (b * L + tl) * D + c;
+                    yout[o] = p[k];
+                    if (a.x_out) store_io<BF16>(a.x_out, o, xk[k]);
+                    row[tl] = xk[k];  // the slot of a consumed accumulator now holds x
+                }
+                if (direct) xring[tl & xmask] = xk[k];
+                if (stage_x) xst[Un - kBlk + kWave * k + lane] = xk[k];   // completes the staged input block
+                accw[(kWave * k + lane) & wmask] = acc_in[k];  // slot of position t now holds position t + W
             }
-            if (tl1 < L) {
-                const int64_t o = (b * L + tl1) * D + c;
-                yout[o] = p1;
-                if (a.x_out) store_io<BF16>(a.x_out, o, xk1);
-                row[tl1] = xk1;
-            }
-            if (direct) {
-                xring[tl0 & xmask] = xk0;
-                xring[tl1 & xmask] = xk1;
-            }
-            if (stage_x) {   // this block's x completes the staged input block
-                xst[Un - kBlk + lane] = xk0;
-                xst[Un - kWave + lane] = xk1;
-            }
-            accw[tl0 & wmask] = acc_in0;  // slot of position t now holds position t + W
-            accw[tl1 & wmask] = acc_in1;
             wave_sync();
             const int64_t i = t0 + kBlk;
             if (i < L) {
@@ -720,8 +784,7 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
                 } else {
                     const int q = ilog2(U);
-                    TileSink s{row, accw, i + d.W, wmask, L,
-                               d.lvl_off[q] >= 0 ? lvl + d.lvl_off[q] : nullptr};
+                    TileSink s{row, accw, i + kBlk, wmask, L, d.lvl_off[q] >= 0 ? lvlw + d.lvl_off[q] : nullptr};
                     const FI_GLOBAL V4* spec =
                         gmem(static_cast<const V4*>(d.spec)) + d.spec_off[q] + c * (int64_t)U;
                     if (stage_x) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged loads landed
