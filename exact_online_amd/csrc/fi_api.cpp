@@ -52,8 +52,6 @@ void free_state(DevState &d) {
     if (d.spec) (void)hipFree(d.spec);
     if (d.twf) (void)hipFree(d.twf);
     if (d.scratch) (void)hipFree(d.scratch);
-    if (d.lvl) (void)hipFree(d.lvl);
-    d.lvl = nullptr;
     d.hT = nullptr;
     d.state = nullptr;
     d.spec = nullptr;
@@ -89,17 +87,14 @@ int build(fi_handle *s, const void *h) {
     d.F = d.umax_fft > 0 ? (d.umax_fft < fi::kLdsFftMax ? d.umax_fft : fi::kLdsFftMax) : 1;
     // FFT region of the persistent pass: the largest LDS transform, or the
     // staging of a tile's input (4U bytes) and, for U <= 1024, its spectrum
-    // (16U bytes) behind that tile's own transform buffer, and in its last
-    // kLvlStageBytes the level-buffer rows being summed while the chain runs
+    // (16U bytes) behind that tile's own transform buffer
     d.fftreg = fi::lds_fft_elems(d.F) * 8;
-    if (d.fftreg < fi::kLvlStageBytes) d.fftreg = fi::kLvlStageBytes;
     for (int q = 0; q < fi::kMaxLevels; ++q) {
         if (d.spec_off[q] < 0) continue;
         const int U = 1 << q;
         int need = 0;
         if (U <= 1024) need = fi::lds_fft_elems(U) * 8 + 4 * U + 16 * U;
         else if (U <= 2048) need = fi::lds_fft_elems(U) * 8 + 4 * U;
-        need += fi::kLvlStageBytes;
         if (need > d.fftreg) d.fftreg = need;
     }
 
@@ -125,25 +120,6 @@ int build(fi_handle *s, const void *h) {
     d.sc_slots = slots;
     d.sc_stride = d.umax_fft > fi::kLdsFftMax ? d.umax_fft : 0;
     if (d.sc_stride > 0) FI_HIP(dalloc(&d.scratch, (size_t)(slots * d.sc_stride) * 8));
-    // level buffers (persistent pass): U floats per FFT level whose tiles
-    // reach past the LDS window, per resident wavefront
-    d.lvl_qlo = fi::kMaxLevels;
-    d.lvl_qhi = -1;
-    int64_t lvl_per_slot = 0;
-    for (int q = 0; q < fi::kMaxLevels; ++q) {
-        d.lvl_off[q] = -1;
-        const int64_t U = (int64_t)1 << q;
-        if (d.spec_off[q] < 0 || U <= d.W) continue;
-        d.lvl_off[q] = lvl_per_slot;   // = 2^q - 2^qlo (the kernels rely on it)
-        lvl_per_slot += U;
-        if (q < d.lvl_qlo) d.lvl_qlo = q;
-        d.lvl_qhi = q;
-    }
-    if (d.lvl_qhi - d.lvl_qlo + 1 > fi::kMaxBufLevels) return FI_ERR_UNSUPPORTED;
-    for (int q = d.lvl_qlo; q <= d.lvl_qhi; ++q)
-        if (d.lvl_off[q] != ((int64_t)1 << q) - ((int64_t)1 << d.lvl_qlo)) return FI_ERR_HIP;
-    d.lvl_stride = lvl_per_slot;
-    if (lvl_per_slot > 0) FI_HIP(dalloc(&d.lvl, (size_t)(slots * lvl_per_slot) * sizeof(float)));
 
     FI_HIP(fi::launch_transpose(d, h, st));
     void *twd = nullptr;

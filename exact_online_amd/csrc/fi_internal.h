@@ -9,8 +9,6 @@ namespace fi {
 
 constexpr int kMaxLevels = 40;
 constexpr int kRunBlock = 256;     // positions per block of the persistent pass (= its LDS ring W)
-constexpr int kMaxBufLevels = 16;  // level buffers the persistent pass sums per position
-constexpr int kLvlStageBytes = kMaxBufLevels * 64 * 4;  // their LDS rows (end of the FFT region)
 constexpr int kLdsFftMax = 4096;  // largest complex FFT held in LDS (32 KiB in fp32)
 // LDS FFT buffers hold one spare slot per 8 points (bank spreading).
 constexpr int lds_fft_elems(int M) { return M + M / 8; }
@@ -46,15 +44,6 @@ struct DevState {
     int64_t sc_stride;     // complex elements per scratch slot
     int64_t sc_slots;
     int umax_fft;          // largest FFT tile side (0 if none)
-    // level buffers of the persistent pass: for each FFT level q with U > W,
-    // per resident wavefront slot k the floats lvl[k*lvl_stride + lvl_off[q]
-    // + (p & (U-1))] hold the output of the latest level-q tile for position p
-    // of the slot's current channel (read before the next level-q tile, 2U
-    // positions later, overwrites it)
-    float *lvl;
-    int64_t lvl_stride;           // floats per slot (all levels)
-    int64_t lvl_off[kMaxLevels];  // float offset of level q within a slot, -1 if none
-    int lvl_qlo, lvl_qhi;         // range of levels with buffers (qlo > qhi: none)
 };
 
 // fi_create helpers (synchronous work on `st`)

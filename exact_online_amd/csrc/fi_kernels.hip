@@ -143,18 +143,17 @@ __global__ void k_zero(float* p, int64_t n) {
 
 // ============================================================== FFT tile
 // Where the outputs of the tile at i go: positions below `wend` into the LDS
-// ring `accw` (slot = position & wmask; none when accw is null).  The others
-// either go with plain stores to the tile's level buffer `lvl` (entry o - i;
-// each position receives at most one tile per level, so nothing accumulates
-// there), or, without a level buffer, are added into the channel's global
-// row.  wend - i is a multiple of 128.
+// ring `accw` (slot = position & wmask; none when accw is null); the others
+// into the channel's global row, added to what earlier tiles left there, or
+// stored when `first` says no earlier tile reached them.  wend - i is a
+// multiple of 128.
 struct TileSink {
     FI_GLOBAL float* row;
     FI_SHARED float* accw;
     int64_t wend;
     int wmask;
     int64_t L;
-    FI_GLOBAL float* lvl;
+    bool first;
 };
 
 // Adds w[m] = (a, b) to positions (i + 2m, i + 2m + 1) for m in [0, n):
@@ -177,12 +176,15 @@ __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n,
             }
         }
     }
-    if (s.lvl) {
+    if (s.first) {
 #pragma unroll 4
         for (int m = m0 + lane; m < n; m += kWave) {
-            if (i + 2 * (int64_t)m < s.L) {
+            const int64_t o = i + 2 * (int64_t)m;
+            if (o + 1 < s.L) {
                 const Cx<float> w = get(m);
-                *reinterpret_cast<FI_GLOBAL V2*>(s.lvl + 2 * m) = V2{w.x, w.y};
+                *reinterpret_cast<FI_GLOBAL V2*>(s.row + o) = V2{w.x, w.y};
+            } else if (o < s.L) {
+                s.row[o] = get(m).x;
             }
         }
         return;
@@ -482,7 +484,7 @@ __global__ __launch_bounds__(64) void k_tile_fft(DevState d, int64_t i, int U) {
     for (int64_t ch = blockIdx.x; ch < d.C; ch += gridDim.x) {
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)blockIdx.x * d.sc_stride;
-        TileSink s{row, nullptr, i, 0, d.L, nullptr};
+        TileSink s{row, nullptr, i, 0, d.L, false};
         fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)U, lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl, s,
                  nullptr, nullptr);
     }
@@ -503,14 +505,15 @@ __global__ __launch_bounds__(64) void k_tile_fft(DevState d, int64_t i, int U) {
 //    kBlk runs: a direct Toeplitz product from LDS when U <= T, else the FFT
 //    tile.
 // Accumulators of positions [t0, t0+W) (W = kBlk) live in an LDS ring.  A
-// tile's outputs beyond it are stored, without accumulation, in its level's
-// buffer: position p gets a tile of side U = 2^q exactly when bit q of p is
-// set, so when p enters the ring its value is the sum of the buffered levels
-// whose bit is set (and whose tile left p outside the ring).  The channel's
-// global row holds the input history x, from which the FFT tiles read their
-// input blocks.
+// tile's outputs beyond it go to the channel's global row, which holds the
+// input history x below the current position (the FFT tiles read their input
+// blocks there) and the accumulated tile outputs above it: the first tile of
+// each level (i = U) stores, later ones add.  A block loads its successor's
+// accumulators from the row while its chain runs.
 constexpr int kRegs = kRunBlock / kWave;   // accumulator registers per lane
 constexpr int kBlk = kRunBlock;
+constexpr int kLog2Blk = 8;
+static_assert((1 << kLog2Blk) == kBlk, "block size");
 constexpr int kTapBatch = 4;         // chain: taps loaded per batch, one batch ahead
 constexpr int kStageSpecMax = 1024;  // tiles up to this side get spectrum and input staged in LDS
 // (FFT buffer 9M bytes + input 4U + spectrum 16U fits the 36 KiB region for
@@ -542,36 +545,6 @@ __device__ __forceinline__ void direct_tile_lds(int64_t i, int U, const FI_SHARE
 // region: FFT / staging area [fftreg bytes] | (T >= kBlk only) xring[XR] | htap[2T].
 inline int run_lds_floats(const DevState& d) { return d.fftreg / 4 + (d.T >= kBlk ? d.XR + 2 * d.T : 0); }
 
-// Level-buffer values of the positions base + 64k + lane entering the ring.
-// Which levels hold a value is the same for the whole block: bits >= 9 of a
-// position are those of the block-aligned base, and level q holds one unless
-// q is base's lowest set bit (that level's tile runs at base itself and puts
-// the block in the ring), so `present` (bit j: level qlo + j) is uniform.
-// Level q's buffer sits at 2^q - 2^qlo in the slot (buffers of U floats,
-// ascending levels).  The values go straight to LDS rows lvst[j][lane]: no
-// register waits on them until they are summed.
-__device__ __forceinline__ void level_loads(const FI_GLOBAL float* lvl, int qlo, uint32_t present, int64_t p,
-                                            FI_SHARED float* lvst) {
-#pragma unroll
-    for (int j = 0; j < kMaxBufLevels; ++j) {
-        if ((present >> j) & 1) {
-            const int64_t U = (int64_t)1 << (qlo + j);
-            __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(lvl + (U - ((int64_t)1 << qlo)) + (p & (U - 1))),
-                                             (FI_SHARED void*)(lvst + kWave * j), 4, 0, 0);
-        }
-    }
-}
-// Sum of the present rows (every row is read; absent ones are masked).
-__device__ __forceinline__ float level_sum(uint32_t present, const FI_SHARED float* lvst, int lane) {
-    float v[kMaxBufLevels];
-#pragma unroll
-    for (int j = 0; j < kMaxBufLevels; ++j) v[j] = lvst[kWave * j + lane];
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxBufLevels; ++j) s += ((present >> j) & 1) ? v[j] : 0.f;
-    return s;
-}
-
 template <bool CLOSED, bool BF16>
 __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -585,8 +558,6 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     FI_SHARED float* hz = smem_ptr(s_taps);
     FI_SHARED float* xring = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.fftreg);  // direct tiles only
     FI_SHARED float* htap = xring + d.XR;    // h[0 .. 2T), direct tiles only
-    // level rows, at the end of the FFT region (idle while the chain runs)
-    FI_SHARED float* lvst = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.fftreg - kLvlStageBytes);
     const bool direct = d.T >= kBlk;
     const int lane = threadIdx.x;
     const int wmask = kBlk - 1, xmask = d.XR - 1;
@@ -598,8 +569,6 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     TwPtr<float> tw = gmem(static_cast<const Cx<float>*>(d.twf));
     FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)bid * d.sc_stride;
     FI_GLOBAL float* yout = gmem(a.y);
-    const FI_GLOBAL float* lvl = gmem(d.lvl) + (int64_t)bid * d.lvl_stride;
-    FI_GLOBAL float* lvlw = gmem(d.lvl) + (int64_t)bid * d.lvl_stride;
     fill_lds_twiddles(twl);
 
     for (int64_t ch = ch0; ch < d.C; ch += G) {
@@ -631,12 +600,11 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
         // only cover what each block issues
         __builtin_amdgcn_s_waitcnt(0x0F70);
         for (int64_t t0 = 0; t0 < L; t0 += kBlk) {
-            float xb[kRegs], p[kRegs], xk[kRegs], acc_in[kRegs];
+            float xb[kRegs], p[kRegs], xk[kRegs];
 #pragma unroll
             for (int k = 0; k < kRegs; ++k) {
                 xb[k] = xbn[k];
                 p[k] = accw[(kWave * k + lane) & wmask];   // t0 is a multiple of the ring size
-                acc_in[k] = 0.f;
             }
             if constexpr (!CLOSED) {
 #pragma unroll
@@ -664,16 +632,17 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(row + (inext - Un) + k + lane),
                                                      (FI_SHARED void*)(xst + k), 4, 0, 0);
             }
-            // Chain over the block.  The level-buffer values of the positions
-            // entering the ring at the block's end are loaded one register row
-            // at a time (row k at step 64k, summed 64 steps later), so they
-            // arrive while the chain runs.
+            // The accumulators of the next block's positions, from the row:
+            // some earlier tile left them outside its ring exactly when a bit
+            // of base other than its lowest is set at or above 2 kBlk (the
+            // tile of that bit's level covered them, its ring did not).
             const int64_t base = t0 + kBlk;
-            uint32_t present = 0;   // level qlo + j holds values for this block
-            if (d.lvl_qhi >= d.lvl_qlo) {
-                const int nq = d.lvl_qhi - d.lvl_qlo + 1;
-                const uint64_t bits = ((uint64_t)base & ~((uint64_t)base & (0 - (uint64_t)base))) >> d.lvl_qlo;
-                present = (uint32_t)(bits & ((1ull << nq) - 1));
+            const bool nx_in_row = ((base & (base - 1)) >> (kLog2Blk + 1)) != 0;
+            float nx[kRegs];
+#pragma unroll
+            for (int k = 0; k < kRegs; ++k) {
+                const int64_t pn = base + kWave * k + lane;
+                nx[k] = (nx_in_row && pn < L) ? row[pn] : 0.f;
             }
             const FI_SHARED float* hz0 = hz + kWave + lane;   // hz0[64k - m]: tap of position 64k + lane, input m
             float ta[kRegs][2 * kTapBatch];
@@ -692,7 +661,6 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
             // one 64-step segment of the chain (steps 64K .. 64K+63)
             auto segment = [&](auto kc) {
                 constexpr int K = decltype(kc)::value;
-                level_loads(lvl, d.lvl_qlo, present, base + kWave * K + lane, lvst);
 #pragma unroll
                 for (int m2 = 0; m2 < kWave; ++m2) {
                     const int m = kWave * K + m2;
@@ -731,9 +699,6 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this segment's level rows landed
-                acc_in[K] = base + kWave * K + lane < L ? level_sum(present, lvst, lane) : 0.f;
-                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): rows read before the next segment refills them
             };
             static_assert(kRegs == 4, "the chain below runs four segments");
             segment(std::integral_constant<int, 0>{});
@@ -774,7 +739,7 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                 }
                 if (direct) xring[tl & xmask] = xk[k];
                 if (stage_x) xst[Un - kBlk + kWave * k + lane] = xk[k];   // completes the staged input block
-                accw[(kWave * k + lane) & wmask] = acc_in[k];  // slot of position t now holds position t + W
+                accw[(kWave * k + lane) & wmask] = nx[k];  // slot of position t now holds position t + W
             }
             wave_sync();
             const int64_t i = t0 + kBlk;
@@ -784,7 +749,7 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
                 } else {
                     const int q = ilog2(U);
-                    TileSink s{row, accw, i + kBlk, wmask, L, d.lvl_off[q] >= 0 ? lvlw + d.lvl_off[q] : nullptr};
+                    TileSink s{row, accw, i + kBlk, wmask, L, i == U};
                     const FI_GLOBAL V4* spec =
                         gmem(static_cast<const V4*>(d.spec)) + d.spec_off[q] + c * (int64_t)U;
                     if (stage_x) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged loads landed
