@@ -327,10 +327,13 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
 // `row` holds the channel's input history (row[s] = x[s] for s < i).
 // xst, when not null, holds the input block x[i-U, i) in LDS (staged by the
 // caller), and spec_lds the tile's alpha/beta entries.
-__device__ __noinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row, const FI_GLOBAL V4* spec,
+// The sink's fields come as separate arguments (registers, not a stack copy).
+__device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row, const FI_GLOBAL V4* spec,
                                       FI_SHARED Cx<float>* lbuf, FI_GLOBAL Cx<float>* sc, TwPtr<float> tw,
-                                      const FI_SHARED Cx<float>* twl, TileSink out, const FI_SHARED float* xst,
+                                      const FI_SHARED Cx<float>* twl, FI_SHARED float* accw, int64_t wend,
+                                      int wmask, int64_t L, bool first, const FI_SHARED float* xst,
                                       const FI_SHARED V4* spec_lds) {
+    const TileSink out{row, accw, wend, wmask, L, first};
     const LdsTw ltw{twl};
     const int M = U;
     const FI_GLOBAL float* xblock = row + (i - U);
@@ -484,9 +487,8 @@ __global__ __launch_bounds__(64) void k_tile_fft(DevState d, int64_t i, int U) {
     for (int64_t ch = blockIdx.x; ch < d.C; ch += gridDim.x) {
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)blockIdx.x * d.sc_stride;
-        TileSink s{row, nullptr, i, 0, d.L, false};
-        fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)U, lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl, s,
-                 nullptr, nullptr);
+        fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)U, lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl,
+                 nullptr, i, 0, d.L, false, nullptr, nullptr);
     }
 }
 
@@ -726,21 +728,37 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) xk[k] = xb[k];
             }
+            // Everything this block loaded (staging, next accumulators) was
+            // issued a whole chain ago: wait for it here, before the stores
+            // below (stores count in the same counter, and their
+            // acknowledgement is not needed before the tile).
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             // p now holds y of the block (lane m's accumulator stopped
             // changing at step m: later pushes carry a zero tap there)
 #pragma unroll
             for (int k = 0; k < kRegs; ++k) {
                 const int64_t tl = t0 + kWave * k + lane;
-                if (tl < L) {
-                    const int64_t o = (b * L + tl) * D + c;
-                    yout[o] = p[k];
-                    if (a.x_out) store_io<BF16>(a.x_out, o, xk[k]);
-                    row[tl] = xk[k];  // the slot of a consumed accumulator now holds x
-                }
                 if (direct) xring[tl & xmask] = xk[k];
                 if (stage_x) xst[Un - kBlk + kWave * k + lane] = xk[k];   // completes the staged input block
                 accw[(kWave * k + lane) & wmask] = nx[k];  // slot of position t now holds position t + W
             }
+            // y, x_out and the input history: before a tile that reads its
+            // input block from the row, after one that has it staged in LDS
+            // (the tile call waits for every outstanding store)
+            auto store_block = [&]() {
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) {
+                    const int64_t tl = t0 + kWave * k + lane;
+                    if (tl < L) {
+                        const int64_t o = (b * L + tl) * D + c;
+                        yout[o] = p[k];
+                        if (a.x_out) store_io<BF16>(a.x_out, o, xk[k]);
+                        row[tl] = xk[k];  // the slot of a consumed accumulator now holds x
+                    }
+                }
+            };
+            const bool row_input = Un > d.T && !stage_x;   // next tile: FFT reading the row
+            if (row_input) store_block();
             wave_sync();
             const int64_t i = t0 + kBlk;
             if (i < L) {
@@ -749,15 +767,14 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
                 } else {
                     const int q = ilog2(U);
-                    TileSink s{row, accw, i + kBlk, wmask, L, i == U};
                     const FI_GLOBAL V4* spec =
                         gmem(static_cast<const V4*>(d.spec)) + d.spec_off[q] + c * (int64_t)U;
-                    if (stage_x) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): staged loads landed
-                    fft_tile(U, i, row, spec, lbuf, sc, tw, twl, s, stage_x ? xst : nullptr,
-                             stage_spec ? sst : nullptr);
+                    fft_tile(U, i, row, spec, lbuf, sc, tw, twl, accw, i + kBlk, wmask, L, i == U,
+                             stage_x ? xst : nullptr, stage_spec ? sst : nullptr);
                 }
                 wave_sync();
             }
+            if (!row_input) store_block();
         }
     }
 }
