@@ -248,6 +248,17 @@ struct TileIn {
     }
 };
 
+// The same input times w_M^n (the second half after one radix-2 pass).
+struct TileInTw {
+    const FI_GLOBAL V2* xs;
+    TwPtr<float> tw;
+    int M;
+    __device__ __forceinline__ Cx<float> operator()(int n) const {
+        const V2 v = xs[n];
+        return cmul(Cx<float>{v.x, v.y}, twiddle<false>(tw, M, n));
+    }
+};
+
 // Untangle W = alpha Z + beta conj(Z') over nitems partner pairs held in the
 // LDS buffer; pos(n) gives the (buffer-relative) positions of pair n and
 // spec index = sbase + position.  All spectrum loads of a lane's batch are
@@ -363,7 +374,33 @@ __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row,
         case 4096: fft_tile_lds<4096>(i, xg, spec, lbuf, ltw, out); return;
         default: break;
     }
-    // M > 4096: radix-2 decimation-in-frequency passes over the scratch slot
+    if (M == 2 * kLdsFftMax) {
+        // One radix-2 decimation-in-frequency pass splits the transform into
+        // halves z[n] + z[n + M/2] and (z[n] - z[n + M/2]) w_M^n; the input's
+        // upper half is the zero padding, so these are z[n] and z[n] w_M^n,
+        // formed while loading.  Each half holds its own partner frequencies
+        // (half 0: octaves 0 .. log2(F)-1, half 1: octave log2(F)), so each
+        // is transformed, untangled and transformed back in LDS; half 0's
+        // result waits in the scratch slot for the last inverse pass, fused
+        // with the output (only outputs M/2 .. M-1 are kept).
+        constexpr int F = kLdsFftMax;
+        const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
+        dif_lds<F, F, float>(TileIn{xs, F}, lbuf, ltw);
+        untangle_lds<8>(lbuf, spec, F / 2 + 1, PairsAll{});
+        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        copy_from_lds(sc, lbuf, F);
+        dif_lds<F, F, float>(TileInTw{xs, tw, M}, lbuf, ltw);
+        untangle_lds<8>(lbuf, spec + F, F / 2, PairsMirror{F});
+        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        tile_output(out, i, F, [sc, lbuf, tw](int j) {
+            const Cx<float> v0 = sc[j];
+            const Cx<float> v1 = cmul(lbuf[lp(j)], twiddle<true>(tw, 2 * F, j));
+            return csub(v0, v1);
+        });
+        wave_sync();
+        return;
+    }
+    // M > 8192: radix-2 decimation-in-frequency passes over the scratch slot
     // until F = 4096-point blocks remain; after the blocks' own transforms,
     // position p (block p / F) holds frequency brev(p) over log2(M) bits.
     // Block 0 holds octaves 0 .. log2(F)-1 and block 1 octave log2(F): both
@@ -549,6 +586,7 @@ inline int run_lds_floats(const DevState& d) { return d.fftreg / 4 + (d.T >= kBl
 
 template <bool CLOSED, bool BF16>
 __global__ __launch_bounds__(64) void k_run(RunArgs a) {
+    constexpr bool RFORM = CLOSED && !BF16;   // fp32 closed loop: inputs pushed as r
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ Cx<float> s_tw[128];     // twiddles A[64] = w_64^a, B[64] = w_4096^b
     __shared__ float s_ring[kBlk];      // accumulators of positions [t0, t0+W)
@@ -578,19 +616,42 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         const FI_GLOBAL float* hrow = gmem(d.hT + c * d.LS);
         for (int q = lane; q < kBlk; q += kWave) accw[q] = 0.f;
+        // taps: h (open loop); c h (closed loop, bf16 inputs); -2 c h (closed
+        // loop, fp32: the inputs are pushed as r, x = 1 - 2 r, see below)
+        const float tap_scale = !CLOSED ? 1.0f : (RFORM ? -2.0f * kTanhScale : kTanhScale);
         for (int q = lane; q < kWave + kBlk; q += kWave)
-            hz[q] = (q >= kWave && q - kWave < L) ? (CLOSED ? kTanhScale * hrow[q - kWave] : hrow[q - kWave]) : 0.f;
+            hz[q] = (q >= kWave && q - kWave < L) ? tap_scale * hrow[q - kWave] : 0.f;
         if (direct)
             for (int q = lane; q < 2 * d.T; q += kWave) htap[q] = q < L ? hrow[q] : 0.f;
         wave_sync();
-        const float ch0v = hz[kWave];   // closed loop: c h[0]
+        const float ch0v = hz[kWave];   // closed loop: c h[0] (-2 c h[0] for fp32)
+        // fp32 closed loop: every input of a block contributes c h[lag] (the
+        // "1" of x = 1 - 2 r) to each later position of it; that part is the
+        // same for every block, cpre[k] = c * sum_{j <= 64k + lane} h[j], and
+        // is added once per block.
+        float cpre[kRegs];
+#pragma unroll
+        for (int k = 0; k < kRegs; ++k) cpre[k] = 0.f;
+        if constexpr (RFORM) {
+            float run = 0.f;
+#pragma unroll 1
+            for (int j = 0; j < kBlk; ++j) {
+                run += hz[kWave + j];
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) cpre[k] = (j == kWave * k + lane) ? run : cpre[k];
+            }
+#pragma unroll
+            for (int k = 0; k < kRegs; ++k) cpre[k] *= -0.5f;
+        }
 
         float xcur = 0.f;        // closed loop: x at the next position (uniform)
+        float rcur = 0.f;        // fp32 closed loop: r with x = 1 - 2 r at the next position
         float xbn[kRegs];        // open loop: inputs of the next block
 #pragma unroll
         for (int k = 0; k < kRegs; ++k) xbn[k] = 0.f;
         if constexpr (CLOSED) {
             xcur = load_io<BF16>(a.x_in, b * D + c);
+            rcur = (1.0f - xcur) * 0.5f;
         } else {
 #pragma unroll
             for (int k = 0; k < kRegs; ++k) {
@@ -656,7 +717,7 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
             float xstart = 0.f;
             if constexpr (CLOSED) {
 #pragma unroll
-                for (int k = 0; k < kRegs; ++k) p[k] *= kTanhScale;
+                for (int k = 0; k < kRegs; ++k) p[k] = __builtin_fmaf(p[k], kTanhScale, cpre[k]);
                 v = readlane(p[0], 0);
                 xstart = xcur;
             }
@@ -669,15 +730,15 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     float tv[kRegs];
 #pragma unroll
                     for (int k = 0; k < kRegs; ++k) tv[k] = ta[k][m % (2 * kTapBatch)];
-                    // closed loop: the accumulators run in units of c = 2 log2(e)
-                    // (the taps hz are c h), so tanh(y) = 1 - 2 r with
-                    // r = 1 / (1 + 2^(c y)); v holds position t0+m's accumulator
-                    // with every input but its own pushed (read one step ahead,
-                    // off the serial path), and the serial path of a position is
-                    // c y = v + c h[0] x, exp2, add, rcp, x = 1 - 2 r.  Position
-                    // m's own lag-0 push is the same fma as c y, so its register
-                    // ends equal to it.
-                    const float xm = CLOSED ? xcur : readlane(xb[K], m2);
+                    // closed loop: the accumulators run in units of c = 2 log2(e),
+                    // so tanh(y) = 1 - 2 r with r = 1 / (1 + 2^(c y)); v holds
+                    // position t0+m's accumulator with every input but its own
+                    // pushed (read one step ahead, off the serial path), and the
+                    // serial path of a position is c y = v + c h[0] x (fp32:
+                    // v + (-2 c h[0]) r), exp2, add, rcp.  Position m's own
+                    // lag-0 push is the same fma as c y, so its register ends
+                    // equal to it.
+                    const float xm = RFORM ? rcur : (CLOSED ? xcur : readlane(xb[K], m2));
                     const float cy = __builtin_fmaf(ch0v, xm, v);
 #pragma unroll
                     for (int k = K; k < kRegs; ++k) {
@@ -696,8 +757,12 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     }
                     if constexpr (CLOSED) {
                         if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
-                        xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
-                        if constexpr (BF16) xcur = round_bf16(xcur);
+                        if constexpr (RFORM) {
+                            rcur = tanh_rcp_scaled(cy);
+                        } else {
+                            xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
+                            if constexpr (BF16) xcur = round_bf16(xcur);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -724,6 +789,7 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     xk[k] = lane == 0 ? prev : sh;
                     p[k] *= 1.0f / kTanhScale;
                 }
+                if constexpr (RFORM) xcur = __builtin_fmaf(-2.0f, rcur, 1.0f);   // next block's x[t0]
             } else {
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) xk[k] = xb[k];
