@@ -164,7 +164,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="hyena-d1024-l16k")
     ap.add_argument("--small-tile-max", type=int, default=0)
-    ap.add_argument("--cpu-channels", type=int, default=256)
+    ap.add_argument("--cpu-channels", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
