@@ -80,27 +80,30 @@ int build(fi_handle *s, const void *h) {
         const int64_t U = (int64_t)1 << q;
         if (U <= d.T) continue;
         d.spec_off[q] = spec_total;
-        spec_total += d.D * U;
+        spec_total += d.D * (U + 2);
         d.umax_fft = (int)U;
         smax = q;
     }
     d.F = d.umax_fft > 0 ? (d.umax_fft < fi::kLdsFftMax ? d.umax_fft : fi::kLdsFftMax) : 1;
     // FFT region of the persistent pass: the largest LDS transform, or the
     // staging of a tile's input (4U bytes) and, for U <= 1024, its spectrum
-    // (16U bytes) behind that tile's own transform buffer
+    // (8 (U + 2) bytes) behind that tile's own transform buffer
     d.fftreg = fi::lds_fft_elems(d.F) * 8;
     for (int q = 0; q < fi::kMaxLevels; ++q) {
         if (d.spec_off[q] < 0) continue;
         const int U = 1 << q;
         int need = 0;
-        if (U <= 1024) need = fi::lds_fft_elems(U) * 8 + 4 * U + 16 * U;
+        if (U <= 1024) need = fi::lds_fft_elems(U) * 8 + 4 * U + 8 * (U + 2);
         else if (U <= 2048) need = fi::lds_fft_elems(U) * 8 + 4 * U;
         if (need > d.fftreg) d.fftreg = need;
     }
 
     FI_HIP(dalloc(&d.hT, (size_t)(d.D * d.LS) * sizeof(float)));
     FI_HIP(dalloc(&d.state, (size_t)(d.C * d.LS) * sizeof(float)));
-    FI_HIP(dalloc(&d.spec, (size_t)(spec_total > 0 ? spec_total : 1) * 16));
+    FI_HIP(dalloc(&d.spec, (size_t)(spec_total > 0 ? spec_total : 1) * 8));
+    // twiddles up to 2 umax points (the untangle of the largest tiles uses
+    // w_2U^k)
+    smax += 1;
     FI_HIP(dalloc(&d.twf, (size_t)((int64_t)2 << smax) * 8));
 
     // persistent-pass grid: every resident wavefront slot, at most one per channel

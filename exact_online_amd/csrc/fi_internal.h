@@ -10,6 +10,7 @@ namespace fi {
 constexpr int kMaxLevels = 40;
 constexpr int kRunBlock = 256;     // positions per block of the persistent pass (= its LDS ring W)
 constexpr int kLdsFftMax = 4096;  // largest complex FFT held in LDS (32 KiB in fp32)
+constexpr int kTwLds = 132;       // LDS twiddle table: w_64^a, w_4096^b (64 each), w_16384^r (4)
 // LDS FFT buffers hold one spare slot per 8 points (bank spreading).
 constexpr int lds_fft_elems(int M) { return M + M / 8; }
 
@@ -20,9 +21,10 @@ constexpr int lds_fft_elems(int M) { return M + M / 8; }
 //                  accumulated tile contributions (the two share one slot per
 //                  position, as the activation buffer is reused for the mixer
 //                  output in the pages' memory optimisation)
-//   spec           per FFT level q (U = 2^q): [D][U] float4 = (alpha, beta) of
-//                  the packed real circular convolution of length 2U, stored in
-//                  the bit-reversed position order of the forward FFT, 1/U folded
+//   spec           per FFT level q (U = 2^q): [D][U + 2] float2, G[k] / (4U) with
+//                  G the 2U-point DFT of the tile's filter segment, entry p < U
+//                  holding frequency brev(p) (the forward FFT's position
+//                  order), entry U holding G[U]
 //   twf            twiddles, twf[S + m] = exp(-2 pi i m / S), S = 1 .. 2^smax
 //                  (spectra in bit-reversed frequency order: entry p is
 //                  frequency brev(p))
@@ -37,8 +39,8 @@ struct DevState {
     int io_bf16;
     float *hT;
     float *state;
-    void *spec;            // float4
-    int64_t spec_off[kMaxLevels];  // element (float4) offset of level q, -1 if none
+    void *spec;            // float2
+    int64_t spec_off[kMaxLevels];  // element (float2) offset of level q, -1 if none
     void *twf;             // Cx<float>
     void *scratch;         // Cx<float>
     int64_t sc_stride;     // complex elements per scratch slot

@@ -80,19 +80,17 @@ __global__ void k_twiddles(Cx<double>* twd, Cx<float>* twf, int smax) {
     }
 }
 
-// Filter spectra of level q (U = 2^q = M complex points): with the tile's
-// length-2U filter segment g[n] = h[n] for 1 <= n < 2U (g[0] = 0: lag 0 never
-// reaches the outputs [U, 2U) that are kept, [FI] "Trucco di Convoluzione
-// Circolare"), z[n] = g[2n] + i g[2n+1] and Z = DFT_M(z) in fp64, per
-// frequency k (partner frequency M-k):
-//   E = (Z[k] + conj Z[M-k])/2,  d = Z[k] - conj Z[M-k],  w = exp(-2 pi i k/M)
-//   alpha = (E + d/4 (1 - w)) / M,   beta = d/4 (1 + w) / M
-// so that the tile's packed output spectrum is W = alpha Z_x + beta conj(Z_x')
-// (Z_x' at frequency M-k).  The FFT is the tile's own (in-place, bit-reversed
-// output); alpha/beta are stored in that position order: entry p belongs to
-// frequency brev(p), its partner to the octave mirror of p.
+// Filter spectra of level q (U = 2^q = M complex points).  The tile's filter
+// segment g[n] = h[n] for 1 <= n < 2M (g[0] = 0: lag 0 never reaches the
+// outputs [U, 2U) that are kept, [FI] "Trucco di Convoluzione Circolare") has
+// the 2M-point DFT G; it is computed in fp64 from Z = DFT_M(g[2n] + i g[2n+1])
+// as G[k] = (Z[k] + conj Z[M-k]) / 2 + w_2M^k (Z[k] - conj Z[M-k]) / (2i).
+// Stored per channel, M + 2 entries G[k] / (4M) (the 1/(4M) folds the
+// packing's halves and the inverse transform's 1/M): entry p < M holds
+// frequency brev(p) (the tile's own bit-reversed position order), entry M
+// holds G[M] (the partner of frequency 0), entry M + 1 is padding.
 __global__ __launch_bounds__(64) void k_spectra(const float* hT, int64_t LS, int64_t L, int64_t D, int M,
-                                                V4* spec, Cx<double>* scd, int64_t scd_stride,
+                                                V2* spec, Cx<double>* scd, int64_t scd_stride,
                                                 const Cx<double>* twd_) {
     extern __shared__ __align__(16) unsigned char smem[];
     FI_SHARED Cx<double>* lbuf = smem_ptr(reinterpret_cast<Cx<double>*>(smem));
@@ -120,17 +118,21 @@ __global__ __launch_bounds__(64) void k_spectra(const float* hT, int64_t LS, int
             }
         }
         auto zat = [&](int p) -> Cx<double> { return P == 1 ? lbuf[lp(p)] : sc[p]; };
-        FI_GLOBAL V4* out = gmem(spec + c * (int64_t)M);
-        const double inv = 1.0 / (double)M;
+        FI_GLOBAL V2* out = gmem(spec + c * (int64_t)(M + 2));
+        const double scale = 1.0 / (4.0 * (double)M);
         for (int p = lane; p < M; p += kWave) {
             const int k = brev_bits(p, lm);
             const Cx<double> z1 = zat(p), z2c = cconj(zat(mirror_pos(p)));
-            const Cx<double> E = {(z1.x + z2c.x) * 0.5, (z1.y + z2c.y) * 0.5};
-            const Cx<double> d4 = {(z1.x - z2c.x) * 0.25, (z1.y - z2c.y) * 0.25};
-            const Cx<double> w = twd[M + k];
-            const Cx<double> a = cadd(E, cmul(d4, Cx<double>{1.0 - w.x, -w.y}));
-            const Cx<double> bb = cmul(d4, Cx<double>{1.0 + w.x, w.y});
-            out[p] = V4{(float)(a.x * inv), (float)(a.y * inv), (float)(bb.x * inv), (float)(bb.y * inv)};
+            const Cx<double> ge = {(z1.x + z2c.x) * 0.5, (z1.y + z2c.y) * 0.5};
+            const Cx<double> dz = {(z1.x - z2c.x) * 0.5, (z1.y - z2c.y) * 0.5};
+            const Cx<double> go = {dz.y, -dz.x};   // dz / i
+            const Cx<double> gk = cadd(ge, cmul(twd[2 * M + k], go));
+            out[p] = V2{(float)(gk.x * scale), (float)(gk.y * scale)};
+        }
+        if (lane == 0) {
+            const Cx<double> z0 = zat(0);
+            out[M] = V2{(float)((z0.x - z0.y) * scale), 0.f};
+            out[M + 1] = V2{0.f, 0.f};
         }
         wave_sync();
     }
@@ -213,27 +215,27 @@ __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n,
     }
 }
 
-// W = alpha Z + beta conj(Z') for a partner pair of frequencies (k, M-k):
-// za/zb are the buffer slots holding them, sa/sb their alpha/beta entries.
-template <typename Acc>
-__device__ __forceinline__ void untangle_pair(const Acc& Z, int za, int zb, V4 sa, V4 sb) {
-    const Cx<float> z1 = Z.get(za), z2 = Z.get(zb);
-    const Cx<float> w1 = cadd(cmul(Cx<float>{sa.x, sa.y}, z1), cmul(Cx<float>{sa.z, sa.w}, cconj(z2)));
-    const Cx<float> w2 = cadd(cmul(Cx<float>{sb.x, sb.y}, z2), cmul(Cx<float>{sb.z, sb.w}, cconj(z1)));
-    Z.set(za, w1);
-    Z.set(zb, w2);
+// Output spectrum of a partner pair of frequencies (k, M-k) whose packed
+// input transform values (z[n] = x[2n] + i x[2n+1]) are A = Z_k, B = Z_{M-k},
+// with the filter entries gk = G[k] / (4M), gm = G[M-k] / (4M), w = w_2M^k:
+//   P = A + conj B,  Q = -i w (A - conj B)
+//   (2 X[k], 2 X[k+M]) = (P + Q, P - Q)             (real 2M-point spectrum)
+//   Ya = gk (P + Q),  Yb = conj(gm) (P - Q)         (G[k+M] = conj G[M-k])
+//   S = Ya + Yb,  E = i conj(w) (Ya - Yb)
+//   W_k = S + E,  W_{M-k} = conj(S - E)             (the packed output spectrum)
+// For the self-paired k = 0 (gm = G[M]) and k = M/2 both results agree.
+__device__ __forceinline__ void untangle_pair(Cx<float>& A, Cx<float>& B, Cx<float> gk, Cx<float> gm, Cx<float> w) {
+    const Cx<float> Bc = cconj(B);
+    const Cx<float> wm = {w.y, -w.x};   // -i w
+    const Cx<float> Pp = cadd(A, Bc);
+    const Cx<float> Qq = cmul(wm, csub(A, Bc));
+    const Cx<float> Ya = cmul(gk, cadd(Pp, Qq));
+    const Cx<float> Yb = cmul(cconj(gm), csub(Pp, Qq));
+    const Cx<float> Ss = cadd(Ya, Yb);
+    const Cx<float> Ee = cmul(cconj(wm), csub(Ya, Yb));
+    A = cadd(Ss, Ee);
+    B = cconj(csub(Ss, Ee));
 }
-struct PadAcc {  // LDS FFT buffer, padded
-    FI_SHARED Cx<float>* b;
-    __device__ __forceinline__ Cx<float> get(int p) const { return b[lp(p)]; }
-    __device__ __forceinline__ void set(int p, Cx<float> v) const { b[lp(p)] = v; }
-};
-struct FlatAcc {  // global scratch
-    FI_GLOBAL Cx<float>* b;
-    __device__ __forceinline__ Cx<float> get(int p) const { return b[p]; }
-    __device__ __forceinline__ void set(int p, Cx<float> v) const { b[p] = v; }
-};
-
 // Forward-FFT input of the tile: z[n] = x[2n] + i x[2n+1] for n < M/2, zero
 // beyond (the input block padded on the right).
 struct TileIn {
@@ -259,31 +261,91 @@ struct TileInTw {
     }
 };
 
-// Untangle W = alpha Z + beta conj(Z') over nitems partner pairs held in the
-// LDS buffer; pos(n) gives the (buffer-relative) positions of pair n and
-// spec index = sbase + position.  All spectrum loads of a lane's batch are
-// issued before the first use.
-template <int NB, typename SpecP, typename Pos>
-__device__ __forceinline__ void untangle_lds(FI_SHARED Cx<float>* lds, SpecP spec, int nitems, const Pos& pos) {
+// Twiddles w_N^k for the untangle: from the LDS table (A[64] = w_64^a,
+// B[64] = w_4096^b, C[4] = w_16384^r) for N <= 16384, else from the global
+// table.
+struct TwLdsN {
+    const FI_SHARED Cx<float>* t;
+    int N;
+    __device__ __forceinline__ Cx<float> operator()(int k) const {
+        if (N <= kLdsFftMax) {
+            const int j = k * (kLdsFftMax / N);
+            return cmul(t[j >> 6], t[64 + (j & 63)]);
+        }
+        const int s = N / kLdsFftMax;   // 2 or 4
+        const int j = k / s, r = k % s;
+        const Cx<float> w = cmul(t[j >> 6], t[64 + (j & 63)]);
+        return r ? cmul(w, t[128 + r * (4 / s)]) : w;
+    }
+};
+struct TwGlobalN {
+    TwPtr<float> tw;
+    int N;
+    __device__ __forceinline__ Cx<float> operator()(int k) const { return twiddle<false>(tw, N, k); }
+};
+
+constexpr int kUntangleBatch = 4;   // pairs per lane per untangle batch
+
+// Filter entries of one batch of NB pairs per lane (pairs n0 + lane + 64u).
+template <int NB>
+struct SpecBatch {
+    V2 ga[NB], gb[NB];
+    template <typename SpecP, typename Pos>
+    __device__ __forceinline__ void load(SpecP spec, int n0, int nitems, const Pos& pos) {
+        const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int n = n0 + lane + kWave * u;
+            int a, b;
+            pos(n < nitems ? n : 0, a, b);
+            if (n < nitems) {
+                ga[u] = spec[a];
+                gb[u] = spec[b];
+            }
+        }
+    }
+};
+
+// Untangle nitems partner pairs held in the LDS buffer: pos(n) gives the
+// (buffer-relative) slots of pair n, spec[slot] their filter entries, and the
+// frequency of slot a is brev(pos_off + a) over lbits bits; gM is G[M] / (4M),
+// the partner entry of frequency 0.  `cur` holds the first batch's filter
+// entries, loaded by the caller (ahead of the forward transform); each later
+// batch is loaded while the one before it is processed.
+template <int NB, typename SpecP, typename Pos, typename TwF>
+__device__ __forceinline__ void untangle_lds(FI_SHARED Cx<float>* lds, SpecP spec, V2 gM, int nitems,
+                                             const Pos& pos, int pos_off, int lbits, const TwF& twf,
+                                             SpecBatch<NB> cur) {
     const int lane = threadIdx.x & (kWave - 1);
-    const PadAcc Z{lds};
 #pragma unroll 1
     for (int n0 = 0; n0 < nitems; n0 += kWave * NB) {
-        V4 sa[NB], sb[NB];
+        SpecBatch<NB> nxt;
+        if (n0 + kWave * NB < nitems) nxt.load(spec, n0 + kWave * NB, nitems, pos);
+        // the pairs of a batch are disjoint: all reads first, then all writes
+        Cx<float> za[NB], zb[NB], w[NB];
         int pa[NB], pb[NB];
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
             const int n = n0 + lane + kWave * u;
             pos(n < nitems ? n : 0, pa[u], pb[u]);
-            if (n < nitems) {
-                sa[u] = spec[pa[u]];
-                sb[u] = spec[pb[u]];
-            }
+            za[u] = lds[lp(pa[u])];
+            zb[u] = lds[lp(pb[u])];
+            w[u] = twf(brev_bits(pos_off + pa[u], lbits));
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            if (n0 + lane + kWave * u < nitems) untangle_pair(Z, pa[u], pb[u], sa[u], sb[u]);
+            const bool first = brev_bits(pos_off + pa[u], lbits) == 0;
+            const V2 gm = first ? gM : cur.gb[u];
+            untangle_pair(za[u], zb[u], Cx<float>{cur.ga[u].x, cur.ga[u].y}, Cx<float>{gm.x, gm.y}, w[u]);
         }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            if (n0 + lane + kWave * u < nitems) {
+                lds[lp(pa[u])] = za[u];
+                lds[lp(pb[u])] = zb[u];
+            }
+        }
+        cur = nxt;
     }
     wave_sync();
 }
@@ -320,9 +382,19 @@ struct TileInLds {
 template <int M, typename XIn, typename SpecP>
 __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP spec, FI_SHARED Cx<float>* lds,
                                              const LdsTw& tw, const TileSink& out) {
+    // spectrum in LDS (staged): batches of up to 8, read after the forward
+    // transform; in global memory: batches of kUntangleBatch, the first one
+    // in flight during the forward transform
+    constexpr bool staged = std::is_same<SpecP, const FI_SHARED V2*>::value;
+    constexpr int NALL = M / 2 / kWave + 1;
+    constexpr int NCAP = staged ? 8 : kUntangleBatch;
+    constexpr int NB = NALL < NCAP ? NALL : NCAP;
+    SpecBatch<NB> first;
+    if constexpr (!staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
+    const V2 gM = spec[M];
     dif_lds<M, M, float>(xin, lds, tw);
-    constexpr int NB = (M / 2 / kWave + 1) < 8 ? (M / 2 / kWave + 1) : 8;
-    untangle_lds<NB>(lds, spec, M / 2 + 1, PairsAll{});
+    if constexpr (staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
+    untangle_lds<NB>(lds, spec, gM, M / 2 + 1, PairsAll{}, 0, ilog2(M), TwLdsN{tw.A, 2 * M}, first);
     dit_lds<M, ct_smallest(M), float>(lds, tw);
     // point M/2 + m carries outputs 2m, 2m + 1 of the tile
     tile_output(out, i, M / 2, [lds](int m) { return lds[lp(M / 2 + m)]; });
@@ -334,16 +406,16 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
 // Convoluzione Circolare": outputs U..2U-1 are free of wrap-around; the input
 // block is padded on the right, [FI] "Dettagli di Implementazione").  The real
 // sequences are packed in pairs into M = U complex points; the per-level
-// (alpha, beta) fold the packing, the filter spectrum and the 1/M scale.
+// filter spectrum G (M + 2 entries) is untangled against the packing.
 // `row` holds the channel's input history (row[s] = x[s] for s < i).
 // xst, when not null, holds the input block x[i-U, i) in LDS (staged by the
-// caller), and spec_lds the tile's alpha/beta entries.
+// caller), and spec_lds the tile's spectrum entries.
 // The sink's fields come as separate arguments (registers, not a stack copy).
-__device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row, const FI_GLOBAL V4* spec,
+__device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row, const FI_GLOBAL V2* spec,
                                       FI_SHARED Cx<float>* lbuf, FI_GLOBAL Cx<float>* sc, TwPtr<float> tw,
                                       const FI_SHARED Cx<float>* twl, FI_SHARED float* accw, int64_t wend,
                                       int wmask, int64_t L, bool first, const FI_SHARED float* xst,
-                                      const FI_SHARED V4* spec_lds) {
+                                      const FI_SHARED V2* spec_lds) {
     const TileSink out{row, accw, wend, wmask, L, first};
     const LdsTw ltw{twl};
     const int M = U;
@@ -385,12 +457,17 @@ __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row,
         // with the output (only outputs M/2 .. M-1 are kept).
         constexpr int F = kLdsFftMax;
         const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
+        const V2 gM = spec[M];
+        const TwLdsN twn{twl, 2 * M};
+        SpecBatch<kUntangleBatch> first;
+        first.load(spec, 0, F / 2 + 1, PairsAll{});
         dif_lds<F, F, float>(TileIn{xs, F}, lbuf, ltw);
-        untangle_lds<8>(lbuf, spec, F / 2 + 1, PairsAll{});
+        untangle_lds<kUntangleBatch>(lbuf, spec, gM, F / 2 + 1, PairsAll{}, 0, ilog2(M), twn, first);
         dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
         copy_from_lds(sc, lbuf, F);
+        first.load(spec + F, 0, F / 2, PairsMirror{F});
         dif_lds<F, F, float>(TileInTw{xs, tw, M}, lbuf, ltw);
-        untangle_lds<8>(lbuf, spec + F, F / 2, PairsMirror{F});
+        untangle_lds<kUntangleBatch>(lbuf, spec + F, gM, F / 2, PairsMirror{F}, F, ilog2(M), twn, first);
         dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
         tile_output(out, i, F, [sc, lbuf, tw](int j) {
             const Cx<float> v0 = sc[j];
@@ -425,31 +502,53 @@ __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row,
         copy_to_lds(lbuf, blk, F);
         dif_lds<F, F, float>(LdsIn<float>{lbuf}, lbuf, ltw);
         if (p <= 1) {
-            if (p == 0) untangle_lds<8>(lbuf, spec, F / 2 + 1, PairsAll{});
-            else untangle_lds<8>(lbuf, spec + F, F / 2, PairsMirror{F});
+            const TwGlobalN twn{tw, 2 * M};
+            SpecBatch<kUntangleBatch> first;
+            if (p == 0) {
+                first.load(spec, 0, F / 2 + 1, PairsAll{});
+                untangle_lds<kUntangleBatch>(lbuf, spec, spec[M], F / 2 + 1, PairsAll{}, 0, ilog2(M), twn, first);
+            } else {
+                first.load(spec + F, 0, F / 2, PairsMirror{F});
+                untangle_lds<kUntangleBatch>(lbuf, spec + F, spec[M], F / 2, PairsMirror{F}, F, ilog2(M), twn, first);
+            }
             dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
         }
         copy_from_lds(blk, lbuf, F);
     }
     if (P > 2) {
-        const FlatAcc Zg{sc};
         for (int p = 2; p < P; ++p) {
             const int a = 31 - __builtin_clz(p);   // octave of block p: blocks [2^a, 2^(a+1))
             const int pp = 3 * (1 << a) - 1 - p;
             if (pp < p) continue;
+            const int lm = ilog2(M);
 #pragma unroll 1
             for (int k0 = 0; k0 < F; k0 += kWave * kBatch) {
-                V4 sa[kBatch], sb[kBatch];
+                V2 sa[kBatch], sb[kBatch];
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u) {
                     const int k = k0 + lane + kWave * u;
                     sa[u] = spec[(int64_t)p * F + k];
                     sb[u] = spec[(int64_t)pp * F + (F - 1 - k)];
                 }
+                Cx<float> za[kBatch], zb[kBatch];
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u) {
                     const int k = k0 + lane + kWave * u;
-                    untangle_pair(Zg, p * F + k, pp * F + (F - 1 - k), sa[u], sb[u]);
+                    za[u] = sc[p * F + k];
+                    zb[u] = sc[pp * F + (F - 1 - k)];
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int k = k0 + lane + kWave * u;
+                    const int fa = brev_bits(p * F + k, lm);   // never 0 in blocks >= 2
+                    untangle_pair(za[u], zb[u], Cx<float>{sa[u].x, sa[u].y}, Cx<float>{sb[u].x, sb[u].y},
+                                  twiddle<false>(tw, 2 * M, fa));
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int k = k0 + lane + kWave * u;
+                    sc[p * F + k] = za[u];
+                    sc[pp * F + (F - 1 - k)] = zb[u];
                 }
             }
         }
@@ -502,7 +601,7 @@ __global__ void k_tile_direct(float* state, const float* hT, int64_t LS, int64_t
     }
 }
 
-// Fills the two-level twiddle table A[64] = w_64^a, B[64] = w_4096^b (fp64
+// Fills the twiddle table A[64] = w_64^a, B[64] = w_4096^b, C[4] = w_16384^r (fp64
 // sincospi of exact dyadic arguments, rounded to fp32).
 __device__ __forceinline__ void fill_lds_twiddles(FI_SHARED Cx<float>* t) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -511,20 +610,24 @@ __device__ __forceinline__ void fill_lds_twiddles(FI_SHARED Cx<float>* t) {
     t[lane] = Cx<float>{(float)cs, (float)-sn};
     sincospi(2.0 * lane / 4096.0, &sn, &cs);
     t[64 + lane] = Cx<float>{(float)cs, (float)-sn};
+    if (lane < 4) {
+        sincospi(2.0 * lane / 16384.0, &sn, &cs);
+        t[128 + lane] = Cx<float>{(float)cs, (float)-sn};
+    }
 }
 
 __global__ __launch_bounds__(64) void k_tile_fft(DevState d, int64_t i, int U) {
     extern __shared__ __align__(16) unsigned char smem[];
     FI_SHARED Cx<float>* twl = smem_ptr(reinterpret_cast<Cx<float>*>(smem));
-    FI_SHARED Cx<float>* lbuf = twl + 128;
+    FI_SHARED Cx<float>* lbuf = twl + kTwLds;
     fill_lds_twiddles(twl);
     wave_sync();
     const int q = ilog2(U);  // level
-    const FI_GLOBAL V4* spec = gmem(static_cast<const V4*>(d.spec)) + d.spec_off[q];
+    const FI_GLOBAL V2* spec = gmem(static_cast<const V2*>(d.spec)) + d.spec_off[q];
     for (int64_t ch = blockIdx.x; ch < d.C; ch += gridDim.x) {
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)blockIdx.x * d.sc_stride;
-        fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)U, lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl,
+        fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)(U + 2), lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl,
                  nullptr, i, 0, d.L, false, nullptr, nullptr);
     }
 }
@@ -555,8 +658,8 @@ constexpr int kLog2Blk = 8;
 static_assert((1 << kLog2Blk) == kBlk, "block size");
 constexpr int kTapBatch = 4;         // chain: taps loaded per batch, one batch ahead
 constexpr int kStageSpecMax = 1024;  // tiles up to this side get spectrum and input staged in LDS
-// (FFT buffer 9M bytes + input 4U + spectrum 16U fits the 36 KiB region for
-// U <= 1024; U = 2048 stages the input only)
+// (FFT buffer 9M bytes + input 4U + spectrum 8 (U + 2) fits the 36 KiB region
+// for U <= 1024; U = 2048 stages the input only)
 
 struct RunArgs {
     DevState d;
@@ -586,9 +689,8 @@ inline int run_lds_floats(const DevState& d) { return d.fftreg / 4 + (d.T >= kBl
 
 template <bool CLOSED, bool BF16>
 __global__ __launch_bounds__(64) void k_run(RunArgs a) {
-    constexpr bool RFORM = CLOSED && !BF16;   // fp32 closed loop: inputs pushed as r
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ Cx<float> s_tw[128];     // twiddles A[64] = w_64^a, B[64] = w_4096^b
+    __shared__ Cx<float> s_tw[kTwLds];  // twiddles A[64] = w_64^a, B[64] = w_4096^b, C[4] = w_16384^r
     __shared__ float s_ring[kBlk];      // accumulators of positions [t0, t0+W)
     __shared__ float s_taps[kWave + kBlk];  // 64 zeros, then the chain's taps
     const DevState& d = a.d;
@@ -616,42 +718,21 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         const FI_GLOBAL float* hrow = gmem(d.hT + c * d.LS);
         for (int q = lane; q < kBlk; q += kWave) accw[q] = 0.f;
-        // taps: h (open loop); c h (closed loop, bf16 inputs); -2 c h (closed
-        // loop, fp32: the inputs are pushed as r, x = 1 - 2 r, see below)
-        const float tap_scale = !CLOSED ? 1.0f : (RFORM ? -2.0f * kTanhScale : kTanhScale);
+        // taps: h (open loop); c h (closed loop, c = 2 log2 e, see below)
+        const float tap_scale = CLOSED ? kTanhScale : 1.0f;
         for (int q = lane; q < kWave + kBlk; q += kWave)
             hz[q] = (q >= kWave && q - kWave < L) ? tap_scale * hrow[q - kWave] : 0.f;
         if (direct)
             for (int q = lane; q < 2 * d.T; q += kWave) htap[q] = q < L ? hrow[q] : 0.f;
         wave_sync();
-        const float ch0v = hz[kWave];   // closed loop: c h[0] (-2 c h[0] for fp32)
-        // fp32 closed loop: every input of a block contributes c h[lag] (the
-        // "1" of x = 1 - 2 r) to each later position of it; that part is the
-        // same for every block, cpre[k] = c * sum_{j <= 64k + lane} h[j], and
-        // is added once per block.
-        float cpre[kRegs];
-#pragma unroll
-        for (int k = 0; k < kRegs; ++k) cpre[k] = 0.f;
-        if constexpr (RFORM) {
-            float run = 0.f;
-#pragma unroll 1
-            for (int j = 0; j < kBlk; ++j) {
-                run += hz[kWave + j];
-#pragma unroll
-                for (int k = 0; k < kRegs; ++k) cpre[k] = (j == kWave * k + lane) ? run : cpre[k];
-            }
-#pragma unroll
-            for (int k = 0; k < kRegs; ++k) cpre[k] *= -0.5f;
-        }
+        const float ch0v = hz[kWave];   // closed loop: c h[0]
 
         float xcur = 0.f;        // closed loop: x at the next position (uniform)
-        float rcur = 0.f;        // fp32 closed loop: r with x = 1 - 2 r at the next position
         float xbn[kRegs];        // open loop: inputs of the next block
 #pragma unroll
         for (int k = 0; k < kRegs; ++k) xbn[k] = 0.f;
         if constexpr (CLOSED) {
             xcur = load_io<BF16>(a.x_in, b * D + c);
-            rcur = (1.0f - xcur) * 0.5f;
         } else {
 #pragma unroll
             for (int k = 0; k < kRegs; ++k) {
@@ -683,12 +764,15 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
             const bool stage_x = Un > d.T && Un <= 2 * kStageSpecMax;
             const bool stage_spec = Un > d.T && Un <= kStageSpecMax;
             FI_SHARED float* xst = reinterpret_cast<FI_SHARED float*>(lbuf + lds_fft_elems(Un));
-            FI_SHARED V4* sst = reinterpret_cast<FI_SHARED V4*>(xst + Un);
-            if (stage_spec) {
-                const FI_GLOBAL V4* sp =
-                    gmem(static_cast<const V4*>(d.spec)) + d.spec_off[ilog2(Un)] + c * (int64_t)Un;
-                for (int k = 0; k < Un; k += kWave)
-                    __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(sp + k + lane), (FI_SHARED void*)(sst + k), 16, 0, 0);
+            FI_SHARED V2* sst = reinterpret_cast<FI_SHARED V2*>(xst + Un);
+            if (stage_spec) {   // Un + 2 entries of 8 bytes, 16 bytes per lane
+                const FI_GLOBAL V4* sp = reinterpret_cast<const FI_GLOBAL V4*>(
+                    gmem(static_cast<const V2*>(d.spec)) + d.spec_off[ilog2(Un)] + c * (int64_t)(Un + 2));
+                FI_SHARED V4* sd = reinterpret_cast<FI_SHARED V4*>(sst);
+                const int n16 = (Un + 2) / 2;
+                for (int k = 0; k < n16; k += kWave)
+                    if (k + lane < n16)
+                        __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(sp + k + lane), (FI_SHARED void*)(sd + k), 16, 0, 0);
             }
             if (stage_x) {
                 for (int k = 0; k < Un - kBlk; k += kWave)
@@ -717,7 +801,7 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
             float xstart = 0.f;
             if constexpr (CLOSED) {
 #pragma unroll
-                for (int k = 0; k < kRegs; ++k) p[k] = __builtin_fmaf(p[k], kTanhScale, cpre[k]);
+                for (int k = 0; k < kRegs; ++k) p[k] *= kTanhScale;
                 v = readlane(p[0], 0);
                 xstart = xcur;
             }
@@ -730,15 +814,15 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     float tv[kRegs];
 #pragma unroll
                     for (int k = 0; k < kRegs; ++k) tv[k] = ta[k][m % (2 * kTapBatch)];
-                    // closed loop: the accumulators run in units of c = 2 log2(e),
-                    // so tanh(y) = 1 - 2 r with r = 1 / (1 + 2^(c y)); v holds
-                    // position t0+m's accumulator with every input but its own
-                    // pushed (read one step ahead, off the serial path), and the
-                    // serial path of a position is c y = v + c h[0] x (fp32:
-                    // v + (-2 c h[0]) r), exp2, add, rcp.  Position m's own
-                    // lag-0 push is the same fma as c y, so its register ends
-                    // equal to it.
-                    const float xm = RFORM ? rcur : (CLOSED ? xcur : readlane(xb[K], m2));
+                    // closed loop: the accumulators run in units of c = 2 log2(e)
+                    // (the taps hz are c h), so tanh(y) = 1 - 2 r with
+                    // r = 1 / (1 + 2^(c y)); v holds position t0+m's accumulator
+                    // with every input but its own pushed (read one step ahead,
+                    // off the serial path), and the serial path of a position is
+                    // c y = v + c h[0] x, exp2, add, rcp, x = 1 - 2 r.  Position
+                    // m's own lag-0 push is the same fma as c y, so its register
+                    // ends equal to it.
+                    const float xm = CLOSED ? xcur : readlane(xb[K], m2);
                     const float cy = __builtin_fmaf(ch0v, xm, v);
 #pragma unroll
                     for (int k = K; k < kRegs; ++k) {
@@ -757,12 +841,8 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     }
                     if constexpr (CLOSED) {
                         if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
-                        if constexpr (RFORM) {
-                            rcur = tanh_rcp_scaled(cy);
-                        } else {
-                            xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
-                            if constexpr (BF16) xcur = round_bf16(xcur);
-                        }
+                        xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
+                        if constexpr (BF16) xcur = round_bf16(xcur);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -789,7 +869,6 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     xk[k] = lane == 0 ? prev : sh;
                     p[k] *= 1.0f / kTanhScale;
                 }
-                if constexpr (RFORM) xcur = __builtin_fmaf(-2.0f, rcur, 1.0f);   // next block's x[t0]
             } else {
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) xk[k] = xb[k];
@@ -833,8 +912,8 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
                 } else {
                     const int q = ilog2(U);
-                    const FI_GLOBAL V4* spec =
-                        gmem(static_cast<const V4*>(d.spec)) + d.spec_off[q] + c * (int64_t)U;
+                    const FI_GLOBAL V2* spec =
+                        gmem(static_cast<const V2*>(d.spec)) + d.spec_off[q] + c * (int64_t)(U + 2);
                     fft_tile(U, i, row, spec, lbuf, sc, tw, twl, accw, i + kBlk, wmask, L, i == U,
                              stage_x ? xst : nullptr, stage_spec ? sst : nullptr);
                 }
@@ -874,7 +953,7 @@ hipError_t launch_spectra(const DevState& d, int q, void* scd, int64_t scd_strid
     const size_t lds = (size_t)lds_fft_elems(F) * sizeof(Cx<double>);
     if (lds > 65536) (void)hipFuncSetAttribute((const void*)k_spectra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     const int grid = (int)(d.D < slots ? d.D : slots);
-    V4* spec = static_cast<V4*>(d.spec) + d.spec_off[q];
+    V2* spec = static_cast<V2*>(d.spec) + d.spec_off[q];
     hipLaunchKernelGGL(k_spectra, dim3(grid), dim3(64), lds, st, d.hT, d.LS, d.L, d.D, M, spec,
                        static_cast<Cx<double>*>(scd), scd_stride, static_cast<const Cx<double>*>(twd));
     return hipGetLastError();
@@ -892,7 +971,7 @@ hipError_t launch_step(const DevState& d, int64_t t, const void* x_t, float* y_t
     return hipGetLastError();
 }
 
-int tile_fft_lds_bytes() { return (lds_fft_elems(kLdsFftMax) + 128) * (int)sizeof(Cx<float>); }
+int tile_fft_lds_bytes() { return (lds_fft_elems(kLdsFftMax) + kTwLds) * (int)sizeof(Cx<float>); }
 
 hipError_t launch_tile(const DevState& d, int64_t i, hipStream_t st) {
     const int U = (int)(i & -i);
@@ -902,7 +981,7 @@ hipError_t launch_tile(const DevState& d, int64_t i, hipStream_t st) {
     } else {
         const int F = U < kLdsFftMax ? U : kLdsFftMax;
         const int grid = (int)(d.C < d.sc_slots ? d.C : d.sc_slots);
-        hipLaunchKernelGGL(k_tile_fft, dim3(grid), dim3(64), (size_t)(lds_fft_elems(F) + 128) * sizeof(Cx<float>), st, d, i, U);
+        hipLaunchKernelGGL(k_tile_fft, dim3(grid), dim3(64), (size_t)(lds_fft_elems(F) + kTwLds) * sizeof(Cx<float>), st, d, i, U);
     }
     return hipGetLastError();
 }
