@@ -181,15 +181,20 @@ __host__ __device__ constexpr int ct_smallest(int M) {
     return S;
 }
 
+// Stage sources / sinks take a butterfly's first slot `off` and the distance
+// `d` (a constant) of the slot wanted.  In the LDS buffer lp(off + d) =
+// lp(off) + lp(d) for every slot a stage touches (off's low three bits stay
+// below the butterfly stride when that stride is under 8), so only lp(off) is
+// computed at run time.
 template <typename T>
 struct LdsIn {
     const FI_SHARED Cx<T>* b;
-    __device__ __forceinline__ Cx<T> operator()(int p) const { return b[lp(p)]; }
+    __device__ __forceinline__ Cx<T> operator()(int off, int d) const { return (b + lp(off))[lp(d)]; }
 };
 template <typename T>
 struct LdsOut {
     FI_SHARED Cx<T>* b;
-    __device__ __forceinline__ void operator()(int p, Cx<T> v) const { b[lp(p)] = v; }
+    __device__ __forceinline__ void operator()(int off, int d, Cx<T> v) const { (b + lp(off))[lp(d)] = v; }
 };
 
 // Bit reversal of r over log2(R) bits, R in {2, 4, 8}.
@@ -230,7 +235,7 @@ __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const T
             off[g] = (n / Q) * S + jj[g];
             if (NB % kWave == 0 || n < NB) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) v[g][r] = src(off[g] + (INV ? rev_r<R>(r) : r) * Q);
+                for (int r = 0; r < R; ++r) v[g][r] = src(off[g], (INV ? rev_r<R>(r) : r) * Q);
             }
         }
 #pragma unroll
@@ -245,7 +250,7 @@ __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const T
                     if constexpr (S > R) twiddle_apply<R, false>(v[g], tw, S, jj[g]);
                 }
 #pragma unroll
-                for (int r = 0; r < R; ++r) dst(off[g] + (INV ? r : rev_r<R>(r)) * Q, v[g][r]);
+                for (int r = 0; r < R; ++r) dst(off[g], (INV ? r : rev_r<R>(r)) * Q, v[g][r]);
             }
         }
     }
@@ -375,6 +380,74 @@ __device__ __forceinline__ void dit_pass(FI_GLOBAL Cx<T>* sc, int M, int S, TwPt
         }
     }
     wave_sync();
+}
+
+// One radix-R stage (R = 2, 4, 8) of span S over an M-point sequence held in
+// global memory, the in-place Cooley-Tukey stage of ct_stage with run-time
+// sizes: forward (decimation in frequency) stores radix outputs in
+// bit-reversed slot order, the inverse (decimation in time) reads them so;
+// twiddles from the global table.  Two butterflies per lane are in flight.
+template <int R, bool INV, typename T>
+__device__ __forceinline__ void global_stage(FI_GLOBAL Cx<T>* sc, int M, int S, TwPtr<T> tw) {
+    constexpr int G = 2;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int Q = S / R, NB = M / R;
+    const GlobalTw<T> gt{tw};
+#pragma unroll 1
+    for (int n0 = 0; n0 < NB; n0 += kWave * G) {
+        Cx<T> v[G][R];
+        int off[G], jj[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int n = n0 + lane + kWave * g;
+            jj[g] = n % Q;
+            off[g] = (n / Q) * S + jj[g];
+            if (n < NB) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) v[g][r] = sc[off[g] + (INV ? rev_r<R>(r) : r) * Q];
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (n0 + lane + kWave * g < NB) {
+                if constexpr (INV) {
+                    twiddle_apply<R, true>(v[g], gt, S, jj[g]);
+                    dft<R, true>(v[g]);
+                } else {
+                    dft<R, false>(v[g]);
+                    twiddle_apply<R, false>(v[g], gt, S, jj[g]);
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) sc[off[g] + (INV ? r : rev_r<R>(r)) * Q] = v[g][r];
+            }
+        }
+    }
+    wave_sync();
+}
+
+// Forward stages of spans S0, S0/R, ... down to (not including) F, radix 8
+// while it fits; inverse stages of spans F R, ..., up to S0 (the same
+// sequence of sub-problem sizes, reversed).
+template <typename T>
+__device__ __forceinline__ void global_dif(FI_GLOBAL Cx<T>* sc, int M, int S0, int F, TwPtr<T> tw) {
+    for (int S = S0; S > F;) {
+        const int q = S / F;
+        if (q >= 8) { global_stage<8, false>(sc, M, S, tw); S /= 8; }
+        else if (q == 4) { global_stage<4, false>(sc, M, S, tw); S /= 4; }
+        else { global_stage<2, false>(sc, M, S, tw); S /= 2; }
+    }
+}
+template <typename T>
+__device__ __forceinline__ void global_dit(FI_GLOBAL Cx<T>* sc, int M, int S0, int F, TwPtr<T> tw) {
+    // the forward sequence's spans, walked back: radix 8 from the top, the
+    // remainder (4 or 2) last in the forward order, so first here
+    int q = S0 / F, r0 = 1;
+    while (q >= 8) q /= 8;
+    r0 = q;   // 1, 2 or 4
+    int S = F;
+    if (r0 == 4) { S *= 4; global_stage<4, true>(sc, M, S, tw); }
+    else if (r0 == 2) { S *= 2; global_stage<2, true>(sc, M, S, tw); }
+    while (S < S0) { S *= 8; global_stage<8, true>(sc, M, S, tw); }
 }
 
 // Copies n elements between global and LDS (padded) buffers in batches.

@@ -241,7 +241,8 @@ __device__ __forceinline__ void untangle_pair(Cx<float>& A, Cx<float>& B, Cx<flo
 struct TileIn {
     const FI_GLOBAL V2* xs;
     int half;
-    __device__ __forceinline__ Cx<float> operator()(int n) const {
+    __device__ __forceinline__ Cx<float> operator()(int off, int d) const {
+        const int n = off + d;
         if (n < half) {
             const V2 v = xs[n];
             return {v.x, v.y};
@@ -255,7 +256,8 @@ struct TileInTw {
     const FI_GLOBAL V2* xs;
     TwPtr<float> tw;
     int M;
-    __device__ __forceinline__ Cx<float> operator()(int n) const {
+    __device__ __forceinline__ Cx<float> operator()(int off, int d) const {
+        const int n = off + d;
         const V2 v = xs[n];
         return cmul(Cx<float>{v.x, v.y}, twiddle<false>(tw, M, n));
     }
@@ -370,7 +372,8 @@ struct PairsMirror {
 struct TileInLds {
     const FI_SHARED V2* xs;
     int half;
-    __device__ __forceinline__ Cx<float> operator()(int n) const {
+    __device__ __forceinline__ Cx<float> operator()(int off, int d) const {
+        const int n = off + d;
         if (n < half) {
             const V2 v = xs[n];
             return {v.x, v.y};
@@ -477,8 +480,9 @@ __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row,
         wave_sync();
         return;
     }
-    // M > 8192: radix-2 decimation-in-frequency passes over the scratch slot
-    // until F = 4096-point blocks remain; after the blocks' own transforms,
+    // M > 8192: one radix-2 decimation-in-frequency pass fused with the load,
+    // then radix-8 (4, 2) passes over the scratch slot until F = 4096-point
+    // blocks remain; after the blocks' own transforms,
     // position p (block p / F) holds frequency brev(p) over log2(M) bits.
     // Block 0 holds octaves 0 .. log2(F)-1 and block 1 octave log2(F): both
     // hold their own partner frequencies and are transformed, multiplied and
@@ -496,7 +500,7 @@ __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row,
         sc[j + half] = cmul(z, twiddle<false>(tw, M, j));
     }
     wave_sync();
-    for (int S = half; S > F; S >>= 1) dif_pass(sc, M, S, tw);
+    global_dif(sc, M, half, F, tw);   // radix-8 stages down to F-point blocks
     for (int p = 0; p < P; ++p) {
         FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
         copy_to_lds(lbuf, blk, F);
@@ -560,7 +564,7 @@ __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row,
             copy_from_lds(blk, lbuf, F);
         }
     }
-    for (int S = 2 * F; S < M; S <<= 1) dit_pass(sc, M, S, tw);
+    global_dit(sc, M, half, F, tw);
     // last inverse pass (size M) fused with the output; only the upper half
     // (outputs U..2U-1 of the circular convolution) is needed
     tile_output(out, i, half, [sc, tw, half](int j) {
