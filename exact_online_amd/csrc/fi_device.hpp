@@ -11,10 +11,10 @@
 // (natural order in, bit-reversed order out) and decimation in time for the
 // inverse (bit-reversed in, natural out), so a convolution never permutes.
 //
-// Every routine here is executed by ONE wavefront (64 lanes) that owns the
-// buffers it touches; workgroups are one wavefront wide.  Pointers carry their
-// address space (global or LDS) so loads and stores compile to global_* and
-// ds_* instructions rather than flat ones.
+// Every routine here is executed by one team: the kTeam threads (kTeam / 64
+// wavefronts) of a workgroup, which own the buffers they touch.  Pointers
+// carry their address space (global or LDS) so loads and stores compile to
+// global_* and ds_* instructions rather than flat ones.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,6 +28,11 @@
 namespace fi {
 
 constexpr int kWave = 64;
+// Threads of the team that runs one channel's FFT tiles: two wavefronts, so
+// that each SIMD has a second wave to issue from while one waits on LDS or
+// global memory.
+constexpr int kTeamWaves = 2;
+constexpr int kTeam = kTeamWaves * kWave;
 
 template <typename T>
 __device__ __forceinline__ FI_GLOBAL T* gmem(T* p) { return (FI_GLOBAL T*)p; }
@@ -120,6 +125,38 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The thread's index in its team, recomputed where it is used: the empty asm
+// keeps the compiler from hoisting lane-dependent indices and addresses of the
+// many inlined FFT stages out of every loop (they would then all stay live,
+// or be spilled, for the whole kernel).
+__device__ __forceinline__ int team_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// Team barriers.  team_sync orders LDS only (it waits for the team's own LDS
+// operations, not for global loads in flight); team_sync_global also makes
+// every global store before it visible to the whole team after it.
+__device__ __forceinline__ void team_sync() {
+    if constexpr (kTeam == kWave) {
+        wave_sync();
+    } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
+}
+__device__ __forceinline__ void team_sync_global() {
+    if constexpr (kTeam == kWave) {
+        wave_sync();
+    } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
 }
 
 // ------------------------------------------- in-place FFT stages in LDS
@@ -215,33 +252,33 @@ __device__ __forceinline__ constexpr int rev_r(int r) {
 // Storing each radix-R output in bit-reversed slot order makes the whole
 // forward transform end in plain bit-reversed order.
 // Each butterfly reads and writes the same slots, so no staging is needed;
-// a lane processes its butterflies GRP at a time to overlap memory latency.
+// a thread processes its butterflies GRP at a time to overlap memory latency.
 template <int M, int S, bool INV, typename T, typename Src, typename Dst, typename Tw>
 __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const Tw& tw) {
     constexpr int R = ct_radix(S);
     constexpr int Q = S / R;
     constexpr int NB = M / R;
-    constexpr int PER = (NB + kWave - 1) / kWave;
+    constexpr int PER = (NB + kTeam - 1) / kTeam;
     constexpr int GRP = PER < 2 ? PER : 2;
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = team_tid();
 #pragma unroll 1
     for (int u0 = 0; u0 < PER; u0 += GRP) {
         Cx<T> v[GRP][R];
         int off[GRP], jj[GRP];
 #pragma unroll
         for (int g = 0; g < GRP; ++g) {
-            const int n = lane + kWave * (u0 + g);
+            const int n = lane + kTeam * (u0 + g);
             jj[g] = n % Q;
             off[g] = (n / Q) * S + jj[g];
-            if (NB % kWave == 0 || n < NB) {
+            if (NB % kTeam == 0 || n < NB) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) v[g][r] = src(off[g], (INV ? rev_r<R>(r) : r) * Q);
             }
         }
 #pragma unroll
         for (int g = 0; g < GRP; ++g) {
-            const int n = lane + kWave * (u0 + g);
-            if (NB % kWave == 0 || n < NB) {
+            const int n = lane + kTeam * (u0 + g);
+            if (NB % kTeam == 0 || n < NB) {
                 if constexpr (INV) {
                     if constexpr (S > R) twiddle_apply<R, true>(v[g], tw, S, jj[g]);
                     dft<R, true>(v[g]);
@@ -254,7 +291,7 @@ __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const T
             }
         }
     }
-    wave_sync();
+    team_sync();
 }
 
 // Forward M-point FFT (unnormalised), natural order in, bit-reversed order
@@ -322,15 +359,15 @@ constexpr int kBatch = 8;
 
 template <typename T>
 __device__ __forceinline__ void dif_pass(FI_GLOBAL Cx<T>* sc, int M, int S, TwPtr<T> tw) {
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = team_tid();
     const int half = S >> 1, nbf = M >> 1;
 #pragma unroll 1
-    for (int n0 = 0; n0 < nbf; n0 += kWave * kBatch) {
+    for (int n0 = 0; n0 < nbf; n0 += kTeam * kBatch) {
         Cx<T> v0[kBatch], v1[kBatch], w[kBatch];
         int o[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int n = n0 + lane + kWave * u;
+            const int n = n0 + lane + kTeam * u;
             const int b = (n / half) * S, j = n % half;
             o[u] = b + j;
             if (n < nbf) {
@@ -341,27 +378,27 @@ __device__ __forceinline__ void dif_pass(FI_GLOBAL Cx<T>* sc, int M, int S, TwPt
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            if (n0 + lane + kWave * u < nbf) {
+            if (n0 + lane + kTeam * u < nbf) {
                 sc[o[u]] = cadd(v0[u], v1[u]);
                 sc[o[u] + half] = cmul(csub(v0[u], v1[u]), w[u]);
             }
         }
     }
-    wave_sync();
+    team_sync_global();
 }
 
 // Inverse of dif_pass (unnormalised): (v0, v1 w_S^-j) -> (v0+., v0-.).
 template <typename T>
 __device__ __forceinline__ void dit_pass(FI_GLOBAL Cx<T>* sc, int M, int S, TwPtr<T> tw) {
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = team_tid();
     const int half = S >> 1, nbf = M >> 1;
 #pragma unroll 1
-    for (int n0 = 0; n0 < nbf; n0 += kWave * kBatch) {
+    for (int n0 = 0; n0 < nbf; n0 += kTeam * kBatch) {
         Cx<T> v0[kBatch], v1[kBatch], w[kBatch];
         int o[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int n = n0 + lane + kWave * u;
+            const int n = n0 + lane + kTeam * u;
             const int b = (n / half) * S, j = n % half;
             o[u] = b + j;
             if (n < nbf) {
@@ -372,34 +409,34 @@ __device__ __forceinline__ void dit_pass(FI_GLOBAL Cx<T>* sc, int M, int S, TwPt
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            if (n0 + lane + kWave * u < nbf) {
+            if (n0 + lane + kTeam * u < nbf) {
                 const Cx<T> t = cmul(v1[u], cconj(w[u]));
                 sc[o[u]] = cadd(v0[u], t);
                 sc[o[u] + half] = csub(v0[u], t);
             }
         }
     }
-    wave_sync();
+    team_sync_global();
 }
 
 // One radix-R stage (R = 2, 4, 8) of span S over an M-point sequence held in
 // global memory, the in-place Cooley-Tukey stage of ct_stage with run-time
 // sizes: forward (decimation in frequency) stores radix outputs in
 // bit-reversed slot order, the inverse (decimation in time) reads them so;
-// twiddles from the global table.  Two butterflies per lane are in flight.
+// twiddles from the global table.  Two butterflies per thread are in flight.
 template <int R, bool INV, typename T>
 __device__ __forceinline__ void global_stage(FI_GLOBAL Cx<T>* sc, int M, int S, TwPtr<T> tw) {
     constexpr int G = 2;
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = team_tid();
     const int Q = S / R, NB = M / R;
     const GlobalTw<T> gt{tw};
 #pragma unroll 1
-    for (int n0 = 0; n0 < NB; n0 += kWave * G) {
+    for (int n0 = 0; n0 < NB; n0 += kTeam * G) {
         Cx<T> v[G][R];
         int off[G], jj[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const int n = n0 + lane + kWave * g;
+            const int n = n0 + lane + kTeam * g;
             jj[g] = n % Q;
             off[g] = (n / Q) * S + jj[g];
             if (n < NB) {
@@ -409,7 +446,7 @@ __device__ __forceinline__ void global_stage(FI_GLOBAL Cx<T>* sc, int M, int S, 
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            if (n0 + lane + kWave * g < NB) {
+            if (n0 + lane + kTeam * g < NB) {
                 if constexpr (INV) {
                     twiddle_apply<R, true>(v[g], gt, S, jj[g]);
                     dft<R, true>(v[g]);
@@ -422,7 +459,7 @@ __device__ __forceinline__ void global_stage(FI_GLOBAL Cx<T>* sc, int M, int S, 
             }
         }
     }
-    wave_sync();
+    team_sync_global();
 }
 
 // Forward stages of spans S0, S0/R, ... down to (not including) F, radix 8
@@ -453,29 +490,28 @@ __device__ __forceinline__ void global_dit(FI_GLOBAL Cx<T>* sc, int M, int S0, i
 // Copies n elements between global and LDS (padded) buffers in batches.
 template <typename T>
 __device__ __forceinline__ void copy_to_lds(FI_SHARED Cx<T>* lds, const FI_GLOBAL Cx<T>* g, int n) {
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = team_tid();
 #pragma unroll 1
-    for (int q0 = 0; q0 < n; q0 += kWave * kBatch) {
+    for (int q0 = 0; q0 < n; q0 += kTeam * kBatch) {
         Cx<T> v[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int q = q0 + lane + kWave * u;
+            const int q = q0 + lane + kTeam * u;
             if (q < n) v[u] = g[q];
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int q = q0 + lane + kWave * u;
+            const int q = q0 + lane + kTeam * u;
             if (q < n) lds[lp(q)] = v[u];
         }
     }
-    wave_sync();
+    team_sync();
 }
 template <typename T>
 __device__ __forceinline__ void copy_from_lds(FI_GLOBAL Cx<T>* g, const FI_SHARED Cx<T>* lds, int n) {
-    const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll 4
-    for (int q = lane; q < n; q += kWave) g[q] = lds[lp(q)];
-    wave_sync();
+    for (int q = team_tid(); q < n; q += kTeam) g[q] = lds[lp(q)];
+    team_sync_global();
 }
 
 __device__ __forceinline__ int brev_bits(int v, int nb) {

@@ -89,14 +89,14 @@ __global__ void k_twiddles(Cx<double>* twd, Cx<float>* twf, int smax) {
 // packing's halves and the inverse transform's 1/M): entry p < M holds
 // frequency brev(p) (the tile's own bit-reversed position order), entry M
 // holds G[M] (the partner of frequency 0), entry M + 1 is padding.
-__global__ __launch_bounds__(64) void k_spectra(const float* hT, int64_t LS, int64_t L, int64_t D, int M,
+__global__ __launch_bounds__(kTeam) void k_spectra(const float* hT, int64_t LS, int64_t L, int64_t D, int M,
                                                 V2* spec, Cx<double>* scd, int64_t scd_stride,
                                                 const Cx<double>* twd_) {
     extern __shared__ __align__(16) unsigned char smem[];
     FI_SHARED Cx<double>* lbuf = smem_ptr(reinterpret_cast<Cx<double>*>(smem));
     TwPtr<double> twd = gmem(twd_);
     const GlobalTw<double> gtw{twd};
-    const int lane = threadIdx.x;
+    const int lane = team_tid();
     const int F = M < kLdsFftMax ? M : kLdsFftMax;
     const int P = M / F, lm = ilog2(M);
     for (int64_t c = blockIdx.x; c < D; c += gridDim.x) {
@@ -104,12 +104,12 @@ __global__ __launch_bounds__(64) void k_spectra(const float* hT, int64_t LS, int
         auto g = [&](int64_t n) -> double { return (n >= 1 && n < L) ? (double)hr[n] : 0.0; };
         FI_GLOBAL Cx<double>* sc = gmem(scd + (int64_t)blockIdx.x * scd_stride);
         if (P == 1) {
-            for (int n = lane; n < M; n += kWave) lbuf[lp(n)] = Cx<double>{g(2 * n), g(2 * n + 1)};
-            wave_sync();
+            for (int n = lane; n < M; n += kTeam) lbuf[lp(n)] = Cx<double>{g(2 * n), g(2 * n + 1)};
+            team_sync();
             dif_lds_any<double>(M, lbuf, gtw);
         } else {
-            for (int n = lane; n < M; n += kWave) sc[n] = Cx<double>{g(2 * n), g(2 * n + 1)};
-            wave_sync();
+            for (int n = lane; n < M; n += kTeam) sc[n] = Cx<double>{g(2 * n), g(2 * n + 1)};
+            team_sync_global();
             for (int S = M; S > F; S >>= 1) dif_pass(sc, M, S, twd);
             for (int p = 0; p < P; ++p) {
                 copy_to_lds(lbuf, sc + p * F, F);
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(64) void k_spectra(const float* hT, int64_t LS, int
         auto zat = [&](int p) -> Cx<double> { return P == 1 ? lbuf[lp(p)] : sc[p]; };
         FI_GLOBAL V2* out = gmem(spec + c * (int64_t)(M + 2));
         const double scale = 1.0 / (4.0 * (double)M);
-        for (int p = lane; p < M; p += kWave) {
+        for (int p = lane; p < M; p += kTeam) {
             const int k = brev_bits(p, lm);
             const Cx<double> z1 = zat(p), z2c = cconj(zat(mirror_pos(p)));
             const Cx<double> ge = {(z1.x + z2c.x) * 0.5, (z1.y + z2c.y) * 0.5};
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64) void k_spectra(const float* hT, int64_t LS, int
             out[M] = V2{(float)((z0.x - z0.y) * scale), 0.f};
             out[M + 1] = V2{0.f, 0.f};
         }
-        wave_sync();
+        team_sync_global();
     }
 }
 
@@ -159,28 +159,28 @@ struct TileSink {
 };
 
 // Adds w[m] = (a, b) to positions (i + 2m, i + 2m + 1) for m in [0, n):
-// lane-strided chunks of 64 pairs, each chunk wholly in the LDS ring or wholly
-// global; global read-modify-writes go kBatch chunks at a time.
+// the first (wend - i) / 2 pairs into the LDS ring, the rest into the row;
+// global read-modify-writes go kBatch thread-strided chunks at a time.
 template <typename Get>
 __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n, const Get& get) {
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = team_tid();
     int m0 = 0;
     if (s.accw) {
         const int nl = (int)((s.wend - i) / 2) < n ? (int)((s.wend - i) / 2) : n;
 #pragma unroll 1
-        for (; m0 < nl; m0 += kWave) {
-            const int m = m0 + lane;
+        for (int m = lane; m < nl; m += kTeam) {
             const int64_t o = i + 2 * (int64_t)m;
-            if (m < n && o < s.L) {
+            if (o < s.L) {
                 const Cx<float> w = get(m);
                 s.accw[o & s.wmask] += w.x;
                 if (o + 1 < s.L) s.accw[(o + 1) & s.wmask] += w.y;
             }
         }
+        m0 = nl;
     }
     if (s.first) {
 #pragma unroll 4
-        for (int m = m0 + lane; m < n; m += kWave) {
+        for (int m = m0 + lane; m < n; m += kTeam) {
             const int64_t o = i + 2 * (int64_t)m;
             if (o + 1 < s.L) {
                 const Cx<float> w = get(m);
@@ -192,19 +192,19 @@ __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n,
         return;
     }
 #pragma unroll 1
-    for (; m0 < n; m0 += kWave * kBatch) {
+    for (; m0 < n; m0 += kTeam * kBatch) {
         V2 v[kBatch];
         Cx<float> w[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int m = m0 + lane + kWave * u;
+            const int m = m0 + lane + kTeam * u;
             const int64_t o = i + 2 * (int64_t)m;
             if (m < n && o + 1 < s.L) v[u] = *reinterpret_cast<const FI_GLOBAL V2*>(s.row + o);
             if (m < n) w[u] = get(m);
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int m = m0 + lane + kWave * u;
+            const int m = m0 + lane + kTeam * u;
             const int64_t o = i + 2 * (int64_t)m;
             if (m < n && o + 1 < s.L) {
                 *reinterpret_cast<FI_GLOBAL V2*>(s.row + o) = V2{v[u].x + w[u].x, v[u].y + w[u].y};
@@ -286,18 +286,18 @@ struct TwGlobalN {
     __device__ __forceinline__ Cx<float> operator()(int k) const { return twiddle<false>(tw, N, k); }
 };
 
-constexpr int kUntangleBatch = 4;   // pairs per lane per untangle batch
+constexpr int kUntangleBatch = 4;   // pairs per thread per untangle batch
 
-// Filter entries of one batch of NB pairs per lane (pairs n0 + lane + 64u).
+// Filter entries of one batch of NB pairs per thread (pairs n0 + tid + kTeam u).
 template <int NB>
 struct SpecBatch {
     V2 ga[NB], gb[NB];
     template <typename SpecP, typename Pos>
     __device__ __forceinline__ void load(SpecP spec, int n0, int nitems, const Pos& pos) {
-        const int lane = threadIdx.x & (kWave - 1);
+        const int lane = team_tid();
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            const int n = n0 + lane + kWave * u;
+            const int n = n0 + lane + kTeam * u;
             int a, b;
             pos(n < nitems ? n : 0, a, b);
             if (n < nitems) {
@@ -318,17 +318,17 @@ template <int NB, typename SpecP, typename Pos, typename TwF>
 __device__ __forceinline__ void untangle_lds(FI_SHARED Cx<float>* lds, SpecP spec, V2 gM, int nitems,
                                              const Pos& pos, int pos_off, int lbits, const TwF& twf,
                                              SpecBatch<NB> cur) {
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = team_tid();
 #pragma unroll 1
-    for (int n0 = 0; n0 < nitems; n0 += kWave * NB) {
+    for (int n0 = 0; n0 < nitems; n0 += kTeam * NB) {
         SpecBatch<NB> nxt;
-        if (n0 + kWave * NB < nitems) nxt.load(spec, n0 + kWave * NB, nitems, pos);
+        if (n0 + kTeam * NB < nitems) nxt.load(spec, n0 + kTeam * NB, nitems, pos);
         // the pairs of a batch are disjoint: all reads first, then all writes
         Cx<float> za[NB], zb[NB], w[NB];
         int pa[NB], pb[NB];
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            const int n = n0 + lane + kWave * u;
+            const int n = n0 + lane + kTeam * u;
             pos(n < nitems ? n : 0, pa[u], pb[u]);
             za[u] = lds[lp(pa[u])];
             zb[u] = lds[lp(pb[u])];
@@ -342,14 +342,14 @@ __device__ __forceinline__ void untangle_lds(FI_SHARED Cx<float>* lds, SpecP spe
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            if (n0 + lane + kWave * u < nitems) {
+            if (n0 + lane + kTeam * u < nitems) {
                 lds[lp(pa[u])] = za[u];
                 lds[lp(pb[u])] = zb[u];
             }
         }
         cur = nxt;
     }
-    wave_sync();
+    team_sync();
 }
 
 // pairs of a whole bit-reversed transform (or of a block holding its octaves)
@@ -385,13 +385,12 @@ struct TileInLds {
 template <int M, typename XIn, typename SpecP>
 __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP spec, FI_SHARED Cx<float>* lds,
                                              const LdsTw& tw, const TileSink& out) {
-    // spectrum in LDS (staged): batches of up to 8, read after the forward
-    // transform; in global memory: batches of kUntangleBatch, the first one
-    // in flight during the forward transform
+    // batches of kUntangleBatch spectrum entries per thread: staged in LDS,
+    // read after the forward transform; in global memory, the first batch in
+    // flight during the forward transform
     constexpr bool staged = std::is_same<SpecP, const FI_SHARED V2*>::value;
-    constexpr int NALL = M / 2 / kWave + 1;
-    constexpr int NCAP = staged ? 8 : kUntangleBatch;
-    constexpr int NB = NALL < NCAP ? NALL : NCAP;
+    constexpr int NALL = M / 2 / kTeam + 1;
+    constexpr int NB = NALL < kUntangleBatch ? NALL : kUntangleBatch;
     SpecBatch<NB> first;
     if constexpr (!staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
     const V2 gM = spec[M];
@@ -401,7 +400,138 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
     dit_lds<M, ct_smallest(M), float>(lds, tw);
     // point M/2 + m carries outputs 2m, 2m + 1 of the tile
     tile_output(out, i, M / 2, [lds](int m) { return lds[lp(M / 2 + m)]; });
-    wave_sync();
+}
+
+// Tiles of more than kLdsFftMax points (the tile of fft_tile below).  The
+// caller synchronises the team afterwards.
+__device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL float* xblock, const FI_GLOBAL V2* spec,
+                                          FI_SHARED Cx<float>* lbuf, FI_GLOBAL Cx<float>* sc, TwPtr<float> tw,
+                                          const FI_SHARED Cx<float>* twl, FI_GLOBAL float* row, FI_SHARED float* accw,
+                                          int64_t wend, int wmask, int64_t L, bool first) {
+    const TileSink out{row, accw, wend, wmask, L, first};
+    const LdsTw ltw{twl};
+    if (M == 2 * kLdsFftMax) {
+        // One radix-2 decimation-in-frequency pass splits the transform into
+        // halves z[n] + z[n + M/2] and (z[n] - z[n + M/2]) w_M^n; the input's
+        // upper half is the zero padding, so these are z[n] and z[n] w_M^n,
+        // formed while loading.  Each half holds its own partner frequencies
+        // (half 0: octaves 0 .. log2(F)-1, half 1: octave log2(F)), so each
+        // is transformed, untangled and transformed back in LDS; half 0's
+        // result waits in the scratch slot for the last inverse pass, fused
+        // with the output (only outputs M/2 .. M-1 are kept).
+        constexpr int F = kLdsFftMax;
+        const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
+        const V2 gM = spec[M];
+        const TwLdsN twn{twl, 2 * M};
+        SpecBatch<kUntangleBatch> sb0;
+        sb0.load(spec, 0, F / 2 + 1, PairsAll{});
+        dif_lds<F, F, float>(TileIn{xs, F}, lbuf, ltw);
+        untangle_lds<kUntangleBatch>(lbuf, spec, gM, F / 2 + 1, PairsAll{}, 0, ilog2(M), twn, sb0);
+        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        copy_from_lds(sc, lbuf, F);
+        sb0.load(spec + F, 0, F / 2, PairsMirror{F});
+        dif_lds<F, F, float>(TileInTw{xs, tw, M}, lbuf, ltw);
+        untangle_lds<kUntangleBatch>(lbuf, spec + F, gM, F / 2, PairsMirror{F}, F, ilog2(M), twn, sb0);
+        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        tile_output(out, i, F, [sc, lbuf, tw](int j) {
+            const Cx<float> v0 = sc[j];
+            const Cx<float> v1 = cmul(lbuf[lp(j)], twiddle<true>(tw, 2 * F, j));
+            return csub(v0, v1);
+        });
+        return;
+    }
+    // M > 8192: one radix-2 decimation-in-frequency pass fused with the load,
+    // then radix-8 (4, 2) passes over the scratch slot until F = 4096-point
+    // blocks remain; after the blocks' own transforms,
+    // position p (block p / F) holds frequency brev(p) over log2(M) bits.
+    // Block 0 holds octaves 0 .. log2(F)-1 and block 1 octave log2(F): both
+    // hold their own partner frequencies and are transformed, multiplied and
+    // transformed back in one LDS visit.  Blocks b >= 2 pair with the mirror
+    // block of their octave through the scratch slot.
+    const int lane = team_tid();
+    const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
+    constexpr int F = kLdsFftMax;
+    const int P = M / F;
+    const int half = M >> 1;
+    for (int j = lane; j < half; j += kTeam) {   // first pass fused with the load (upper half is 0)
+        const V2 v = xs[j];
+        const Cx<float> z = {v.x, v.y};
+        sc[j] = z;
+        sc[j + half] = cmul(z, twiddle<false>(tw, M, j));
+    }
+    team_sync_global();
+    global_dif(sc, M, half, F, tw);   // radix-8 stages down to F-point blocks
+    for (int p = 0; p < P; ++p) {
+        FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
+        copy_to_lds(lbuf, blk, F);
+        dif_lds<F, F, float>(LdsIn<float>{lbuf}, lbuf, ltw);
+        if (p <= 1) {
+            const TwGlobalN twn{tw, 2 * M};
+            SpecBatch<kUntangleBatch> sb0;
+            if (p == 0) {
+                sb0.load(spec, 0, F / 2 + 1, PairsAll{});
+                untangle_lds<kUntangleBatch>(lbuf, spec, spec[M], F / 2 + 1, PairsAll{}, 0, ilog2(M), twn, sb0);
+            } else {
+                sb0.load(spec + F, 0, F / 2, PairsMirror{F});
+                untangle_lds<kUntangleBatch>(lbuf, spec + F, spec[M], F / 2, PairsMirror{F}, F, ilog2(M), twn, sb0);
+            }
+            dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        }
+        copy_from_lds(blk, lbuf, F);
+    }
+    if (P > 2) {
+        for (int p = 2; p < P; ++p) {
+            const int a = 31 - __builtin_clz(p);   // octave of block p: blocks [2^a, 2^(a+1))
+            const int pp = 3 * (1 << a) - 1 - p;
+            if (pp < p) continue;
+            const int lm = ilog2(M);
+#pragma unroll 1
+            for (int k0 = 0; k0 < F; k0 += kTeam * kBatch) {
+                V2 sa[kBatch], sb[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int k = k0 + lane + kTeam * u;
+                    sa[u] = spec[(int64_t)p * F + k];
+                    sb[u] = spec[(int64_t)pp * F + (F - 1 - k)];
+                }
+                Cx<float> za[kBatch], zb[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int k = k0 + lane + kTeam * u;
+                    za[u] = sc[p * F + k];
+                    zb[u] = sc[pp * F + (F - 1 - k)];
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int k = k0 + lane + kTeam * u;
+                    const int fa = brev_bits(p * F + k, lm);   // never 0 in blocks >= 2
+                    untangle_pair(za[u], zb[u], Cx<float>{sa[u].x, sa[u].y}, Cx<float>{sb[u].x, sb[u].y},
+                                  twiddle<false>(tw, 2 * M, fa));
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int k = k0 + lane + kTeam * u;
+                    sc[p * F + k] = za[u];
+                    sc[pp * F + (F - 1 - k)] = zb[u];
+                }
+            }
+        }
+        team_sync_global();
+        for (int p = 2; p < P; ++p) {
+            FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
+            copy_to_lds(lbuf, blk, F);
+            dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+            copy_from_lds(blk, lbuf, F);
+        }
+    }
+    global_dit(sc, M, half, F, tw);
+    // last inverse pass (size M) fused with the output; only the upper half
+    // (outputs U..2U-1 of the circular convolution) is needed
+    tile_output(out, i, half, [sc, tw, half](int j) {
+        const Cx<float> v0 = sc[j];
+        const Cx<float> v1 = cmul(sc[j + half], twiddle<true>(tw, 2 * half, j));
+        return csub(v0, v1);
+    });
 }
 
 // The tile tau(x, [i-U, i), h, [i, i+U)) as the circular convolution of
@@ -414,6 +544,7 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
 // xst, when not null, holds the input block x[i-U, i) in LDS (staged by the
 // caller), and spec_lds the tile's spectrum entries.
 // The sink's fields come as separate arguments (registers, not a stack copy).
+// The team synchronises after the call (no barrier at its end).
 __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row, const FI_GLOBAL V2* spec,
                                       FI_SHARED Cx<float>* lbuf, FI_GLOBAL Cx<float>* sc, TwPtr<float> tw,
                                       const FI_SHARED Cx<float>* twl, FI_SHARED float* accw, int64_t wend,
@@ -449,130 +580,7 @@ __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row,
         case 4096: fft_tile_lds<4096>(i, xg, spec, lbuf, ltw, out); return;
         default: break;
     }
-    if (M == 2 * kLdsFftMax) {
-        // One radix-2 decimation-in-frequency pass splits the transform into
-        // halves z[n] + z[n + M/2] and (z[n] - z[n + M/2]) w_M^n; the input's
-        // upper half is the zero padding, so these are z[n] and z[n] w_M^n,
-        // formed while loading.  Each half holds its own partner frequencies
-        // (half 0: octaves 0 .. log2(F)-1, half 1: octave log2(F)), so each
-        // is transformed, untangled and transformed back in LDS; half 0's
-        // result waits in the scratch slot for the last inverse pass, fused
-        // with the output (only outputs M/2 .. M-1 are kept).
-        constexpr int F = kLdsFftMax;
-        const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
-        const V2 gM = spec[M];
-        const TwLdsN twn{twl, 2 * M};
-        SpecBatch<kUntangleBatch> first;
-        first.load(spec, 0, F / 2 + 1, PairsAll{});
-        dif_lds<F, F, float>(TileIn{xs, F}, lbuf, ltw);
-        untangle_lds<kUntangleBatch>(lbuf, spec, gM, F / 2 + 1, PairsAll{}, 0, ilog2(M), twn, first);
-        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
-        copy_from_lds(sc, lbuf, F);
-        first.load(spec + F, 0, F / 2, PairsMirror{F});
-        dif_lds<F, F, float>(TileInTw{xs, tw, M}, lbuf, ltw);
-        untangle_lds<kUntangleBatch>(lbuf, spec + F, gM, F / 2, PairsMirror{F}, F, ilog2(M), twn, first);
-        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
-        tile_output(out, i, F, [sc, lbuf, tw](int j) {
-            const Cx<float> v0 = sc[j];
-            const Cx<float> v1 = cmul(lbuf[lp(j)], twiddle<true>(tw, 2 * F, j));
-            return csub(v0, v1);
-        });
-        wave_sync();
-        return;
-    }
-    // M > 8192: one radix-2 decimation-in-frequency pass fused with the load,
-    // then radix-8 (4, 2) passes over the scratch slot until F = 4096-point
-    // blocks remain; after the blocks' own transforms,
-    // position p (block p / F) holds frequency brev(p) over log2(M) bits.
-    // Block 0 holds octaves 0 .. log2(F)-1 and block 1 octave log2(F): both
-    // hold their own partner frequencies and are transformed, multiplied and
-    // transformed back in one LDS visit.  Blocks b >= 2 pair with the mirror
-    // block of their octave through the scratch slot.
-    const int lane = threadIdx.x & (kWave - 1);
-    const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
-    constexpr int F = kLdsFftMax;
-    const int P = M / F;
-    const int half = M >> 1;
-    for (int j = lane; j < half; j += kWave) {   // first pass fused with the load (upper half is 0)
-        const V2 v = xs[j];
-        const Cx<float> z = {v.x, v.y};
-        sc[j] = z;
-        sc[j + half] = cmul(z, twiddle<false>(tw, M, j));
-    }
-    wave_sync();
-    global_dif(sc, M, half, F, tw);   // radix-8 stages down to F-point blocks
-    for (int p = 0; p < P; ++p) {
-        FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
-        copy_to_lds(lbuf, blk, F);
-        dif_lds<F, F, float>(LdsIn<float>{lbuf}, lbuf, ltw);
-        if (p <= 1) {
-            const TwGlobalN twn{tw, 2 * M};
-            SpecBatch<kUntangleBatch> first;
-            if (p == 0) {
-                first.load(spec, 0, F / 2 + 1, PairsAll{});
-                untangle_lds<kUntangleBatch>(lbuf, spec, spec[M], F / 2 + 1, PairsAll{}, 0, ilog2(M), twn, first);
-            } else {
-                first.load(spec + F, 0, F / 2, PairsMirror{F});
-                untangle_lds<kUntangleBatch>(lbuf, spec + F, spec[M], F / 2, PairsMirror{F}, F, ilog2(M), twn, first);
-            }
-            dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
-        }
-        copy_from_lds(blk, lbuf, F);
-    }
-    if (P > 2) {
-        for (int p = 2; p < P; ++p) {
-            const int a = 31 - __builtin_clz(p);   // octave of block p: blocks [2^a, 2^(a+1))
-            const int pp = 3 * (1 << a) - 1 - p;
-            if (pp < p) continue;
-            const int lm = ilog2(M);
-#pragma unroll 1
-            for (int k0 = 0; k0 < F; k0 += kWave * kBatch) {
-                V2 sa[kBatch], sb[kBatch];
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int k = k0 + lane + kWave * u;
-                    sa[u] = spec[(int64_t)p * F + k];
-                    sb[u] = spec[(int64_t)pp * F + (F - 1 - k)];
-                }
-                Cx<float> za[kBatch], zb[kBatch];
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int k = k0 + lane + kWave * u;
-                    za[u] = sc[p * F + k];
-                    zb[u] = sc[pp * F + (F - 1 - k)];
-                }
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int k = k0 + lane + kWave * u;
-                    const int fa = brev_bits(p * F + k, lm);   // never 0 in blocks >= 2
-                    untangle_pair(za[u], zb[u], Cx<float>{sa[u].x, sa[u].y}, Cx<float>{sb[u].x, sb[u].y},
-                                  twiddle<false>(tw, 2 * M, fa));
-                }
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int k = k0 + lane + kWave * u;
-                    sc[p * F + k] = za[u];
-                    sc[pp * F + (F - 1 - k)] = zb[u];
-                }
-            }
-        }
-        wave_sync();
-        for (int p = 2; p < P; ++p) {
-            FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
-            copy_to_lds(lbuf, blk, F);
-            dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
-            copy_from_lds(blk, lbuf, F);
-        }
-    }
-    global_dit(sc, M, half, F, tw);
-    // last inverse pass (size M) fused with the output; only the upper half
-    // (outputs U..2U-1 of the circular convolution) is needed
-    tile_output(out, i, half, [sc, tw, half](int j) {
-        const Cx<float> v0 = sc[j];
-        const Cx<float> v1 = cmul(sc[j + half], twiddle<true>(tw, 2 * half, j));
-        return csub(v0, v1);
-    });
-    wave_sync();
+    fft_tile_big(M, i, xblock, spec, lbuf, sc, tw, twl, row, accw, wend, wmask, L, first);
 }
 
 // ================================================================ fi_step
@@ -608,7 +616,8 @@ __global__ void k_tile_direct(float* state, const float* hT, int64_t LS, int64_t
 // Fills the twiddle table A[64] = w_64^a, B[64] = w_4096^b, C[4] = w_16384^r (fp64
 // sincospi of exact dyadic arguments, rounded to fp32).
 __device__ __forceinline__ void fill_lds_twiddles(FI_SHARED Cx<float>* t) {
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = threadIdx.x;
+    if (lane >= 64) return;
     double sn, cs;
     sincospi(2.0 * lane / 64.0, &sn, &cs);
     t[lane] = Cx<float>{(float)cs, (float)-sn};
@@ -620,12 +629,12 @@ __device__ __forceinline__ void fill_lds_twiddles(FI_SHARED Cx<float>* t) {
     }
 }
 
-__global__ __launch_bounds__(64) void k_tile_fft(DevState d, int64_t i, int U) {
+__global__ __launch_bounds__(kTeam) void k_tile_fft(DevState d, int64_t i, int U) {
     extern __shared__ __align__(16) unsigned char smem[];
     FI_SHARED Cx<float>* twl = smem_ptr(reinterpret_cast<Cx<float>*>(smem));
     FI_SHARED Cx<float>* lbuf = twl + kTwLds;
     fill_lds_twiddles(twl);
-    wave_sync();
+    team_sync();
     const int q = ilog2(U);  // level
     const FI_GLOBAL V2* spec = gmem(static_cast<const V2*>(d.spec)) + d.spec_off[q];
     for (int64_t ch = blockIdx.x; ch < d.C; ch += gridDim.x) {
@@ -633,12 +642,15 @@ __global__ __launch_bounds__(64) void k_tile_fft(DevState d, int64_t i, int U) {
         FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)blockIdx.x * d.sc_stride;
         fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)(U + 2), lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl,
                  nullptr, i, 0, d.L, false, nullptr, nullptr);
+        team_sync_global();
     }
 }
 
 // ============================================================ persistent run
-// One wavefront per channel runs all L positions, in blocks of kBlk = 256
-// positions; lane r holds positions t0 + 64k + r (k < kRegs) in registers.
+// One team per channel runs all L positions, in blocks of kBlk = 256
+// positions.  Its first wavefront runs the serial part (lane r holds
+// positions t0 + 64k + r, k < kRegs, in registers); the whole team runs the
+// tiles.
 //  * Within a block, the red cells and every tile of side < 256 -- these lie
 //    inside one 256-position block and together cover its lower triangle --
 //    run in registers: once x[t] is known it is pushed, times the filter tap
@@ -675,8 +687,7 @@ struct RunArgs {
 __device__ __forceinline__ void direct_tile_lds(int64_t i, int U, const FI_SHARED float* xring, int xmask,
                                                 const FI_SHARED float* htap, FI_SHARED float* accw, int wmask,
                                                 int64_t L) {
-    const int lane = threadIdx.x & (kWave - 1);
-    for (int r = lane; r < U; r += kWave) {
+    for (int r = team_tid(); r < U; r += kTeam) {
         float acc = 0.f;
         const FI_SHARED float* hp = htap + U + r;
 #pragma unroll 8
@@ -692,7 +703,7 @@ __device__ __forceinline__ void direct_tile_lds(int64_t i, int U, const FI_SHARE
 inline int run_lds_floats(const DevState& d) { return d.fftreg / 4 + (d.T >= kBlk ? d.XR + 2 * d.T : 0); }
 
 template <bool CLOSED, bool BF16>
-__global__ __launch_bounds__(64) void k_run(RunArgs a) {
+__global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWaves))) void k_run(RunArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ Cx<float> s_tw[kTwLds];  // twiddles A[64] = w_64^a, B[64] = w_4096^b, C[4] = w_16384^r
     __shared__ float s_ring[kBlk];      // accumulators of positions [t0, t0+W)
@@ -705,7 +716,12 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
     FI_SHARED float* xring = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.fftreg);  // direct tiles only
     FI_SHARED float* htap = xring + d.XR;    // h[0 .. 2T), direct tiles only
     const bool direct = d.T >= kBlk;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    // The team's first wavefront runs the chain; the others wait at the
+    // barrier before each tile and share the tile's work (the test is uniform
+    // per wavefront, so it is a branch, not a mask).
+    const bool chain_wave = __builtin_amdgcn_readfirstlane(tid) < kWave;
     const int wmask = kBlk - 1, xmask = d.XR - 1;
     const int64_t L = d.L, D = d.D;
     const int G = gridDim.x, bid = blockIdx.x;
@@ -721,46 +737,37 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
         const int64_t b = ch / D, c = ch % D;
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         const FI_GLOBAL float* hrow = gmem(d.hT + c * d.LS);
-        for (int q = lane; q < kBlk; q += kWave) accw[q] = 0.f;
+        team_sync();   // the previous channel's last chain is done with the taps and the ring
+        for (int q = tid; q < kBlk; q += kTeam) accw[q] = 0.f;
         // taps: h (open loop); c h (closed loop, c = 2 log2 e, see below)
         const float tap_scale = CLOSED ? kTanhScale : 1.0f;
-        for (int q = lane; q < kWave + kBlk; q += kWave)
+        for (int q = tid; q < kWave + kBlk; q += kTeam)
             hz[q] = (q >= kWave && q - kWave < L) ? tap_scale * hrow[q - kWave] : 0.f;
         if (direct)
-            for (int q = lane; q < 2 * d.T; q += kWave) htap[q] = q < L ? hrow[q] : 0.f;
-        wave_sync();
+            for (int q = tid; q < 2 * d.T; q += kTeam) htap[q] = q < L ? hrow[q] : 0.f;
+        team_sync();
         const float ch0v = hz[kWave];   // closed loop: c h[0]
 
         float xcur = 0.f;        // closed loop: x at the next position (uniform)
         float xbn[kRegs];        // open loop: inputs of the next block
 #pragma unroll
         for (int k = 0; k < kRegs; ++k) xbn[k] = 0.f;
-        if constexpr (CLOSED) {
-            xcur = load_io<BF16>(a.x_in, b * D + c);
-        } else {
-#pragma unroll
-            for (int k = 0; k < kRegs; ++k) {
-                const int64_t n = kWave * k + lane;
-                if (n < L) xbn[k] = load_io<BF16>(a.x_in, (b * L + n) * D + c);
-            }
-        }
-        // nothing in flight when the block loop starts, so the waits inside it
-        // only cover what each block issues
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        for (int64_t t0 = 0; t0 < L; t0 += kBlk) {
-            float xb[kRegs], p[kRegs], xk[kRegs];
-#pragma unroll
-            for (int k = 0; k < kRegs; ++k) {
-                xb[k] = xbn[k];
-                p[k] = accw[(kWave * k + lane) & wmask];   // t0 is a multiple of the ring size
-            }
-            if constexpr (!CLOSED) {
+        if (chain_wave) {
+            if constexpr (CLOSED) {
+                xcur = load_io<BF16>(a.x_in, b * D + c);
+            } else {
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) {
-                    const int64_t n = t0 + kBlk + kWave * k + lane;
-                    xbn[k] = n < L ? load_io<BF16>(a.x_in, (b * L + n) * D + c) : 0.f;
+                    const int64_t n = kWave * k + lane;
+                    if (n < L) xbn[k] = load_io<BF16>(a.x_in, (b * L + n) * D + c);
                 }
             }
+            // nothing in flight when the block loop starts, so the waits inside it
+            // only cover what each block issues
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
+        for (int64_t t0 = 0; t0 < L; t0 += kBlk) {
+            float p[kRegs], xk[kRegs];
             // the next tile's spectrum and older input block go straight to the
             // idle LDS FFT region while the chain runs
             const int64_t inext = t0 + kBlk;
@@ -769,131 +776,9 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
             const bool stage_spec = Un > d.T && Un <= kStageSpecMax;
             FI_SHARED float* xst = reinterpret_cast<FI_SHARED float*>(lbuf + lds_fft_elems(Un));
             FI_SHARED V2* sst = reinterpret_cast<FI_SHARED V2*>(xst + Un);
-            if (stage_spec) {   // Un + 2 entries of 8 bytes, 16 bytes per lane
-                const FI_GLOBAL V4* sp = reinterpret_cast<const FI_GLOBAL V4*>(
-                    gmem(static_cast<const V2*>(d.spec)) + d.spec_off[ilog2(Un)] + c * (int64_t)(Un + 2));
-                FI_SHARED V4* sd = reinterpret_cast<FI_SHARED V4*>(sst);
-                const int n16 = (Un + 2) / 2;
-                for (int k = 0; k < n16; k += kWave)
-                    if (k + lane < n16)
-                        __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(sp + k + lane), (FI_SHARED void*)(sd + k), 16, 0, 0);
-            }
-            if (stage_x) {
-                for (int k = 0; k < Un - kBlk; k += kWave)
-                    __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(row + (inext - Un) + k + lane),
-                                                     (FI_SHARED void*)(xst + k), 4, 0, 0);
-            }
-            // The accumulators of the next block's positions, from the row:
-            // some earlier tile left them outside its ring exactly when a bit
-            // of base other than its lowest is set at or above 2 kBlk (the
-            // tile of that bit's level covered them, its ring did not).
-            const int64_t base = t0 + kBlk;
-            const bool nx_in_row = ((base & (base - 1)) >> (kLog2Blk + 1)) != 0;
-            float nx[kRegs];
-#pragma unroll
-            for (int k = 0; k < kRegs; ++k) {
-                const int64_t pn = base + kWave * k + lane;
-                nx[k] = (nx_in_row && pn < L) ? row[pn] : 0.f;
-            }
-            const FI_SHARED float* hz0 = hz + kWave + lane;   // hz0[64k - m]: tap of position 64k + lane, input m
-            float ta[kRegs][2 * kTapBatch];
-#pragma unroll
-            for (int n = 0; n < kTapBatch; ++n)
-#pragma unroll
-                for (int k = 0; k < kRegs; ++k) ta[k][n] = hz0[kWave * k - n];
-            float v = 0.f;
-            float xstart = 0.f;
-            if constexpr (CLOSED) {
-#pragma unroll
-                for (int k = 0; k < kRegs; ++k) p[k] *= kTanhScale;
-                v = readlane(p[0], 0);
-                xstart = xcur;
-            }
-            // one 64-step segment of the chain (steps 64K .. 64K+63)
-            auto segment = [&](auto kc) {
-                constexpr int K = decltype(kc)::value;
-#pragma unroll
-                for (int m2 = 0; m2 < kWave; ++m2) {
-                    const int m = kWave * K + m2;
-                    float tv[kRegs];
-#pragma unroll
-                    for (int k = 0; k < kRegs; ++k) tv[k] = ta[k][m % (2 * kTapBatch)];
-                    // closed loop: the accumulators run in units of c = 2 log2(e)
-                    // (the taps hz are c h), so tanh(y) = 1 - 2 r with
-                    // r = 1 / (1 + 2^(c y)); v holds position t0+m's accumulator
-                    // with every input but its own pushed (read one step ahead,
-                    // off the serial path), and the serial path of a position is
-                    // c y = v + c h[0] x, exp2, add, rcp, x = 1 - 2 r.  Position
-                    // m's own lag-0 push is the same fma as c y, so its register
-                    // ends equal to it.
-                    const float xm = CLOSED ? xcur : readlane(xb[K], m2);
-                    const float cy = __builtin_fmaf(ch0v, xm, v);
-#pragma unroll
-                    for (int k = K; k < kRegs; ++k) {
-                        p[k] = __builtin_fmaf(tv[k], xm, p[k]);
-                        pin(p[k]);   // push now: x[t] is then dead after this step
-                    }
-                    if (m % kTapBatch == 0 && m + kTapBatch < kBlk) {
-                        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                        for (int n2 = 0; n2 < kTapBatch; ++n2) {
-                            const int n = m + kTapBatch + n2;
-#pragma unroll
-                            for (int k = 0; k < kRegs; ++k)
-                                if (n < kWave * (k + 1)) ta[k][n % (2 * kTapBatch)] = hz0[kWave * k - n];
-                        }
-                    }
-                    if constexpr (CLOSED) {
-                        if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
-                        xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
-                        if constexpr (BF16) xcur = round_bf16(xcur);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            };
-            static_assert(kRegs == 4, "the chain below runs four segments");
-            segment(std::integral_constant<int, 0>{});
-            segment(std::integral_constant<int, 1>{});
-            segment(std::integral_constant<int, 2>{});
-            segment(std::integral_constant<int, 3>{});
-            if constexpr (CLOSED) {
-                // The inputs of the block, one per lane: the register of
-                // position t ended as the same fma as the chain's c y[t], so
-                // the same exp2 / rcp / fma on it gives back x[t+1] exactly.
-                float f[kRegs];
-#pragma unroll
-                for (int k = 0; k < kRegs; ++k) {
-                    f[k] = __builtin_fmaf(-2.0f, tanh_rcp_scaled(p[k]), 1.0f);
-                    if constexpr (BF16) f[k] = round_bf16(f[k]);
-                }
-#pragma unroll
-                for (int k = 0; k < kRegs; ++k) {
-                    const float prev = k == 0 ? xstart : readlane(f[k - 1], kWave - 1);
-                    const float sh = __shfl_up(f[k], 1);
-                    xk[k] = lane == 0 ? prev : sh;
-                    p[k] *= 1.0f / kTanhScale;
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < kRegs; ++k) xk[k] = xb[k];
-            }
-            // Everything this block loaded (staging, next accumulators) was
-            // issued a whole chain ago: wait for it here, before the stores
-            // below (stores count in the same counter, and their
-            // acknowledgement is not needed before the tile).
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-            // p now holds y of the block (lane m's accumulator stopped
-            // changing at step m: later pushes carry a zero tap there)
-#pragma unroll
-            for (int k = 0; k < kRegs; ++k) {
-                const int64_t tl = t0 + kWave * k + lane;
-                if (direct) xring[tl & xmask] = xk[k];
-                if (stage_x) xst[Un - kBlk + kWave * k + lane] = xk[k];   // completes the staged input block
-                accw[(kWave * k + lane) & wmask] = nx[k];  // slot of position t now holds position t + W
-            }
+            const bool row_input = Un > d.T && !stage_x;   // next tile: FFT reading the row
             // y, x_out and the input history: before a tile that reads its
             // input block from the row, after one that has it staged in LDS
-            // (the tile call waits for every outstanding store)
             auto store_block = [&]() {
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) {
@@ -906,9 +791,150 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     }
                 }
             };
-            const bool row_input = Un > d.T && !stage_x;   // next tile: FFT reading the row
-            if (row_input) store_block();
-            wave_sync();
+            if (chain_wave) {
+                // the serial chain goes first wherever it shares a SIMD with
+                // another team's tile work
+                __builtin_amdgcn_s_setprio(2);
+                float xb[kRegs];
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) {
+                    xb[k] = xbn[k];
+                    p[k] = accw[(kWave * k + lane) & wmask];   // t0 is a multiple of the ring size
+                }
+                if constexpr (!CLOSED) {
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) {
+                        const int64_t n = t0 + kBlk + kWave * k + lane;
+                        xbn[k] = n < L ? load_io<BF16>(a.x_in, (b * L + n) * D + c) : 0.f;
+                    }
+                }
+                if (stage_spec) {   // Un + 2 entries of 8 bytes, 16 bytes per lane
+                    const FI_GLOBAL V4* sp = reinterpret_cast<const FI_GLOBAL V4*>(
+                        gmem(static_cast<const V2*>(d.spec)) + d.spec_off[ilog2(Un)] + c * (int64_t)(Un + 2));
+                    FI_SHARED V4* sd = reinterpret_cast<FI_SHARED V4*>(sst);
+                    const int n16 = (Un + 2) / 2;
+                    for (int k = 0; k < n16; k += kWave)
+                        if (k + lane < n16)
+                            __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(sp + k + lane), (FI_SHARED void*)(sd + k), 16, 0, 0);
+                }
+                if (stage_x) {
+                    for (int k = 0; k < Un - kBlk; k += kWave)
+                        __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(row + (inext - Un) + k + lane),
+                                                         (FI_SHARED void*)(xst + k), 4, 0, 0);
+                }
+                // The accumulators of the next block's positions, from the row:
+                // some earlier tile left them outside its ring exactly when a bit
+                // of base other than its lowest is set at or above 2 kBlk (the
+                // tile of that bit's level covered them, its ring did not).
+                const int64_t base = t0 + kBlk;
+                const bool nx_in_row = ((base & (base - 1)) >> (kLog2Blk + 1)) != 0;
+                float nx[kRegs];
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) {
+                    const int64_t pn = base + kWave * k + lane;
+                    nx[k] = (nx_in_row && pn < L) ? row[pn] : 0.f;
+                }
+                const FI_SHARED float* hz0 = hz + kWave + lane;   // hz0[64k - m]: tap of position 64k + lane, input m
+                float ta[kRegs][2 * kTapBatch];
+#pragma unroll
+                for (int n = 0; n < kTapBatch; ++n)
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) ta[k][n] = hz0[kWave * k - n];
+                float v = 0.f;
+                float xstart = 0.f;
+                if constexpr (CLOSED) {
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) p[k] *= kTanhScale;
+                    v = readlane(p[0], 0);
+                    xstart = xcur;
+                }
+                // one 64-step segment of the chain (steps 64K .. 64K+63)
+                auto segment = [&](auto kc) {
+                    constexpr int K = decltype(kc)::value;
+#pragma unroll
+                    for (int m2 = 0; m2 < kWave; ++m2) {
+                        const int m = kWave * K + m2;
+                        float tv[kRegs];
+#pragma unroll
+                        for (int k = 0; k < kRegs; ++k) tv[k] = ta[k][m % (2 * kTapBatch)];
+                        // closed loop: the accumulators run in units of c = 2 log2(e)
+                        // (the taps hz are c h), so tanh(y) = 1 - 2 r with
+                        // r = 1 / (1 + 2^(c y)); v holds position t0+m's accumulator
+                        // with every input but its own pushed (read one step ahead,
+                        // off the serial path), and the serial path of a position is
+                        // c y = v + c h[0] x, exp2, add, rcp, x = 1 - 2 r.  Position
+                        // m's own lag-0 push is the same fma as c y, so its register
+                        // ends equal to it.
+                        const float xm = CLOSED ? xcur : readlane(xb[K], m2);
+                        const float cy = __builtin_fmaf(ch0v, xm, v);
+#pragma unroll
+                        for (int k = K; k < kRegs; ++k) {
+                            p[k] = __builtin_fmaf(tv[k], xm, p[k]);
+                            pin(p[k]);   // push now: x[t] is then dead after this step
+                        }
+                        if (m % kTapBatch == 0 && m + kTapBatch < kBlk) {
+                            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                            for (int n2 = 0; n2 < kTapBatch; ++n2) {
+                                const int n = m + kTapBatch + n2;
+#pragma unroll
+                                for (int k = 0; k < kRegs; ++k)
+                                    if (n < kWave * (k + 1)) ta[k][n % (2 * kTapBatch)] = hz0[kWave * k - n];
+                            }
+                        }
+                        if constexpr (CLOSED) {
+                            if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
+                            xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
+                            if constexpr (BF16) xcur = round_bf16(xcur);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                };
+                static_assert(kRegs == 4, "the chain below runs four segments");
+                segment(std::integral_constant<int, 0>{});
+                segment(std::integral_constant<int, 1>{});
+                segment(std::integral_constant<int, 2>{});
+                segment(std::integral_constant<int, 3>{});
+                if constexpr (CLOSED) {
+                    // The inputs of the block, one per lane: the register of
+                    // position t ended as the same fma as the chain's c y[t], so
+                    // the same exp2 / rcp / fma on it gives back x[t+1] exactly.
+                    float f[kRegs];
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) {
+                        f[k] = __builtin_fmaf(-2.0f, tanh_rcp_scaled(p[k]), 1.0f);
+                        if constexpr (BF16) f[k] = round_bf16(f[k]);
+                    }
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) {
+                        const float prev = k == 0 ? xstart : readlane(f[k - 1], kWave - 1);
+                        const float sh = __shfl_up(f[k], 1);
+                        xk[k] = lane == 0 ? prev : sh;
+                        p[k] *= 1.0f / kTanhScale;
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) xk[k] = xb[k];
+                }
+                // Everything this block loaded (staging, next accumulators) was
+                // issued a whole chain ago: wait for it here, before the stores
+                // below (stores count in the same counter, and their
+                // acknowledgement is not needed before the tile).
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                // p now holds y of the block (lane m's accumulator stopped
+                // changing at step m: later pushes carry a zero tap there)
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) {
+                    const int64_t tl = t0 + kWave * k + lane;
+                    if (direct) xring[tl & xmask] = xk[k];
+                    if (stage_x) xst[Un - kBlk + kWave * k + lane] = xk[k];   // completes the staged input block
+                    accw[(kWave * k + lane) & wmask] = nx[k];  // slot of position t now holds position t + W
+                }
+                if (row_input) store_block();
+                __builtin_amdgcn_s_setprio(0);
+            }
+            // the whole team sees the block's LDS writes and its stores
+            team_sync_global();
             const int64_t i = t0 + kBlk;
             if (i < L) {
                 const int U = (int)(i & -i);
@@ -921,9 +947,15 @@ __global__ __launch_bounds__(64) void k_run(RunArgs a) {
                     fft_tile(U, i, row, spec, lbuf, sc, tw, twl, accw, i + kBlk, wmask, L, i == U,
                              stage_x ? xst : nullptr, stage_spec ? sst : nullptr);
                 }
-                wave_sync();
+                // The chain wavefront reads the ring and (a block later) the row
+                // positions this tile wrote: the other wavefronts' stores must
+                // be complete; the chain wavefront's own stores stay in flight
+                // (its later loads of the same addresses come after them).
+                if (!chain_wave) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                team_sync();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
             }
-            if (!row_input) store_block();
+            if (chain_wave && !row_input) store_block();
         }
     }
 }
@@ -958,7 +990,7 @@ hipError_t launch_spectra(const DevState& d, int q, void* scd, int64_t scd_strid
     if (lds > 65536) (void)hipFuncSetAttribute((const void*)k_spectra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     const int grid = (int)(d.D < slots ? d.D : slots);
     V2* spec = static_cast<V2*>(d.spec) + d.spec_off[q];
-    hipLaunchKernelGGL(k_spectra, dim3(grid), dim3(64), lds, st, d.hT, d.LS, d.L, d.D, M, spec,
+    hipLaunchKernelGGL(k_spectra, dim3(grid), dim3(kTeam), lds, st, d.hT, d.LS, d.L, d.D, M, spec,
                        static_cast<Cx<double>*>(scd), scd_stride, static_cast<const Cx<double>*>(twd));
     return hipGetLastError();
 }
@@ -985,7 +1017,7 @@ hipError_t launch_tile(const DevState& d, int64_t i, hipStream_t st) {
     } else {
         const int F = U < kLdsFftMax ? U : kLdsFftMax;
         const int grid = (int)(d.C < d.sc_slots ? d.C : d.sc_slots);
-        hipLaunchKernelGGL(k_tile_fft, dim3(grid), dim3(64), (size_t)(lds_fft_elems(F) + kTwLds) * sizeof(Cx<float>), st, d, i, U);
+        hipLaunchKernelGGL(k_tile_fft, dim3(grid), dim3(kTeam), (size_t)(lds_fft_elems(F) + kTwLds) * sizeof(Cx<float>), st, d, i, U);
     }
     return hipGetLastError();
 }
@@ -999,7 +1031,7 @@ int run_max_blocks_per_cu(const DevState& d, int closed) {
     else fn = d.io_bf16 ? (const void*)k_run<false, true> : (const void*)k_run<false, false>;
     const int lds = run_lds_bytes(d);
     if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64, lds) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kTeam, lds) != hipSuccess) return 0;
     return nb;
 }
 
@@ -1008,11 +1040,11 @@ hipError_t launch_run(const DevState& d, const void* x_in, int closed, float* y,
     RunArgs a{d, x_in, y, x_out};
     const size_t lds = (size_t)run_lds_bytes(d);
     if (closed) {
-        if (d.io_bf16) hipLaunchKernelGGL((k_run<true, true>), dim3(grid), dim3(64), lds, st, a);
-        else hipLaunchKernelGGL((k_run<true, false>), dim3(grid), dim3(64), lds, st, a);
+        if (d.io_bf16) hipLaunchKernelGGL((k_run<true, true>), dim3(grid), dim3(kTeam), lds, st, a);
+        else hipLaunchKernelGGL((k_run<true, false>), dim3(grid), dim3(kTeam), lds, st, a);
     } else {
-        if (d.io_bf16) hipLaunchKernelGGL((k_run<false, true>), dim3(grid), dim3(64), lds, st, a);
-        else hipLaunchKernelGGL((k_run<false, false>), dim3(grid), dim3(64), lds, st, a);
+        if (d.io_bf16) hipLaunchKernelGGL((k_run<false, true>), dim3(grid), dim3(kTeam), lds, st, a);
+        else hipLaunchKernelGGL((k_run<false, false>), dim3(grid), dim3(kTeam), lds, st, a);
     }
     return hipGetLastError();
 }
