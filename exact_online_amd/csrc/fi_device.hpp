@@ -234,6 +234,8 @@ struct LdsOut {
     __device__ __forceinline__ void operator()(int off, int d, Cx<T> v) const { (b + lp(off))[lp(d)] = v; }
 };
 
+__host__ __device__ constexpr int ilog2c(int v) { return v <= 1 ? 0 : 1 + ilog2c(v / 2); }
+
 // Bit reversal of r over log2(R) bits, R in {2, 4, 8}.
 template <int R>
 __device__ __forceinline__ constexpr int rev_r(int r) {
@@ -303,6 +305,17 @@ __device__ __forceinline__ void dif_lds(const Src& src, FI_SHARED Cx<T>* lds, co
         if constexpr (S == M) ct_stage<M, S, false, T>(src, LdsOut<T>{lds}, tw);
         else ct_stage<M, S, false, T>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
         dif_lds<M, S / ct_radix(S), T>(src, lds, tw);
+    }
+}
+
+// The forward stages of dif_lds but the last (the smallest sub-problem
+// size ct_smallest(M) is left to the caller).
+template <int M, int S, typename T, typename Src, typename Tw>
+__device__ __forceinline__ void dif_lds_head(const Src& src, FI_SHARED Cx<T>* lds, const Tw& tw) {
+    if constexpr (S > ct_smallest(M)) {
+        if constexpr (S == M) ct_stage<M, S, false, T>(src, LdsOut<T>{lds}, tw);
+        else ct_stage<M, S, false, T>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
+        dif_lds_head<M, S / ct_radix(S), T>(src, lds, tw);
     }
 }
 

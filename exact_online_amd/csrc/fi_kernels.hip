@@ -215,6 +215,54 @@ __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n,
     }
 }
 
+// The row values that tile_output adds to, loaded ahead of the inverse
+// transform: for a sink whose ring takes the first kRunBlock positions, NP
+// per thread, the pairs m = kRunBlock/2 + tid + kTeam u (the order of
+// tile_output_ahead).  The last position of an odd L is left to a scalar
+// read-modify-write.
+template <int NP>
+struct RowAhead {
+    V2 v[NP];
+    __device__ __forceinline__ void load(const TileSink& s, int64_t i, int n) {
+        const int lane = team_tid();
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+            const int m = kRunBlock / 2 + lane + kTeam * u;
+            const int64_t o = i + 2 * (int64_t)m;
+            if (m < n && o + 1 < s.L) v[u] = *reinterpret_cast<const FI_GLOBAL V2*>(s.row + o);
+        }
+    }
+};
+
+// tile_output for a sink that is not a level's first and whose ring takes
+// the first kRunBlock positions, with the row values already loaded.
+template <int NP, typename Get>
+__device__ __forceinline__ void tile_output_ahead(const TileSink& s, int64_t i, int n, const Get& get,
+                                                  const RowAhead<NP>& ra) {
+    const int lane = team_tid();
+    constexpr int nl = kRunBlock / 2;
+#pragma unroll 1
+    for (int m = lane; m < nl; m += kTeam) {
+        const int64_t o = i + 2 * (int64_t)m;
+        if (m < n && o < s.L) {
+            const Cx<float> w = get(m);
+            s.accw[o & s.wmask] += w.x;
+            if (o + 1 < s.L) s.accw[(o + 1) & s.wmask] += w.y;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int m = nl + lane + kTeam * u;
+        const int64_t o = i + 2 * (int64_t)m;
+        if (m < n && o + 1 < s.L) {
+            const Cx<float> w = get(m);
+            *reinterpret_cast<FI_GLOBAL V2*>(s.row + o) = V2{ra.v[u].x + w.x, ra.v[u].y + w.y};
+        } else if (m < n && o < s.L) {
+            s.row[o] += get(m).x;
+        }
+    }
+}
+
 // Output spectrum of a partner pair of frequencies (k, M-k) whose packed
 // input transform values (z[n] = x[2n] + i x[2n+1]) are A = Z_k, B = Z_{M-k},
 // with the filter entries gk = G[k] / (4M), gm = G[M-k] / (4M), w = w_2M^k:
@@ -352,6 +400,121 @@ __device__ __forceinline__ void untangle_lds(FI_SHARED Cx<float>* lds, SpecP spe
     team_sync();
 }
 
+// ---------------------------------------------------------------- middle
+// The middle of a tile's transform pair in one LDS pass: the forward
+// transform's last stage, the untangle of every partner pair and the inverse
+// transform's first stage.  Both stages have radix R = ct_smallest(M) and no
+// twiddles, and work on groups of R consecutive positions.  The partner of
+// position gR + s is g'R + R-1-s with g' = mirror_pos(g) the mirror group
+// (groups 0 and 1 hold their own partners), so one thread takes a group and
+// its mirror group through all three steps in registers.
+// Position gR + s holds frequency k = brev(gR + s) = kg + brev_R(s) M/R, kg the
+// bit reversal of g over log2(M/R) bits, so w_2M^k = w_2M^kg w_2R^brev_R(s).
+// Item n of the pass: n = 0 takes groups 0 and 1, n >= 1 the group
+// pair_first(n + 1) and its mirror.
+template <int R>
+struct GroupSpec {
+    V2 a[R], b[R];
+    template <typename SpecP>
+    __device__ __forceinline__ void load(SpecP spec, int ga, int gb) {
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+            a[s] = spec[ga * R + s];
+            b[s] = spec[gb * R + s];
+        }
+    }
+};
+
+__device__ __forceinline__ void middle_groups(int n, int& ga, int& gb) {
+    ga = n == 0 ? 0 : pair_first(n + 1);
+    gb = n == 0 ? 1 : mirror_pos(ga);
+}
+
+// w_2R^e as a compile-time constant (forward sign).
+template <int R>
+__device__ __forceinline__ Cx<float> w2r(int e) {
+    const double ang = -3.14159265358979323846 * (double)e / (double)R;
+    return Cx<float>{(float)__builtin_cos(ang), (float)__builtin_sin(ang)};
+}
+
+template <int M, typename SpecP>
+__device__ __forceinline__ void middle_lds(FI_SHARED Cx<float>* lds, SpecP spec, V2 gM, const LdsTw& tw,
+                                           GroupSpec<ct_smallest(M)> cur) {
+    constexpr int R = ct_smallest(M);
+    constexpr int NI = M / R / 2;             // items
+    constexpr int GB = ilog2c(M / R);         // bits of a group index
+    const int tid = team_tid();
+    const TwLdsN twn{tw.A, 2 * M};
+#pragma unroll 1
+    for (int n = tid; n < NI; n += kTeam) {
+        GroupSpec<R> nxt;
+        if (n + kTeam < NI) {
+            int na, nb;
+            middle_groups(n + kTeam, na, nb);
+            nxt.load(spec, na, nb);
+        }
+        int ga, gb;
+        middle_groups(n, ga, gb);
+        Cx<float> a[R], b[R];
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+            a[s] = lds[lp(ga * R + s)];
+            b[s] = lds[lp(gb * R + s)];
+        }
+        // last forward stage: afterwards position gR + s holds a[rev(s)]
+        dft<R, false>(a);
+        dft<R, false>(b);
+        if (n == 0) {
+            // group 0: positions 0 (k = 0, partner G[M]) and 1 (k = M/2) pair
+            // with themselves, the others p with mirror_pos(p); group 1 (the
+            // octave of R): R + s with 2R - 1 - s.  All twiddles are constants.
+#pragma unroll
+            for (int s = 0; s < R; ++s) {
+                const int s2 = s < 2 ? s : 3 * (1 << ilog2c(s)) - 1 - s;
+                if (s2 < s) continue;
+                Cx<float>& A = a[rev_r<R>(s)];
+                Cx<float>& B = a[rev_r<R>(s2)];
+                const V2 gm = s == 0 ? gM : cur.a[s2];
+                if (s2 == s) {
+                    Cx<float> t = A;
+                    untangle_pair(A, t, Cx<float>{cur.a[s].x, cur.a[s].y}, Cx<float>{gm.x, gm.y},
+                                  w2r<R>(rev_r<R>(s)));
+                } else {
+                    untangle_pair(A, B, Cx<float>{cur.a[s].x, cur.a[s].y}, Cx<float>{gm.x, gm.y},
+                                  w2r<R>(rev_r<R>(s)));
+                }
+            }
+            // group 1: k = M/(2R) + brev_R(s) M/R, w_2M^k = w_4R w_2R^brev_R(s)
+#pragma unroll
+            for (int s = 0; s < R / 2; ++s) {
+                const int s2 = R - 1 - s;
+                const Cx<float> w = cmul(w2r<2 * R>(1), w2r<R>(rev_r<R>(s)));
+                untangle_pair(b[rev_r<R>(s)], b[rev_r<R>(s2)], Cx<float>{cur.b[s].x, cur.b[s].y},
+                              Cx<float>{cur.b[s2].x, cur.b[s2].y}, w);
+            }
+        } else {
+            const Cx<float> wg = twn(brev_bits(ga, GB));
+#pragma unroll
+            for (int s = 0; s < R; ++s) {
+                const int s2 = R - 1 - s;
+                const Cx<float> w = s == 0 ? wg : cmul(wg, w2r<R>(rev_r<R>(s)));
+                untangle_pair(a[rev_r<R>(s)], b[rev_r<R>(s2)], Cx<float>{cur.a[s].x, cur.a[s].y},
+                              Cx<float>{cur.b[s2].x, cur.b[s2].y}, w);
+            }
+        }
+        // first inverse stage: it reads position gR + rev(rho) = a[rho]
+        dft<R, true>(a);
+        dft<R, true>(b);
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+            lds[lp(ga * R + s)] = a[s];
+            lds[lp(gb * R + s)] = b[s];
+        }
+        cur = nxt;
+    }
+    team_sync();
+}
+
 // pairs of a whole bit-reversed transform (or of a block holding its octaves)
 struct PairsAll {
     __device__ __forceinline__ void operator()(int n, int& a, int& b) const {
@@ -385,19 +548,51 @@ struct TileInLds {
 template <int M, typename XIn, typename SpecP>
 __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP spec, FI_SHARED Cx<float>* lds,
                                              const LdsTw& tw, const TileSink& out) {
-    // batches of kUntangleBatch spectrum entries per thread: staged in LDS,
-    // read after the forward transform; in global memory, the first batch in
-    // flight during the forward transform
+    // spectrum entries staged in LDS are read after the forward transform;
+    // from global memory, the first batch is in flight during it
     constexpr bool staged = std::is_same<SpecP, const FI_SHARED V2*>::value;
-    constexpr int NALL = M / 2 / kTeam + 1;
-    constexpr int NB = NALL < kUntangleBatch ? NALL : kUntangleBatch;
-    SpecBatch<NB> first;
-    if constexpr (!staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
+    constexpr int R = ct_smallest(M);
     const V2 gM = spec[M];
-    dif_lds<M, M, float>(xin, lds, tw);
-    if constexpr (staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
-    untangle_lds<NB>(lds, spec, gM, M / 2 + 1, PairsAll{}, 0, ilog2(M), TwLdsN{tw.A, 2 * M}, first);
-    dit_lds<M, ct_smallest(M), float>(lds, tw);
+    if constexpr (M / R / 2 >= kTeam) {
+        // the fused middle pass (one LDS pass instead of three)
+        GroupSpec<R> first;
+        const int tid = team_tid();
+        if constexpr (!staged) {
+            int ga, gb;
+            middle_groups(tid, ga, gb);
+            first.load(spec, ga, gb);
+        }
+        dif_lds_head<M, M, float>(xin, lds, tw);
+        if constexpr (staged) {
+            int ga, gb;
+            middle_groups(tid, ga, gb);
+            first.load(spec, ga, gb);
+        }
+        middle_lds<M>(lds, spec, gM, tw, first);
+        // the row values the output adds to, in flight during the inverse
+        // transform
+        constexpr int NPA = (M / 2 - kRunBlock / 2 + kTeam - 1) / kTeam;
+        RowAhead<NPA> ra;
+        const bool ahead = !out.first && out.accw != nullptr && out.wend - i == kRunBlock;
+        if (ahead) ra.load(out, i, M / 2);
+        dit_lds<M, R * 8, float>(lds, tw);
+        if (ahead) {
+            tile_output_ahead(out, i, M / 2, [lds](int m) { return lds[lp(M / 2 + m)]; }, ra);
+            return;
+        }
+    } else {
+        // small transforms: too few groups to spread the fused pass over the
+        // team, so the last and first stages stay separate from an untangle
+        // pass over single pairs
+        constexpr int NALL = M / 2 / kTeam + 1;
+        constexpr int NB = NALL < kUntangleBatch ? NALL : kUntangleBatch;
+        SpecBatch<NB> first;
+        if constexpr (!staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
+        dif_lds<M, M, float>(xin, lds, tw);
+        if constexpr (staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
+        untangle_lds<NB>(lds, spec, gM, M / 2 + 1, PairsAll{}, 0, ilog2(M), TwLdsN{tw.A, 2 * M}, first);
+        dit_lds<M, R, float>(lds, tw);
+    }
     // point M/2 + m carries outputs 2m, 2m + 1 of the tile
     tile_output(out, i, M / 2, [lds](int m) { return lds[lp(M / 2 + m)]; });
 }
