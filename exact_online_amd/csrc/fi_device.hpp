@@ -208,13 +208,17 @@ __device__ __forceinline__ void twiddle_apply(Cx<T>* v, const Tw& tw, int S, int
     }
 }
 
+// Radix of the stages of an M-point transform: 4 up to 512 points, where a
+// stage has too few butterflies to fill a team and its latency is set by the
+// work of one butterfly, else 8.
+__host__ __device__ constexpr int ct_base(int M) { return M <= 512 ? 4 : 8; }
 // Radix of the stage that splits a sub-problem of size S.
-__host__ __device__ constexpr int ct_radix(int S) { return S >= 8 ? 8 : S; }
+__host__ __device__ constexpr int ct_radix(int S, int M) { return S >= ct_base(M) ? ct_base(M) : S; }
 
 // Size of the last (smallest) sub-problem stage of an M-point transform.
 __host__ __device__ constexpr int ct_smallest(int M) {
     int S = M;
-    while (S / ct_radix(S) > 1) S /= ct_radix(S);
+    while (S / ct_radix(S, M) > 1) S /= ct_radix(S, M);
     return S;
 }
 
@@ -245,7 +249,7 @@ __device__ __forceinline__ constexpr int rev_r(int r) {
 }
 
 // One in-place Cooley-Tukey stage on every sub-problem of size S of an
-// M-point sequence (sub-problems contiguous), radix R = ct_radix(S), Q = S/R.
+// M-point sequence (sub-problems contiguous), radix R = ct_radix(S, M), Q = S/R.
 // Butterfly (base, j) owns the slots base + j + r*Q, r < R:
 //   forward (decimation in frequency): v_r from slot r; u = DFT_R(v),
 //     u_rho *= w_S^{j rho}, u_rho to slot rev(rho);
@@ -257,7 +261,7 @@ __device__ __forceinline__ constexpr int rev_r(int r) {
 // a thread processes its butterflies GRP at a time to overlap memory latency.
 template <int M, int S, bool INV, typename T, typename Src, typename Dst, typename Tw>
 __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const Tw& tw) {
-    constexpr int R = ct_radix(S);
+    constexpr int R = ct_radix(S, M);
     constexpr int Q = S / R;
     constexpr int NB = M / R;
     constexpr int PER = (NB + kTeam - 1) / kTeam;
@@ -304,7 +308,7 @@ __device__ __forceinline__ void dif_lds(const Src& src, FI_SHARED Cx<T>* lds, co
     if constexpr (S > 1) {
         if constexpr (S == M) ct_stage<M, S, false, T>(src, LdsOut<T>{lds}, tw);
         else ct_stage<M, S, false, T>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
-        dif_lds<M, S / ct_radix(S), T>(src, lds, tw);
+        dif_lds<M, S / ct_radix(S, M), T>(src, lds, tw);
     }
 }
 
@@ -315,18 +319,19 @@ __device__ __forceinline__ void dif_lds_head(const Src& src, FI_SHARED Cx<T>* ld
     if constexpr (S > ct_smallest(M)) {
         if constexpr (S == M) ct_stage<M, S, false, T>(src, LdsOut<T>{lds}, tw);
         else ct_stage<M, S, false, T>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
-        dif_lds_head<M, S / ct_radix(S), T>(src, lds, tw);
+        dif_lds_head<M, S / ct_radix(S, M), T>(src, lds, tw);
     }
 }
 
 // Inverse of dif_lds (unnormalised, times M): bit-reversed order in, natural
 // order out, in place on the LDS buffer.  Every stage but the smallest has
-// radix 8, so the sizes run ct_smallest(M), 8x that, ..., M.
+// radix ct_base(M), so the sizes run ct_smallest(M), ct_base(M) times that,
+// ..., M.
 template <int M, int S, typename T, typename Tw>
 __device__ __forceinline__ void dit_lds(FI_SHARED Cx<T>* lds, const Tw& tw) {
     if constexpr (S <= M) {
         ct_stage<M, S, true, T>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
-        if constexpr (S < M) dit_lds<M, S * 8, T>(lds, tw);
+        if constexpr (S < M) dit_lds<M, S * ct_base(M), T>(lds, tw);
     }
 }
 

@@ -575,7 +575,7 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
         RowAhead<NPA> ra;
         const bool ahead = !out.first && out.accw != nullptr && out.wend - i == kRunBlock;
         if (ahead) ra.load(out, i, M / 2);
-        dit_lds<M, R * 8, float>(lds, tw);
+        dit_lds<M, R * ct_base(M), float>(lds, tw);
         if (ahead) {
             tile_output_ahead(out, i, M / 2, [lds](int m) { return lds[lp(M / 2 + m)]; }, ra);
             return;
