@@ -299,17 +299,6 @@ struct TileIn {
     }
 };
 
-// The same input times w_M^n (the second half after one radix-2 pass).
-struct TileInTw {
-    const FI_GLOBAL V2* xs;
-    TwPtr<float> tw;
-    int M;
-    __device__ __forceinline__ Cx<float> operator()(int off, int d) const {
-        const int n = off + d;
-        const V2 v = xs[n];
-        return cmul(Cx<float>{v.x, v.y}, twiddle<false>(tw, M, n));
-    }
-};
 
 // Twiddles w_N^k for the untangle: from the LDS table (A[64] = w_64^a,
 // B[64] = w_4096^b, C[4] = w_16384^r) for N <= 16384, else from the global
@@ -412,6 +401,10 @@ __device__ __forceinline__ void untangle_lds(FI_SHARED Cx<float>* lds, SpecP spe
 // bit reversal of g over log2(M/R) bits, so w_2M^k = w_2M^kg w_2R^brev_R(s).
 // Item n of the pass: n = 0 takes groups 0 and 1, n >= 1 the group
 // pair_first(n + 1) and its mirror.
+// ODD: the M points are the odd-frequency half of a 2M-point transform
+// (position q holds frequency 1 + 2 brev(q)); partners are q and M-1-q, so
+// item n takes groups n and M/R-1-n, and every twiddle carries a factor
+// w_4M.
 template <int R>
 struct GroupSpec {
     V2 a[R], b[R];
@@ -425,9 +418,15 @@ struct GroupSpec {
     }
 };
 
+template <bool ODD, int NG>
 __device__ __forceinline__ void middle_groups(int n, int& ga, int& gb) {
-    ga = n == 0 ? 0 : pair_first(n + 1);
-    gb = n == 0 ? 1 : mirror_pos(ga);
+    if constexpr (ODD) {
+        ga = n;
+        gb = NG - 1 - n;
+    } else {
+        ga = n == 0 ? 0 : pair_first(n + 1);
+        gb = n == 0 ? 1 : mirror_pos(ga);
+    }
 }
 
 // w_2R^e as a compile-time constant (forward sign).
@@ -437,10 +436,25 @@ __device__ __forceinline__ Cx<float> w2r(int e) {
     return Cx<float>{(float)__builtin_cos(ang), (float)__builtin_sin(ang)};
 }
 
-template <int M, typename SpecP>
+// The tile input (x[2n] + i x[2n+1], n < N/2) times w_N^n, N = 2 kLdsFftMax:
+// the second half of an N-point transform after one radix-2 pass.  In a
+// stage the offset d of a butterfly's point is a constant, so w_N^(off+d) =
+// w_N^off (LDS table, once per butterfly) times a folded constant.
+struct TileInTw {
+    const FI_GLOBAL V2* xs;
+    const FI_SHARED Cx<float>* twl;
+    __device__ __forceinline__ Cx<float> operator()(int off, int d) const {
+        const V2 v = xs[off + d];
+        const Cx<float> w = cmul(TwLdsN{twl, 2 * kLdsFftMax}(off), w2r<kLdsFftMax>(d));
+        return cmul(Cx<float>{v.x, v.y}, w);
+    }
+};
+
+template <int M, bool ODD, typename SpecP>
 __device__ __forceinline__ void middle_lds(FI_SHARED Cx<float>* lds, SpecP spec, V2 gM, const LdsTw& tw,
                                            GroupSpec<ct_smallest(M)> cur) {
     constexpr int R = ct_smallest(M);
+    constexpr int NG = M / R;
     constexpr int NI = M / R / 2;             // items
     constexpr int GB = ilog2c(M / R);         // bits of a group index
     const int tid = team_tid();
@@ -450,11 +464,11 @@ __device__ __forceinline__ void middle_lds(FI_SHARED Cx<float>* lds, SpecP spec,
         GroupSpec<R> nxt;
         if (n + kTeam < NI) {
             int na, nb;
-            middle_groups(n + kTeam, na, nb);
+            middle_groups<ODD, NG>(n + kTeam, na, nb);
             nxt.load(spec, na, nb);
         }
         int ga, gb;
-        middle_groups(n, ga, gb);
+        middle_groups<ODD, NG>(n, ga, gb);
         Cx<float> a[R], b[R];
 #pragma unroll
         for (int s = 0; s < R; ++s) {
@@ -464,7 +478,7 @@ __device__ __forceinline__ void middle_lds(FI_SHARED Cx<float>* lds, SpecP spec,
         // last forward stage: afterwards position gR + s holds a[rev(s)]
         dft<R, false>(a);
         dft<R, false>(b);
-        if (n == 0) {
+        if (!ODD && n == 0) {
             // group 0: positions 0 (k = 0, partner G[M]) and 1 (k = M/2) pair
             // with themselves, the others p with mirror_pos(p); group 1 (the
             // octave of R): R + s with 2R - 1 - s.  All twiddles are constants.
@@ -493,7 +507,8 @@ __device__ __forceinline__ void middle_lds(FI_SHARED Cx<float>* lds, SpecP spec,
                               Cx<float>{cur.b[s2].x, cur.b[s2].y}, w);
             }
         } else {
-            const Cx<float> wg = twn(brev_bits(ga, GB));
+            Cx<float> wg = twn(brev_bits(ga, GB));
+            if constexpr (ODD) wg = cmul(wg, w2r<2 * M>(1));
 #pragma unroll
             for (int s = 0; s < R; ++s) {
                 const int s2 = R - 1 - s;
@@ -559,16 +574,16 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
         const int tid = team_tid();
         if constexpr (!staged) {
             int ga, gb;
-            middle_groups(tid, ga, gb);
+            middle_groups<false, M / R>(tid, ga, gb);
             first.load(spec, ga, gb);
         }
         dif_lds_head<M, M, float>(xin, lds, tw);
         if constexpr (staged) {
             int ga, gb;
-            middle_groups(tid, ga, gb);
+            middle_groups<false, M / R>(tid, ga, gb);
             first.load(spec, ga, gb);
         }
-        middle_lds<M>(lds, spec, gM, tw, first);
+        middle_lds<M, false>(lds, spec, gM, tw, first);
         // the row values the output adds to, in flight during the inverse
         // transform
         constexpr int NPA = (M / 2 - kRunBlock / 2 + kTeam - 1) / kTeam;
@@ -615,22 +630,29 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
         // result waits in the scratch slot for the last inverse pass, fused
         // with the output (only outputs M/2 .. M-1 are kept).
         constexpr int F = kLdsFftMax;
+        constexpr int R = ct_smallest(F);
         const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
         const V2 gM = spec[M];
-        const TwLdsN twn{twl, 2 * M};
-        SpecBatch<kUntangleBatch> sb0;
-        sb0.load(spec, 0, F / 2 + 1, PairsAll{});
-        dif_lds<F, F, float>(TileIn{xs, F}, lbuf, ltw);
-        untangle_lds<kUntangleBatch>(lbuf, spec, gM, F / 2 + 1, PairsAll{}, 0, ilog2(M), twn, sb0);
-        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        const TwLdsN twn{twl, 2 * F};
+        const int tid = team_tid();
+        int ga, gb;
+        // half 0: the even frequencies, a 4096-point tile of its own
+        GroupSpec<R> g0;
+        middle_groups<false, F / R>(tid, ga, gb);
+        g0.load(spec, ga, gb);
+        dif_lds_head<F, F, float>(TileIn{xs, F}, lbuf, ltw);
+        middle_lds<F, false>(lbuf, spec, gM, ltw, g0);
+        dit_lds<F, R * ct_base(F), float>(lbuf, ltw);
         copy_from_lds(sc, lbuf, F);
-        sb0.load(spec + F, 0, F / 2, PairsMirror{F});
-        dif_lds<F, F, float>(TileInTw{xs, tw, M}, lbuf, ltw);
-        untangle_lds<kUntangleBatch>(lbuf, spec + F, gM, F / 2, PairsMirror{F}, F, ilog2(M), twn, sb0);
-        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
-        tile_output(out, i, F, [sc, lbuf, tw](int j) {
+        // half 1: the odd frequencies
+        middle_groups<true, F / R>(tid, ga, gb);
+        g0.load(spec + F, ga, gb);
+        dif_lds_head<F, F, float>(TileInTw{xs, twl}, lbuf, ltw);
+        middle_lds<F, true>(lbuf, spec + F, gM, ltw, g0);
+        dit_lds<F, R * ct_base(F), float>(lbuf, ltw);
+        tile_output(out, i, F, [sc, lbuf, twn](int j) {
             const Cx<float> v0 = sc[j];
-            const Cx<float> v1 = cmul(lbuf[lp(j)], twiddle<true>(tw, 2 * F, j));
+            const Cx<float> v1 = cmul(lbuf[lp(j)], cconj(twn(j)));
             return csub(v0, v1);
         });
         return;
