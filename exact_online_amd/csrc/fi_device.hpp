@@ -267,6 +267,16 @@ __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const T
     constexpr int PER = (NB + kTeam - 1) / kTeam;
     constexpr int GRP = PER < 2 ? PER : 2;
     const int lane = team_tid();
+    // When Q divides kTeam, a thread's butterflies (n = lane + kTeam u) all
+    // have j = lane mod Q: their twiddles are computed once.
+    constexpr bool ONE_J = S > R && kTeam % Q == 0;
+    Cx<T> wj[R];
+    if constexpr (ONE_J) {
+        tw.template powers<R>(S, lane % Q, wj);
+#pragma unroll
+        for (int r = 1; r < R; ++r)
+            if constexpr (INV) wj[r].y = -wj[r].y;
+    }
 #pragma unroll 1
     for (int u0 = 0; u0 < PER; u0 += GRP) {
         Cx<T> v[GRP][R];
@@ -286,11 +296,21 @@ __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const T
             const int n = lane + kTeam * (u0 + g);
             if (NB % kTeam == 0 || n < NB) {
                 if constexpr (INV) {
-                    if constexpr (S > R) twiddle_apply<R, true>(v[g], tw, S, jj[g]);
+                    if constexpr (ONE_J) {
+#pragma unroll
+                        for (int r = 1; r < R; ++r) v[g][r] = cmul(v[g][r], wj[r]);
+                    } else if constexpr (S > R) {
+                        twiddle_apply<R, true>(v[g], tw, S, jj[g]);
+                    }
                     dft<R, true>(v[g]);
                 } else {
                     dft<R, false>(v[g]);
-                    if constexpr (S > R) twiddle_apply<R, false>(v[g], tw, S, jj[g]);
+                    if constexpr (ONE_J) {
+#pragma unroll
+                        for (int r = 1; r < R; ++r) v[g][r] = cmul(v[g][r], wj[r]);
+                    } else if constexpr (S > R) {
+                        twiddle_apply<R, false>(v[g], tw, S, jj[g]);
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < R; ++r) dst(off[g], (INV ? r : rev_r<R>(r)) * Q, v[g][r]);
