@@ -11,6 +11,9 @@ constexpr int kMaxLevels = 40;
 constexpr int kRunBlock = 256;     // positions per block of the persistent pass (= its LDS ring W)
 constexpr int kLdsFftMax = 4096;  // largest complex FFT held in LDS (32 KiB in fp32)
 constexpr int kTwLds = 132;       // LDS twiddle table: w_64^a, w_4096^b (64 each), w_16384^r (4)
+// The run kernel's chain taps as 16-byte entries (four consecutive taps in
+// reverse order), at the top of its FFT region: 64 + kRunBlock + 4 entries.
+constexpr int kTapTableBytes = (64 + kRunBlock + 4) * 16;
 // LDS FFT buffers hold one spare slot per 8 points (bank spreading).
 constexpr int lds_fft_elems(int M) { return M + M / 8; }
 

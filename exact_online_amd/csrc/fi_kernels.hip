@@ -948,6 +948,20 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     TwPtr<float> tw = gmem(static_cast<const Cx<float>*>(d.twf));
     FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)bid * d.sc_stride;
     FI_GLOBAL float* yout = gmem(a.y);
+    // tz[q + 3] = (hz[q], hz[q-1], hz[q-2], hz[q-3]) (zero outside hz): the
+    // taps of four consecutive chain steps in one 16-byte read
+    const int t4_off = d.fftreg - kTapTableBytes;
+    FI_SHARED V4* tz = reinterpret_cast<FI_SHARED V4*>(smem_ptr(smem) + t4_off);
+    auto build_taps4 = [&]() {
+        constexpr int NH = kWave + kBlk;
+        for (int e = tid; e < kTapTableBytes / 16; e += kTeam) {
+            const int q = e - 3;
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (q - j >= 0 && q - j < NH) ? hz[q - j] : 0.f;
+            tz[e] = V4{v[0], v[1], v[2], v[3]};
+        }
+    };
     fill_lds_twiddles(twl);
 
     for (int64_t ch = ch0; ch < d.C; ch += G) {
@@ -962,6 +976,8 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             hz[q] = (q >= kWave && q - kWave < L) ? tap_scale * hrow[q - kWave] : 0.f;
         if (direct)
             for (int q = tid; q < 2 * d.T; q += kTeam) htap[q] = q < L ? hrow[q] : 0.f;
+        team_sync();
+        build_taps4();
         team_sync();
         const float ch0v = hz[kWave];   // closed loop: c h[0]
 
@@ -1051,12 +1067,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     const int64_t pn = base + kWave * k + lane;
                     nx[k] = (nx_in_row && pn < L) ? row[pn] : 0.f;
                 }
-                const FI_SHARED float* hz0 = hz + kWave + lane;   // hz0[64k - m]: tap of position 64k + lane, input m
-                float ta[kRegs][2 * kTapBatch];
+                // tz0[64k - n]: the taps of position 64k + lane for inputs
+                // n .. n+3 (n a multiple of kTapBatch), in two batches
+                static_assert(kTapBatch == 4, "a tap batch is one 16-byte entry");
+                const FI_SHARED V4* tz0 = tz + 3 + kWave + lane;
+                V4 ta[kRegs][2];
 #pragma unroll
-                for (int n = 0; n < kTapBatch; ++n)
-#pragma unroll
-                    for (int k = 0; k < kRegs; ++k) ta[k][n] = hz0[kWave * k - n];
+                for (int k = 0; k < kRegs; ++k) ta[k][0] = tz0[kWave * k];
                 float v = 0.f;
                 float xstart = 0.f;
                 if constexpr (CLOSED) {
@@ -1073,7 +1090,10 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         const int m = kWave * K + m2;
                         float tv[kRegs];
 #pragma unroll
-                        for (int k = 0; k < kRegs; ++k) tv[k] = ta[k][m % (2 * kTapBatch)];
+                        for (int k = 0; k < kRegs; ++k) {
+                            const V4 t4 = ta[k][(m / kTapBatch) % 2];
+                            tv[k] = m % 4 == 0 ? t4.x : m % 4 == 1 ? t4.y : m % 4 == 2 ? t4.z : t4.w;
+                        }
                         // closed loop: the accumulators run in units of c = 2 log2(e)
                         // (the taps hz are c h), so tanh(y) = 1 - 2 r with
                         // r = 1 / (1 + 2^(c y)); v holds position t0+m's accumulator
@@ -1091,13 +1111,10 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         }
                         if (m % kTapBatch == 0 && m + kTapBatch < kBlk) {
                             __builtin_amdgcn_sched_barrier(0);
+                            const int n = m + kTapBatch;
 #pragma unroll
-                            for (int n2 = 0; n2 < kTapBatch; ++n2) {
-                                const int n = m + kTapBatch + n2;
-#pragma unroll
-                                for (int k = 0; k < kRegs; ++k)
-                                    if (n < kWave * (k + 1)) ta[k][n % (2 * kTapBatch)] = hz0[kWave * k - n];
-                            }
+                            for (int k = 0; k < kRegs; ++k)
+                                if (n < kWave * (k + 1)) ta[k][(n / kTapBatch) % 2] = tz0[kWave * k - n];
                         }
                         if constexpr (CLOSED) {
                             if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
@@ -1163,6 +1180,11 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         gmem(static_cast<const V2*>(d.spec)) + d.spec_off[q] + c * (int64_t)(U + 2);
                     fft_tile(U, i, row, spec, lbuf, sc, tw, twl, accw, i + kBlk, wmask, L, i == U,
                              stage_x ? xst : nullptr, stage_spec ? sst : nullptr);
+                    // the transform buffer reached the tap table: rebuild it
+                    if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > t4_off) {
+                        team_sync();
+                        build_taps4();
+                    }
                 }
                 // The chain wavefront reads the ring and (a block later) the row
                 // positions this tile wrote: the other wavefronts' stores must
