@@ -874,8 +874,8 @@ __global__ __launch_bounds__(kTeam) void k_tile_fft(DevState d, int64_t i, int U
 //    of each lag, into the accumulators of t and of every later position of
 //    the block (lag 0 is the red cell), so the register of position t holds
 //    y[t] when it is read.  The same products reach the same outputs as those
-//    tiles.  Taps come from LDS: hz[kWave + j] = h[j], zeros below (a lane's
-//    lag is never below -63).
+//    tiles.  Taps come from an LDS table of 16-byte entries, the taps of
+//    four consecutive steps each (zero for negative lags).
 //  * At each block boundary i = t0 + kBlk the tile of side U = lowbit(i) >=
 //    kBlk runs: a direct Toeplitz product from LDS when U <= T, else the FFT
 //    tile.
@@ -887,8 +887,17 @@ __global__ __launch_bounds__(kTeam) void k_tile_fft(DevState d, int64_t i, int U
 // accumulators from the row while its chain runs.
 constexpr int kRegs = kRunBlock / kWave;   // accumulator registers per lane
 constexpr int kBlk = kRunBlock;
-constexpr int kLog2Blk = 8;
-static_assert((1 << kLog2Blk) == kBlk, "block size");
+constexpr int kLog2Blk = ilog2c(kBlk);
+static_assert((1 << kLog2Blk) == kBlk && kRegs <= 8, "block size");
+
+// f(integral_constant<int, K>) for K = K0 .. kRegs-1, in order.
+template <int K0, typename F>
+__device__ __forceinline__ void for_segments(F&& f) {
+    if constexpr (K0 < kRegs) {
+        f(std::integral_constant<int, K0>{});
+        for_segments<K0 + 1>(f);
+    }
+}
 constexpr int kTapBatch = 4;         // chain: taps loaded per batch, one batch ahead
 constexpr int kStageSpecMax = 1024;  // tiles up to this side get spectrum and input staged in LDS
 // (FFT buffer 9M bytes + input 4U + spectrum 8 (U + 2) fits the 36 KiB region
@@ -924,12 +933,10 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ Cx<float> s_tw[kTwLds];  // twiddles A[64] = w_64^a, B[64] = w_4096^b, C[4] = w_16384^r
     __shared__ float s_ring[kBlk];      // accumulators of positions [t0, t0+W)
-    __shared__ float s_taps[kWave + kBlk];  // 64 zeros, then the chain's taps
     const DevState& d = a.d;
     FI_SHARED Cx<float>* lbuf = smem_ptr(reinterpret_cast<Cx<float>*>(smem));
     FI_SHARED Cx<float>* twl = smem_ptr(s_tw);
     FI_SHARED float* accw = smem_ptr(s_ring);
-    FI_SHARED float* hz = smem_ptr(s_taps);
     FI_SHARED float* xring = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.fftreg);  // direct tiles only
     FI_SHARED float* htap = xring + d.XR;    // h[0 .. 2T), direct tiles only
     const bool direct = d.T >= kBlk;
@@ -948,17 +955,19 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     TwPtr<float> tw = gmem(static_cast<const Cx<float>*>(d.twf));
     FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)bid * d.sc_stride;
     FI_GLOBAL float* yout = gmem(a.y);
-    // tz[q + 3] = (hz[q], hz[q-1], hz[q-2], hz[q-3]) (zero outside hz): the
-    // taps of four consecutive chain steps in one 16-byte read
+    // The chain's taps: with hz[q] = s h[q - 64] for 64 <= q < 64 + kBlk, else
+    // 0 (s = c in closed loop, see below, else 1), tz[q + 3] = (hz[q],
+    // hz[q-1], hz[q-2], hz[q-3]) holds the taps of four consecutive chain
+    // steps in one 16-byte read.
     const int t4_off = d.fftreg - kTapTableBytes;
     FI_SHARED V4* tz = reinterpret_cast<FI_SHARED V4*>(smem_ptr(smem) + t4_off);
-    auto build_taps4 = [&]() {
-        constexpr int NH = kWave + kBlk;
+    const float tap_scale = CLOSED ? kTanhScale : 1.0f;
+    auto build_taps4 = [&](const FI_GLOBAL float* hrow) {
         for (int e = tid; e < kTapTableBytes / 16; e += kTeam) {
-            const int q = e - 3;
+            const int q = e - 3 - kWave;   // lag of the first component
             float v[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = (q - j >= 0 && q - j < NH) ? hz[q - j] : 0.f;
+            for (int j = 0; j < 4; ++j) v[j] = (q - j >= 0 && q - j < kBlk && q - j < L) ? tap_scale * hrow[q - j] : 0.f;
             tz[e] = V4{v[0], v[1], v[2], v[3]};
         }
     };
@@ -970,16 +979,11 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
         const FI_GLOBAL float* hrow = gmem(d.hT + c * d.LS);
         team_sync();   // the previous channel's last chain is done with the taps and the ring
         for (int q = tid; q < kBlk; q += kTeam) accw[q] = 0.f;
-        // taps: h (open loop); c h (closed loop, c = 2 log2 e, see below)
-        const float tap_scale = CLOSED ? kTanhScale : 1.0f;
-        for (int q = tid; q < kWave + kBlk; q += kTeam)
-            hz[q] = (q >= kWave && q - kWave < L) ? tap_scale * hrow[q - kWave] : 0.f;
         if (direct)
             for (int q = tid; q < 2 * d.T; q += kTeam) htap[q] = q < L ? hrow[q] : 0.f;
+        build_taps4(hrow);
         team_sync();
-        build_taps4();
-        team_sync();
-        const float ch0v = hz[kWave];   // closed loop: c h[0]
+        const float ch0v = tap_scale * hrow[0];   // closed loop: c h[0]
 
         float xcur = 0.f;        // closed loop: x at the next position (uniform)
         float xbn[kRegs];        // open loop: inputs of the next block
@@ -1095,7 +1099,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                             tv[k] = m % 4 == 0 ? t4.x : m % 4 == 1 ? t4.y : m % 4 == 2 ? t4.z : t4.w;
                         }
                         // closed loop: the accumulators run in units of c = 2 log2(e)
-                        // (the taps hz are c h), so tanh(y) = 1 - 2 r with
+                        // (the taps are c h), so tanh(y) = 1 - 2 r with
                         // r = 1 / (1 + 2^(c y)); v holds position t0+m's accumulator
                         // with every input but its own pushed (read one step ahead,
                         // off the serial path), and the serial path of a position is
@@ -1124,11 +1128,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 };
-                static_assert(kRegs == 4, "the chain below runs four segments");
-                segment(std::integral_constant<int, 0>{});
-                segment(std::integral_constant<int, 1>{});
-                segment(std::integral_constant<int, 2>{});
-                segment(std::integral_constant<int, 3>{});
+                for_segments<0>(segment);
                 if constexpr (CLOSED) {
                     // The inputs of the block, one per lane: the register of
                     // position t ended as the same fma as the chain's c y[t], so
@@ -1183,7 +1183,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     // the transform buffer reached the tap table: rebuild it
                     if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > t4_off) {
                         team_sync();
-                        build_taps4();
+                        build_taps4(hrow);
                     }
                 }
                 // The chain wavefront reads the ring and (a block later) the row
