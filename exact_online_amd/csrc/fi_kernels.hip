@@ -145,10 +145,11 @@ __global__ void k_zero(float* p, int64_t n) {
 
 // ============================================================== FFT tile
 // Where the outputs of the tile at i go: positions below `wend` into the LDS
-// ring `accw` (slot = position & wmask; none when accw is null); the others
-// into the channel's global row, added to what earlier tiles left there, or
-// stored when `first` says no earlier tile reached them.  wend - i is a
-// multiple of 128.
+// ring `accw` (slot = position & wmask; no ring when wend <= i -- an LDS
+// pointer is never tested against null, since an object may sit at LDS
+// address 0); the others into the channel's global row, added to what
+// earlier tiles left there, or stored when `first` says no earlier tile
+// reached them.
 struct TileSink {
     FI_GLOBAL float* row;
     FI_SHARED float* accw;
@@ -165,7 +166,7 @@ template <typename Get>
 __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n, const Get& get) {
     const int lane = team_tid();
     int m0 = 0;
-    if (s.accw) {
+    if (s.wend > i) {
         const int nl = (int)((s.wend - i) / 2) < n ? (int)((s.wend - i) / 2) : n;
 #pragma unroll 1
         for (int m = lane; m < nl; m += kTeam) {
@@ -588,7 +589,7 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
         // transform
         constexpr int NPA = (M / 2 - kRunBlock / 2 + kTeam - 1) / kTeam;
         RowAhead<NPA> ra;
-        const bool ahead = !out.first && out.accw != nullptr && out.wend - i == kRunBlock;
+        const bool ahead = !out.first && out.wend - i == kRunBlock;
         if (ahead) ra.load(out, i, M / 2);
         dit_lds<M, R * ct_base(M), float>(lds, tw);
         if (ahead) {
@@ -758,22 +759,22 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
 // sequences are packed in pairs into M = U complex points; the per-level
 // filter spectrum G (M + 2 entries) is untangled against the packing.
 // `row` holds the channel's input history (row[s] = x[s] for s < i).
-// xst, when not null, holds the input block x[i-U, i) in LDS (staged by the
-// caller), and spec_lds the tile's spectrum entries.
+// When x_staged, xst holds the input block x[i-U, i) in LDS (staged by the
+// caller); when spec_staged, spec_lds holds the tile's spectrum entries.
 // The sink's fields come as separate arguments (registers, not a stack copy).
 // The team synchronises after the call (no barrier at its end).
 __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row, const FI_GLOBAL V2* spec,
                                       FI_SHARED Cx<float>* lbuf, FI_GLOBAL Cx<float>* sc, TwPtr<float> tw,
                                       const FI_SHARED Cx<float>* twl, FI_SHARED float* accw, int64_t wend,
-                                      int wmask, int64_t L, bool first, const FI_SHARED float* xst,
-                                      const FI_SHARED V2* spec_lds) {
+                                      int wmask, int64_t L, bool first, bool x_staged, const FI_SHARED float* xst,
+                                      bool spec_staged, const FI_SHARED V2* spec_lds) {
     const TileSink out{row, accw, wend, wmask, L, first};
     const LdsTw ltw{twl};
     const int M = U;
     const FI_GLOBAL float* xblock = row + (i - U);
-    if (xst) {
+    if (x_staged) {
         const TileInLds xin{reinterpret_cast<const FI_SHARED V2*>(xst), M / 2};
-        if (spec_lds) {
+        if (spec_staged) {
             switch (M) {
                 case 128: fft_tile_lds<128>(i, xin, spec_lds, lbuf, ltw, out); return;
                 case 256: fft_tile_lds<256>(i, xin, spec_lds, lbuf, ltw, out); return;
@@ -858,7 +859,7 @@ __global__ __launch_bounds__(kTeam) void k_tile_fft(DevState d, int64_t i, int U
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)blockIdx.x * d.sc_stride;
         fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)(U + 2), lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl,
-                 nullptr, i, 0, d.L, false, nullptr, nullptr);
+                 reinterpret_cast<FI_SHARED float*>(lbuf), i, 0, d.L, false, false, nullptr, false, nullptr);
         team_sync_global();
     }
 }
@@ -1179,7 +1180,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     const FI_GLOBAL V2* spec =
                         gmem(static_cast<const V2*>(d.spec)) + d.spec_off[q] + c * (int64_t)(U + 2);
                     fft_tile(U, i, row, spec, lbuf, sc, tw, twl, accw, i + kBlk, wmask, L, i == U,
-                             stage_x ? xst : nullptr, stage_spec ? sst : nullptr);
+                             stage_x, xst, stage_spec, sst);
                     // the transform buffer reached the tap table: rebuild it
                     if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > t4_off) {
                         team_sync();
