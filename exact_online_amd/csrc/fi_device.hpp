@@ -149,6 +149,13 @@ __device__ __forceinline__ void team_sync() {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     }
 }
+// The barrier of NT threads at the team's front: the whole team, or its first
+// wavefront alone (whose LDS operations are ordered among themselves).
+template <int NT>
+__device__ __forceinline__ void group_sync() {
+    if constexpr (NT == kWave) wave_sync();
+    else team_sync();
+}
 __device__ __forceinline__ void team_sync_global() {
     if constexpr (kTeam == kWave) {
         wave_sync();
@@ -259,17 +266,19 @@ __device__ __forceinline__ constexpr int rev_r(int r) {
 // forward transform end in plain bit-reversed order.
 // Each butterfly reads and writes the same slots, so no staging is needed;
 // a thread processes its butterflies GRP at a time to overlap memory latency.
-template <int M, int S, bool INV, typename T, typename Src, typename Dst, typename Tw>
+// The stage is run by the team's first NT threads (the whole team, or its
+// first wavefront).
+template <int M, int S, bool INV, typename T, int NT = kTeam, typename Src, typename Dst, typename Tw>
 __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const Tw& tw) {
     constexpr int R = ct_radix(S, M);
     constexpr int Q = S / R;
     constexpr int NB = M / R;
-    constexpr int PER = (NB + kTeam - 1) / kTeam;
+    constexpr int PER = (NB + NT - 1) / NT;
     constexpr int GRP = PER < 2 ? PER : 2;
     const int lane = team_tid();
-    // When Q divides kTeam, a thread's butterflies (n = lane + kTeam u) all
+    // When Q divides NT, a thread's butterflies (n = lane + NT u) all
     // have j = lane mod Q: their twiddles are computed once.
-    constexpr bool ONE_J = S > R && kTeam % Q == 0;
+    constexpr bool ONE_J = S > R && NT % Q == 0;
     Cx<T> wj[R];
     if constexpr (ONE_J) {
         tw.template powers<R>(S, lane % Q, wj);
@@ -283,18 +292,18 @@ __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const T
         int off[GRP], jj[GRP];
 #pragma unroll
         for (int g = 0; g < GRP; ++g) {
-            const int n = lane + kTeam * (u0 + g);
+            const int n = lane + NT * (u0 + g);
             jj[g] = n % Q;
             off[g] = (n / Q) * S + jj[g];
-            if (NB % kTeam == 0 || n < NB) {
+            if (NB % NT == 0 || n < NB) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) v[g][r] = src(off[g], (INV ? rev_r<R>(r) : r) * Q);
             }
         }
 #pragma unroll
         for (int g = 0; g < GRP; ++g) {
-            const int n = lane + kTeam * (u0 + g);
-            if (NB % kTeam == 0 || n < NB) {
+            const int n = lane + NT * (u0 + g);
+            if (NB % NT == 0 || n < NB) {
                 if constexpr (INV) {
                     if constexpr (ONE_J) {
 #pragma unroll
@@ -317,18 +326,18 @@ __device__ __forceinline__ void ct_stage(const Src& src, const Dst& dst, const T
             }
         }
     }
-    team_sync();
+    group_sync<NT>();
 }
 
 // Forward M-point FFT (unnormalised), natural order in, bit-reversed order
 // out (position brev(k) holds frequency k): the first stage reads src,
 // the others work in place on the LDS buffer.
-template <int M, int S, typename T, typename Src, typename Tw>
+template <int M, int S, typename T, int NT = kTeam, typename Src, typename Tw>
 __device__ __forceinline__ void dif_lds(const Src& src, FI_SHARED Cx<T>* lds, const Tw& tw) {
     if constexpr (S > 1) {
-        if constexpr (S == M) ct_stage<M, S, false, T>(src, LdsOut<T>{lds}, tw);
-        else ct_stage<M, S, false, T>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
-        dif_lds<M, S / ct_radix(S, M), T>(src, lds, tw);
+        if constexpr (S == M) ct_stage<M, S, false, T, NT>(src, LdsOut<T>{lds}, tw);
+        else ct_stage<M, S, false, T, NT>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
+        dif_lds<M, S / ct_radix(S, M), T, NT>(src, lds, tw);
     }
 }
 
@@ -347,11 +356,11 @@ __device__ __forceinline__ void dif_lds_head(const Src& src, FI_SHARED Cx<T>* ld
 // order out, in place on the LDS buffer.  Every stage but the smallest has
 // radix ct_base(M), so the sizes run ct_smallest(M), ct_base(M) times that,
 // ..., M.
-template <int M, int S, typename T, typename Tw>
+template <int M, int S, typename T, int NT = kTeam, typename Tw>
 __device__ __forceinline__ void dit_lds(FI_SHARED Cx<T>* lds, const Tw& tw) {
     if constexpr (S <= M) {
-        ct_stage<M, S, true, T>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
-        if constexpr (S < M) dit_lds<M, S * ct_base(M), T>(lds, tw);
+        ct_stage<M, S, true, T, NT>(LdsIn<T>{lds}, LdsOut<T>{lds}, tw);
+        if constexpr (S < M) dit_lds<M, S * ct_base(M), T, NT>(lds, tw);
     }
 }
 

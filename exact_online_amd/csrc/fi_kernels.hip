@@ -162,14 +162,15 @@ struct TileSink {
 // Adds w[m] = (a, b) to positions (i + 2m, i + 2m + 1) for m in [0, n):
 // the first (wend - i) / 2 pairs into the LDS ring, the rest into the row;
 // global read-modify-writes go kBatch thread-strided chunks at a time.
-template <typename Get>
+// Run by the team's first NT threads.
+template <int NT = kTeam, typename Get>
 __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n, const Get& get) {
     const int lane = team_tid();
     int m0 = 0;
     if (s.wend > i) {
         const int nl = (int)((s.wend - i) / 2) < n ? (int)((s.wend - i) / 2) : n;
 #pragma unroll 1
-        for (int m = lane; m < nl; m += kTeam) {
+        for (int m = lane; m < nl; m += NT) {
             const int64_t o = i + 2 * (int64_t)m;
             if (o < s.L) {
                 const Cx<float> w = get(m);
@@ -181,7 +182,7 @@ __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n,
     }
     if (s.first) {
 #pragma unroll 4
-        for (int m = m0 + lane; m < n; m += kTeam) {
+        for (int m = m0 + lane; m < n; m += NT) {
             const int64_t o = i + 2 * (int64_t)m;
             if (o + 1 < s.L) {
                 const Cx<float> w = get(m);
@@ -193,19 +194,19 @@ __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n,
         return;
     }
 #pragma unroll 1
-    for (; m0 < n; m0 += kTeam * kBatch) {
+    for (; m0 < n; m0 += NT * kBatch) {
         V2 v[kBatch];
         Cx<float> w[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int m = m0 + lane + kTeam * u;
+            const int m = m0 + lane + NT * u;
             const int64_t o = i + 2 * (int64_t)m;
             if (m < n && o + 1 < s.L) v[u] = *reinterpret_cast<const FI_GLOBAL V2*>(s.row + o);
             if (m < n) w[u] = get(m);
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int m = m0 + lane + kTeam * u;
+            const int m = m0 + lane + NT * u;
             const int64_t o = i + 2 * (int64_t)m;
             if (m < n && o + 1 < s.L) {
                 *reinterpret_cast<FI_GLOBAL V2*>(s.row + o) = V2{v[u].x + w[u].x, v[u].y + w[u].y};
@@ -326,8 +327,8 @@ struct TwGlobalN {
 
 constexpr int kUntangleBatch = 4;   // pairs per thread per untangle batch
 
-// Filter entries of one batch of NB pairs per thread (pairs n0 + tid + kTeam u).
-template <int NB>
+// Filter entries of one batch of NB pairs per thread (pairs n0 + tid + NT u).
+template <int NB, int NT = kTeam>
 struct SpecBatch {
     V2 ga[NB], gb[NB];
     template <typename SpecP, typename Pos>
@@ -335,7 +336,7 @@ struct SpecBatch {
         const int lane = team_tid();
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            const int n = n0 + lane + kTeam * u;
+            const int n = n0 + lane + NT * u;
             int a, b;
             pos(n < nitems ? n : 0, a, b);
             if (n < nitems) {
@@ -351,22 +352,23 @@ struct SpecBatch {
 // frequency of slot a is brev(pos_off + a) over lbits bits; gM is G[M] / (4M),
 // the partner entry of frequency 0.  `cur` holds the first batch's filter
 // entries, loaded by the caller (ahead of the forward transform); each later
-// batch is loaded while the one before it is processed.
-template <int NB, typename SpecP, typename Pos, typename TwF>
+// batch is loaded while the one before it is processed.  Run by the team's
+// first NT threads.
+template <int NB, int NT = kTeam, typename SpecP, typename Pos, typename TwF>
 __device__ __forceinline__ void untangle_lds(FI_SHARED Cx<float>* lds, SpecP spec, V2 gM, int nitems,
                                              const Pos& pos, int pos_off, int lbits, const TwF& twf,
-                                             SpecBatch<NB> cur) {
+                                             SpecBatch<NB, NT> cur) {
     const int lane = team_tid();
 #pragma unroll 1
-    for (int n0 = 0; n0 < nitems; n0 += kTeam * NB) {
-        SpecBatch<NB> nxt;
-        if (n0 + kTeam * NB < nitems) nxt.load(spec, n0 + kTeam * NB, nitems, pos);
+    for (int n0 = 0; n0 < nitems; n0 += NT * NB) {
+        SpecBatch<NB, NT> nxt;
+        if (n0 + NT * NB < nitems) nxt.load(spec, n0 + NT * NB, nitems, pos);
         // the pairs of a batch are disjoint: all reads first, then all writes
         Cx<float> za[NB], zb[NB], w[NB];
         int pa[NB], pb[NB];
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            const int n = n0 + lane + kTeam * u;
+            const int n = n0 + lane + NT * u;
             pos(n < nitems ? n : 0, pa[u], pb[u]);
             za[u] = lds[lp(pa[u])];
             zb[u] = lds[lp(pb[u])];
@@ -380,14 +382,14 @@ __device__ __forceinline__ void untangle_lds(FI_SHARED Cx<float>* lds, SpecP spe
         }
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            if (n0 + lane + kTeam * u < nitems) {
+            if (n0 + lane + NT * u < nitems) {
                 lds[lp(pa[u])] = za[u];
                 lds[lp(pb[u])] = zb[u];
             }
         }
         cur = nxt;
     }
-    team_sync();
+    group_sync<NT>();
 }
 
 // ---------------------------------------------------------------- middle
@@ -599,17 +601,26 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
     } else {
         // small transforms: too few groups to spread the fused pass over the
         // team, so the last and first stages stay separate from an untangle
-        // pass over single pairs
-        constexpr int NALL = M / 2 / kTeam + 1;
-        constexpr int NB = NALL < kUntangleBatch ? NALL : kUntangleBatch;
-        SpecBatch<NB> first;
-        if constexpr (!staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
-        dif_lds<M, M, float>(xin, lds, tw);
-        if constexpr (staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
-        untangle_lds<NB>(lds, spec, gM, M / 2 + 1, PairsAll{}, 0, ilog2(M), TwLdsN{tw.A, 2 * M}, first);
-        dit_lds<M, R, float>(lds, tw);
+        // pass over single pairs.  Up to 256 points a stage is at most one
+        // butterfly per lane of one wavefront: the first wavefront runs the
+        // whole tile alone, its LDS operations ordered among themselves, with
+        // no team barrier between the stages (the others wait for it at the
+        // caller's barrier).
+        constexpr int NT = M <= 256 ? kWave : kTeam;
+        if (NT == kTeam || __builtin_amdgcn_readfirstlane(team_tid()) < kWave) {
+            constexpr int NALL = M / 2 / NT + 1;
+            constexpr int NB = NALL < kUntangleBatch ? NALL : kUntangleBatch;
+            SpecBatch<NB, NT> first;
+            if constexpr (!staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
+            dif_lds<M, M, float, NT>(xin, lds, tw);
+            if constexpr (staged) first.load(spec, 0, M / 2 + 1, PairsAll{});
+            untangle_lds<NB, NT>(lds, spec, gM, M / 2 + 1, PairsAll{}, 0, ilog2(M), TwLdsN{tw.A, 2 * M}, first);
+            dit_lds<M, R, float, NT>(lds, tw);
+            // point M/2 + m carries outputs 2m, 2m + 1 of the tile
+            tile_output<NT>(out, i, M / 2, [lds](int m) { return lds[lp(M / 2 + m)]; });
+        }
+        return;
     }
-    // point M/2 + m carries outputs 2m, 2m + 1 of the tile
     tile_output(out, i, M / 2, [lds](int m) { return lds[lp(M / 2 + m)]; });
 }
 
