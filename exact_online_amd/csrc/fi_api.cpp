@@ -87,20 +87,24 @@ int build(fi_handle *s, const void *h) {
     d.F = d.umax_fft > 0 ? (d.umax_fft < fi::kLdsFftMax ? d.umax_fft : fi::kLdsFftMax) : 1;
     // FFT region of the persistent pass: the largest LDS transform, or the
     // staging of a tile's input (4U bytes) and, for U <= 1024, its spectrum
-    // (8 (U + 2) bytes) behind that tile's own transform buffer
-    // The chain's tap table sits at the top of the region, above every
-    // staging area (it is rebuilt after a tile whose transform reaches it).
+    // (8 (U + 2) bytes) behind that tile's own transform buffer.  Above every
+    // staging area: the data of the tile of side kRunBlock (done on the
+    // matrix cores), then the chain's tap table at the top of the region
+    // (both rebuilt after a tile whose transform reaches them).
     int staged = 0;
     for (int q = 0; q < fi::kMaxLevels; ++q) {
         if (d.spec_off[q] < 0) continue;
         const int U = 1 << q;
         int need = 0;
-        if (U <= 1024) need = fi::lds_fft_elems(U) * 8 + 4 * U + 8 * (U + 2);
+        if (U == fi::kRunBlock) need = 0;   // the matrix-core tile: its own area
+        else if (U <= 1024) need = fi::lds_fft_elems(U) * 8 + 4 * U + 8 * (U + 2);
         else if (U <= 2048) need = fi::lds_fft_elems(U) * 8 + 4 * U;
         if (need > staged) staged = need;
     }
+    d.mm_off = (staged + 15) / 16 * 16;
     d.fftreg = fi::lds_fft_elems(d.F) * 8;
-    if (staged + fi::kTapTableBytes > d.fftreg) d.fftreg = staged + fi::kTapTableBytes;
+    if (d.mm_off + fi::kMmBytes + fi::kTapTableBytes > d.fftreg)
+        d.fftreg = d.mm_off + fi::kMmBytes + fi::kTapTableBytes;
 
     FI_HIP(dalloc(&d.hT, (size_t)(d.D * d.LS) * sizeof(float)));
     FI_HIP(dalloc(&d.state, (size_t)(d.C * d.LS) * sizeof(float)));

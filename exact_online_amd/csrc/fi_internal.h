@@ -16,6 +16,14 @@ constexpr int kTwLds = 132;       // LDS twiddle table: w_64^a, w_4096^b (64 eac
 constexpr int kTapTableBytes = (64 + kRunBlock + 4) * 16;
 // LDS FFT buffers hold one spare slot per 8 points (bank spreading).
 constexpr int lds_fft_elems(int M) { return M + M / 8; }
+// The run kernel's tile of side kRunBlock on the matrix cores keeps in its
+// FFT region, above every staging area of the tiles up to 2048 points, the
+// input block zero-padded (15 zeros before, 65 after) and the filter
+// h[-64, 2 kRunBlock) (zero at negative lags) with one spare slot per 16
+// (bank spreading).
+constexpr int kMmXFloats = 15 + kRunBlock + 65;
+constexpr int kMmHSlots = (64 + 2 * kRunBlock) + (64 + 2 * kRunBlock) / 16 + 4;
+constexpr int kMmBytes = (kMmXFloats + kMmHSlots) * 4;
 
 // Device state of one handle.  Layouts (rows padded to LS = L rounded up to 64):
 //   hT[D][LS]      filter, one contiguous row per channel c, fp32
@@ -39,6 +47,7 @@ struct DevState {
     int XR;                // LDS ring of recent inputs (positions)
     int F;                 // LDS FFT buffer (complex points) of the run kernel
     int fftreg;            // bytes of the run kernel's LDS FFT / staging region
+    int mm_off;            // bytes: its matrix-core tile data (above the staging areas)
     int io_bf16;
     float *hT;
     float *state;

@@ -910,6 +910,89 @@ __device__ __forceinline__ void for_segments(F&& f) {
         for_segments<K0 + 1>(f);
     }
 }
+// f(integral_constant<int, N>) for N = N0 .. N1-1, in order.
+template <int N0, int N1, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (N0 < N1) {
+        f(std::integral_constant<int, N0>{});
+        static_for<N0 + 1, N1>(f);
+    }
+}
+
+// ------------------------------------------------ tile of side kBlk, MFMA
+// The tile at a block boundary i with U = lowbit(i) = kBlk = 256 (the pages'
+// relaxed tiling: inputs [i-256, i), outputs [i, i+256), filter lags
+// 1 .. 511), as a direct Toeplitz product on the matrix cores.
+// Outputs q = a + 16 alpha (a, alpha < 16) and inputs p = a - d + 16 bt, with
+// d = (a - p) mod 16 in [0, 16) and bt in [0, 17): the lag is
+//   256 + q - p = 256 + d + 16 (alpha - bt),
+// which does not depend on a.  So with K = (d, bt) and
+//   A_d[alpha][bt] = h[256 + d + 16 (alpha - bt)],  B_d[bt][a] = x[a - d + 16 bt]
+// (x = 0 outside [0, 256)), y[a + 16 alpha] = sum_d (A_d B_d)[alpha][a]: per
+// d five 16x16x4 fp32 MFMA steps over bt = 4c + kk (bt = 17 .. 19 meet zero
+// inputs), 80 steps in all.  The 16x16 result is added into the LDS ring
+// (the next block's accumulators).
+//   xz[15 + p] = x[p], zero for p in [-15, 0) and [256, 321);
+//   hsk[s(g)] = h[g] for g in [-64, 512) (zero for g < 0 and g >= L), at
+//     slot s(g) = (g + 64) + (g + 64) / 16: consecutive alpha - kk = j read
+//     slots 17 apart (distinct banks).
+// MFMA lane layout (16x16x4): A[i][k] in lane i + 16k, B[k][j] in lane
+// j + 16k, D[i][j] in lane j + 16 (i / 4), register i % 4.
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void mm_tile256(const FI_SHARED float* xz, const FI_SHARED float* hsk,
+                                           FI_SHARED float* ring) {
+    static_assert(kBlk == 256, "the matrix-core tile covers one 256-position block");
+    const int tid = team_tid();
+    const int l = tid & (kWave - 1);
+    const int al = l & 15, kk = l >> 4;
+    // A of step (d, c), lane (alpha, kk): lag g = 256 + d - 64 c + 16 j with
+    // j = alpha - kk; with G = g - 16 j + 64 = 320 + d - 64 c (>= 64), s(g) =
+    // G + G / 16 + 17 j (16 j / 16 = j exactly)
+    const FI_SHARED float* ab = hsk + 17 * (al - kk);
+    // B of step (d, c), lane (a, kk): x[a - d + 16 (4c + kk)] = xz[a + 16 kk + 64 c - d + 15]
+    const FI_SHARED float* bb = xz + al + 16 * kk;
+    // The team's first wavefront alone: the others share their SIMDs with
+    // other teams' chains, which matrix work beside them slows down.  The
+    // operands of a group of kG steps are loaded while the group before it
+    // is multiplied; four accumulators keep four products in flight.
+    constexpr int kSteps = 80, kG = 8, kGroups = kSteps / kG;
+    if (__builtin_amdgcn_readfirstlane(tid) < kWave) {
+        v4f acc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+        float av[2][kG], bv[2][kG];
+        auto load = [&](auto gc) {
+            constexpr int g = decltype(gc)::value;
+            static_for<0, kG>([&](auto uc) {
+                constexpr int n = g * kG + decltype(uc)::value;
+                constexpr int d = n / 5, c = n % 5;
+                constexpr int G = 320 + d - 64 * c;
+                av[g & 1][n % kG] = ab[G + G / 16];
+                bv[g & 1][n % kG] = bb[64 * c - d + 15];
+            });
+        };
+        load(std::integral_constant<int, 0>{});
+        static_for<0, kGroups>([&](auto gc) {
+            constexpr int g = decltype(gc)::value;
+            // the scheduler keeps the next group's loads ahead of this
+            // group's products
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (g + 1 < kGroups) load(std::integral_constant<int, g + 1>{});
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, kG>([&](auto uc) {
+                constexpr int u = decltype(uc)::value, n = g * kG + u;
+                acc[n & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[g & 1][u], bv[g & 1][u], acc[n & 3], 0, 0, 0);
+            });
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        // D[alpha][a] in lane a + 16 (alpha / 4), register alpha % 4:
+        // position q = a + 16 alpha of the next block
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            ring[al + 16 * (4 * kk + r)] += (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+    }
+}
+
 constexpr int kTapBatch = 4;         // chain: taps loaded per batch, one batch ahead
 constexpr int kStageSpecMax = 1024;  // tiles up to this side get spectrum and input staged in LDS
 // (FFT buffer 9M bytes + input 4U + spectrum 8 (U + 2) fits the 36 KiB region
@@ -983,6 +1066,19 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             tz[e] = V4{v[0], v[1], v[2], v[3]};
         }
     };
+    // the matrix-core tile's zero-padded input block and its filter h[-64,
+    // 512) at slots (g + 64) + (g + 64) / 16 (zero at g < 0 and g >= L):
+    // built when a channel starts and after a tile whose transform reaches
+    // them
+    FI_SHARED float* mxz = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.mm_off);
+    FI_SHARED float* mhs = mxz + kMmXFloats;
+    auto build_mm = [&](const FI_GLOBAL float* hrow) {
+        for (int q = tid; q < kMmXFloats; q += kTeam) mxz[q] = 0.f;
+        for (int e = tid; e < 64 + 2 * kBlk; e += kTeam) {
+            const int g = e - 64;
+            mhs[e + e / 16] = (g >= 0 && g < L) ? hrow[g] : 0.f;
+        }
+    };
     fill_lds_twiddles(twl);
 
     for (int64_t ch = ch0; ch < d.C; ch += G) {
@@ -994,6 +1090,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
         if (direct)
             for (int q = tid; q < 2 * d.T; q += kTeam) htap[q] = q < L ? hrow[q] : 0.f;
         build_taps4(hrow);
+        build_mm(hrow);
         team_sync();
         const float ch0v = tap_scale * hrow[0];   // closed loop: c h[0]
 
@@ -1021,11 +1118,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             // idle LDS FFT region while the chain runs
             const int64_t inext = t0 + kBlk;
             const int Un = inext < L ? (int)(inext & -inext) : 0;
-            const bool stage_x = Un > d.T && Un <= 2 * kStageSpecMax;
-            const bool stage_spec = Un > d.T && Un <= kStageSpecMax;
+            // next tile of side kBlk: on the matrix cores (mm_tile256)
+            const bool mm_next = Un == kBlk && Un > d.T;
+            const bool stage_x = Un > d.T && Un <= 2 * kStageSpecMax && !mm_next;
+            const bool stage_spec = Un > d.T && Un <= kStageSpecMax && !mm_next;
             FI_SHARED float* xst = reinterpret_cast<FI_SHARED float*>(lbuf + lds_fft_elems(Un));
             FI_SHARED V2* sst = reinterpret_cast<FI_SHARED V2*>(xst + Un);
-            const bool row_input = Un > d.T && !stage_x;   // next tile: FFT reading the row
+            const bool row_input = Un > d.T && !stage_x && !mm_next;   // next tile: FFT reading the row
             // y, x_out and the input history: before a tile that reads its
             // input block from the row, after one that has it staged in LDS
             auto store_block = [&]() {
@@ -1174,6 +1273,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     const int64_t tl = t0 + kWave * k + lane;
                     if (direct) xring[tl & xmask] = xk[k];
                     if (stage_x) xst[Un - kBlk + kWave * k + lane] = xk[k];   // completes the staged input block
+                    if (mm_next) mxz[15 + kWave * k + lane] = xk[k];
                     accw[(kWave * k + lane) & wmask] = nx[k];  // slot of position t now holds position t + W
                 }
                 if (row_input) store_block();
@@ -1186,16 +1286,20 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 const int U = (int)(i & -i);
                 if (U <= d.T) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
+                } else if (U == kBlk) {
+                    mm_tile256(mxz, mhs, accw);
                 } else {
                     const int q = ilog2(U);
                     const FI_GLOBAL V2* spec =
                         gmem(static_cast<const V2*>(d.spec)) + d.spec_off[q] + c * (int64_t)(U + 2);
                     fft_tile(U, i, row, spec, lbuf, sc, tw, twl, accw, i + kBlk, wmask, L, i == U,
                              stage_x, xst, stage_spec, sst);
-                    // the transform buffer reached the tap table: rebuild it
-                    if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > t4_off) {
+                    // the transform buffer reached the matrix-core tile's data
+                    // and the tap table: rebuild them
+                    if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > d.mm_off) {
                         team_sync();
-                        build_taps4(hrow);
+                        if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > t4_off) build_taps4(hrow);
+                        build_mm(hrow);
                     }
                 }
                 // The chain wavefront reads the ring and (a block later) the row
