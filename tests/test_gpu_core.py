@@ -71,7 +71,8 @@ def test_small_mixer_open_steps():
 
 
 @pytest.mark.parametrize("L,T", [(1, 64), (2, 64), (5, 64), (63, 64), (64, 64), (65, 64), (100, 64),
-                                 (129, 64), (1000, 64), (3000, 128), (5000, 64)])
+                                 (129, 64), (257, 64), (300, 0), (511, 64), (513, 64), (1000, 64),
+                                 (3000, 128), (5000, 64)])
 def test_ragged_lengths_open(L, T):
     w = small(B=2, D=3, L=L, seed=L)
     log("case ragged open L", L, "T", T)
@@ -102,16 +103,18 @@ def test_delta_filters_hit_every_level(T):
         ref[k:] = x[0, :L - k, c]
         err = np.abs(y[0, :, c] - ref).max()
         assert err <= 2e-5, (k, err)
-        # positions before the first FFT tile see only direct and in-register
-        # tiles of a single nonzero tap: exact
-        first_fft = 2 * T if T >= 64 else 128
+        # positions before the first FFT tile (side 512: the tiles of side
+        # 256 are direct products, on the matrix cores or from LDS) see only
+        # direct tiles of a single nonzero tap: exact
+        first_fft = max(2 * T, 512)
         assert np.array_equal(y[0, :first_fft, c], ref[:first_fft].astype(np.float32)), k
 
 
-@pytest.mark.parametrize("L,T", [(8192, 128), (512, 256)])
+@pytest.mark.parametrize("L,T", [(8192, 128), (8192, 0), (512, 256)])
 def test_integer_data(L, T):
     """x, h in {-3..3}: direct tiles are exact; FFT tiles round to the exact
-    integer (|y| < 2^24)."""
+    integer (|y| < 2^24).  Positions below 512 see no FFT tile (the tiles of
+    side 256 are direct products), so they are exact too."""
     D, B = 4, 2
     r = np.random.default_rng(9)
     h = r.integers(-3, 4, size=(L, D)).astype(np.float32)
@@ -122,6 +125,7 @@ def test_integer_data(L, T):
     ref = orc().conv_open(h, x)
     assert np.array_equal(np.rint(y), ref)
     assert np.abs(y - ref).max() < 0.05
+    assert np.array_equal(y[:, :512], ref[:, :512])
     if L <= 2 * T:   # every tile direct (the largest tile side is L/2)
         assert np.array_equal(y, ref)
 
@@ -165,7 +169,7 @@ def test_small_mixer_closed(T):
     assert np.abs(y - ytf).max() <= 1e-4
 
 
-@pytest.mark.parametrize("L", [1, 3, 64, 65, 700, 3000])
+@pytest.mark.parametrize("L", [1, 3, 64, 65, 300, 511, 700, 3000])
 def test_ragged_closed(L):
     w = small(B=2, D=3, L=L, seed=L + 1)
     log("case ragged closed L", L)
