@@ -160,9 +160,12 @@ struct TileSink {
 };
 
 // Adds w[m] = (a, b) to positions (i + 2m, i + 2m + 1) for m in [0, n):
-// the first (wend - i) / 2 pairs into the LDS ring, the rest into the row;
-// global read-modify-writes go kBatch thread-strided chunks at a time.
-// Run by the team's first NT threads.
+// the first (wend - i) / 2 pairs into the LDS ring, the rest into the row
+// (stored when the sink is its level's first, else added), kBatch
+// thread-strided pairs at a time.  Every load of a batch is issued before
+// any is used, from a clamped in-range index where the pair is out of range
+// (a load under a branch would wait for the ones before it).  Run by the
+// team's first NT threads.
 template <int NT = kTeam, typename Get>
 __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n, const Get& get) {
     const int lane = team_tid();
@@ -180,19 +183,6 @@ __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n,
         }
         m0 = nl;
     }
-    if (s.first) {
-#pragma unroll 4
-        for (int m = m0 + lane; m < n; m += NT) {
-            const int64_t o = i + 2 * (int64_t)m;
-            if (o + 1 < s.L) {
-                const Cx<float> w = get(m);
-                *reinterpret_cast<FI_GLOBAL V2*>(s.row + o) = V2{w.x, w.y};
-            } else if (o < s.L) {
-                s.row[o] = get(m).x;
-            }
-        }
-        return;
-    }
 #pragma unroll 1
     for (; m0 < n; m0 += NT * kBatch) {
         V2 v[kBatch];
@@ -201,17 +191,18 @@ __device__ __forceinline__ void tile_output(const TileSink& s, int64_t i, int n,
         for (int u = 0; u < kBatch; ++u) {
             const int m = m0 + lane + NT * u;
             const int64_t o = i + 2 * (int64_t)m;
-            if (m < n && o + 1 < s.L) v[u] = *reinterpret_cast<const FI_GLOBAL V2*>(s.row + o);
-            if (m < n) w[u] = get(m);
+            w[u] = get(m < n ? m : n - 1);
+            if (!s.first) v[u] = *reinterpret_cast<const FI_GLOBAL V2*>(s.row + (m < n && o + 1 < s.L ? o : 0));
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int m = m0 + lane + NT * u;
             const int64_t o = i + 2 * (int64_t)m;
+            const V2 r = s.first ? V2{w[u].x, w[u].y} : V2{v[u].x + w[u].x, v[u].y + w[u].y};
             if (m < n && o + 1 < s.L) {
-                *reinterpret_cast<FI_GLOBAL V2*>(s.row + o) = V2{v[u].x + w[u].x, v[u].y + w[u].y};
+                *reinterpret_cast<FI_GLOBAL V2*>(s.row + o) = r;
             } else if (m < n && o < s.L) {
-                s.row[o] += w[u].x;
+                s.row[o] = s.first ? w[u].x : s.row[o] + w[u].x;
             }
         }
     }
@@ -231,7 +222,9 @@ struct RowAhead {
         for (int u = 0; u < NP; ++u) {
             const int m = kRunBlock / 2 + lane + kTeam * u;
             const int64_t o = i + 2 * (int64_t)m;
-            if (m < n && o + 1 < s.L) v[u] = *reinterpret_cast<const FI_GLOBAL V2*>(s.row + o);
+            // unconditional (a load under a branch would wait for the ones
+            // before it): out-of-range pairs read position 0 and are unused
+            v[u] = *reinterpret_cast<const FI_GLOBAL V2*>(s.row + (m < n && o + 1 < s.L ? o : 0));
         }
     }
 };
@@ -286,14 +279,17 @@ __device__ __forceinline__ void untangle_pair(Cx<float>& A, Cx<float>& B, Cx<flo
     A = cadd(Ss, Ee);
     B = cconj(csub(Ss, Ee));
 }
-// Forward-FFT input of the tile: z[n] = x[2n] + i x[2n+1] for n < M/2, zero
-// beyond (the input block padded on the right).
+// Forward-FFT input of the tile: z[n] = x[2n] + i x[2n+1] for n < HALF,
+// zero beyond (the input block padded on the right).  d is a constant once
+// the stage is unrolled, so a slot that is padding in every butterfly is a
+// constant zero.
+template <int HALF>
 struct TileIn {
     const FI_GLOBAL V2* xs;
-    int half;
     __device__ __forceinline__ Cx<float> operator()(int off, int d) const {
+        if (d >= HALF) return {0.f, 0.f};
         const int n = off + d;
-        if (n < half) {
+        if (n < HALF) {
             const V2 v = xs[n];
             return {v.x, v.y};
         }
@@ -338,11 +334,9 @@ struct SpecBatch {
         for (int u = 0; u < NB; ++u) {
             const int n = n0 + lane + NT * u;
             int a, b;
-            pos(n < nitems ? n : 0, a, b);
-            if (n < nitems) {
-                ga[u] = spec[a];
-                gb[u] = spec[b];
-            }
+            pos(n < nitems ? n : 0, a, b);   // item 0 stands in past the end (unused)
+            ga[u] = spec[a];
+            gb[u] = spec[b];
         }
     }
 };
@@ -550,12 +544,13 @@ struct PairsMirror {
 };
 
 // The same input staged in LDS.
+template <int HALF>
 struct TileInLds {
     const FI_SHARED V2* xs;
-    int half;
     __device__ __forceinline__ Cx<float> operator()(int off, int d) const {
+        if (d >= HALF) return {0.f, 0.f};
         const int n = off + d;
-        if (n < half) {
+        if (n < HALF) {
             const V2 v = xs[n];
             return {v.x, v.y};
         }
@@ -652,7 +647,7 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
         GroupSpec<R> g0;
         middle_groups<false, F / R>(tid, ga, gb);
         g0.load(spec, ga, gb);
-        dif_lds_head<F, F, float>(TileIn{xs, F}, lbuf, ltw);
+        dif_lds_head<F, F, float>(TileIn<F>{xs}, lbuf, ltw);
         middle_lds<F, false>(lbuf, spec, gM, ltw, g0);
         dit_lds<F, R * ct_base(F), float>(lbuf, ltw);
         copy_from_lds(sc, lbuf, F);
@@ -682,11 +677,20 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
     constexpr int F = kLdsFftMax;
     const int P = M / F;
     const int half = M >> 1;
-    for (int j = lane; j < half; j += kTeam) {   // first pass fused with the load (upper half is 0)
-        const V2 v = xs[j];
-        const Cx<float> z = {v.x, v.y};
-        sc[j] = z;
-        sc[j + half] = cmul(z, twiddle<false>(tw, M, j));
+    // first pass fused with the load (upper half is 0), kBatch loads in
+    // flight per thread (half is a multiple of kTeam * kBatch)
+#pragma unroll 1
+    for (int j0 = 0; j0 < half; j0 += kTeam * kBatch) {
+        V2 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) v[u] = xs[j0 + lane + kTeam * u];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = j0 + lane + kTeam * u;
+            const Cx<float> z = {v[u].x, v[u].y};
+            sc[j] = z;
+            sc[j + half] = cmul(z, twiddle<false>(tw, M, j));
+        }
     }
     team_sync_global();
     global_dif(sc, M, half, F, tw);   // radix-8 stages down to F-point blocks
@@ -784,29 +788,29 @@ __device__ __forceinline__ void fft_tile(int U, int64_t i, FI_GLOBAL float* row,
     const int M = U;
     const FI_GLOBAL float* xblock = row + (i - U);
     if (x_staged) {
-        const TileInLds xin{reinterpret_cast<const FI_SHARED V2*>(xst), M / 2};
+        const FI_SHARED V2* xsl = reinterpret_cast<const FI_SHARED V2*>(xst);
         if (spec_staged) {
             switch (M) {
-                case 128: fft_tile_lds<128>(i, xin, spec_lds, lbuf, ltw, out); return;
-                case 256: fft_tile_lds<256>(i, xin, spec_lds, lbuf, ltw, out); return;
-                case 512: fft_tile_lds<512>(i, xin, spec_lds, lbuf, ltw, out); return;
-                case 1024: fft_tile_lds<1024>(i, xin, spec_lds, lbuf, ltw, out); return;
+                case 128: fft_tile_lds<128>(i, TileInLds<64>{xsl}, spec_lds, lbuf, ltw, out); return;
+                case 256: fft_tile_lds<256>(i, TileInLds<128>{xsl}, spec_lds, lbuf, ltw, out); return;
+                case 512: fft_tile_lds<512>(i, TileInLds<256>{xsl}, spec_lds, lbuf, ltw, out); return;
+                case 1024: fft_tile_lds<1024>(i, TileInLds<512>{xsl}, spec_lds, lbuf, ltw, out); return;
                 default: break;
             }
         } else if (M == 2048) {
-            fft_tile_lds<2048>(i, xin, spec, lbuf, ltw, out);
+            fft_tile_lds<2048>(i, TileInLds<1024>{xsl}, spec, lbuf, ltw, out);
             return;
         }
     }
-    const TileIn xg{reinterpret_cast<const FI_GLOBAL V2*>(xblock), M / 2};
+    const FI_GLOBAL V2* xg = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
     switch (M) {
-        case 64: fft_tile_lds<64>(i, xg, spec, lbuf, ltw, out); return;
-        case 128: fft_tile_lds<128>(i, xg, spec, lbuf, ltw, out); return;
-        case 256: fft_tile_lds<256>(i, xg, spec, lbuf, ltw, out); return;
-        case 512: fft_tile_lds<512>(i, xg, spec, lbuf, ltw, out); return;
-        case 1024: fft_tile_lds<1024>(i, xg, spec, lbuf, ltw, out); return;
-        case 2048: fft_tile_lds<2048>(i, xg, spec, lbuf, ltw, out); return;
-        case 4096: fft_tile_lds<4096>(i, xg, spec, lbuf, ltw, out); return;
+        case 64: fft_tile_lds<64>(i, TileIn<32>{xg}, spec, lbuf, ltw, out); return;
+        case 128: fft_tile_lds<128>(i, TileIn<64>{xg}, spec, lbuf, ltw, out); return;
+        case 256: fft_tile_lds<256>(i, TileIn<128>{xg}, spec, lbuf, ltw, out); return;
+        case 512: fft_tile_lds<512>(i, TileIn<256>{xg}, spec, lbuf, ltw, out); return;
+        case 1024: fft_tile_lds<1024>(i, TileIn<512>{xg}, spec, lbuf, ltw, out); return;
+        case 2048: fft_tile_lds<2048>(i, TileIn<1024>{xg}, spec, lbuf, ltw, out); return;
+        case 4096: fft_tile_lds<4096>(i, TileIn<2048>{xg}, spec, lbuf, ltw, out); return;
         default: break;
     }
     fft_tile_big(M, i, xblock, spec, lbuf, sc, tw, twl, row, accw, wend, wmask, L, first);
