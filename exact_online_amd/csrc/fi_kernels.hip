@@ -315,6 +315,13 @@ struct TwLdsN {
         return r ? cmul(w, t[128 + r * (4 / s)]) : w;
     }
 };
+// w_{2 kLdsFftMax}^k from the same table with no branch (C[0] = 1, and a
+// product with it is exact), so the table reads of neighbouring calls are not
+// serialised behind one another.
+__device__ __forceinline__ Cx<float> tw_lds_2f(const FI_SHARED Cx<float>* t, int k) {
+    const int j = k >> 1;
+    return cmul(cmul(t[j >> 6], t[64 + (j & 63)]), t[128 + 2 * (k & 1)]);
+}
 struct TwGlobalN {
     TwPtr<float> tw;
     int N;
@@ -640,7 +647,6 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
         constexpr int R = ct_smallest(F);
         const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
         const V2 gM = spec[M];
-        const TwLdsN twn{twl, 2 * F};
         const int tid = team_tid();
         int ga, gb;
         // half 0: the even frequencies, a 4096-point tile of its own
@@ -657,9 +663,9 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
         dif_lds_head<F, F, float>(TileInTw{xs, twl}, lbuf, ltw);
         middle_lds<F, true>(lbuf, spec + F, gM, ltw, g0);
         dit_lds<F, R * ct_base(F), float>(lbuf, ltw);
-        tile_output(out, i, F, [sc, lbuf, twn](int j) {
+        tile_output(out, i, F, [sc, lbuf, twl](int j) {
             const Cx<float> v0 = sc[j];
-            const Cx<float> v1 = cmul(lbuf[lp(j)], cconj(twn(j)));
+            const Cx<float> v1 = cmul(lbuf[lp(j)], cconj(tw_lds_2f(twl, j)));
             return csub(v0, v1);
         });
         return;
