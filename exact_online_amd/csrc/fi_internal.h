@@ -20,10 +20,11 @@ constexpr int lds_fft_elems(int M) { return M + M / 8; }
 // FFT region, above every staging area of the tiles up to 2048 points, the
 // input block zero-padded (15 zeros before, 65 after) and the filter
 // h[-64, 2 kRunBlock) (zero at negative lags) with one spare slot per 16
-// (bank spreading).
+// (bank spreading), then the block's outputs y (handed to the other
+// wavefronts, which store them during that tile).
 constexpr int kMmXFloats = 15 + kRunBlock + 65;
 constexpr int kMmHSlots = (64 + 2 * kRunBlock) + (64 + 2 * kRunBlock) / 16 + 4;
-constexpr int kMmBytes = (kMmXFloats + kMmHSlots) * 4;
+constexpr int kMmBytes = (kMmXFloats + kMmHSlots + kRunBlock) * 4;
 
 // Device state of one handle.  Layouts (rows padded to LS = L rounded up to 64):
 //   hT[D][LS]      filter, one contiguous row per channel c, fp32

@@ -1082,6 +1082,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     // them
     FI_SHARED float* mxz = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.mm_off);
     FI_SHARED float* mhs = mxz + kMmXFloats;
+    FI_SHARED float* myb = mhs + kMmHSlots;   // the block's y, for the other wavefronts' stores
     auto build_mm = [&](const FI_GLOBAL float* hrow) {
         for (int q = tid; q < kMmXFloats; q += kTeam) mxz[q] = 0.f;
         for (int e = tid; e < 64 + 2 * kBlk; e += kTeam) {
@@ -1136,7 +1137,10 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             FI_SHARED V2* sst = reinterpret_cast<FI_SHARED V2*>(xst + Un);
             const bool row_input = Un > d.T && !stage_x && !mm_next;   // next tile: FFT reading the row
             // y, x_out and the input history: before a tile that reads its
-            // input block from the row, after one that has it staged in LDS
+            // input block from the row, after one that has it staged in LDS;
+            // before the matrix-core tile the chain wavefront leaves y in LDS
+            // (x is the tile's input there) and the other wavefronts, idle
+            // during that tile, store the block
             auto store_block = [&]() {
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) {
@@ -1283,7 +1287,10 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     const int64_t tl = t0 + kWave * k + lane;
                     if (direct) xring[tl & xmask] = xk[k];
                     if (stage_x) xst[Un - kBlk + kWave * k + lane] = xk[k];   // completes the staged input block
-                    if (mm_next) mxz[15 + kWave * k + lane] = xk[k];
+                    if (mm_next) {
+                        mxz[15 + kWave * k + lane] = xk[k];
+                        myb[kWave * k + lane] = p[k];
+                    }
                     accw[(kWave * k + lane) & wmask] = nx[k];  // slot of position t now holds position t + W
                 }
                 if (row_input) store_block();
@@ -1297,6 +1304,18 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 if (U <= d.T) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
                 } else if (U == kBlk) {
+                    if (!chain_wave) {
+                        static_assert(kTeamWaves == 2, "one wavefront stores the block");
+#pragma unroll
+                        for (int k = 0; k < kRegs; ++k) {
+                            const int64_t tl = t0 + kWave * k + lane;   // < i < L
+                            const int64_t o = (b * L + tl) * D + c;
+                            const float xv = mxz[15 + kWave * k + lane];
+                            yout[o] = myb[kWave * k + lane];
+                            if (a.x_out) store_io<BF16>(a.x_out, o, xv);
+                            row[tl] = xv;
+                        }
+                    }
                     mm_tile256(mxz, mhs, accw);
                 } else {
                     const int q = ilog2(U);
@@ -1320,7 +1339,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 team_sync();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
             }
-            if (chain_wave && !row_input) store_block();
+            if (chain_wave && !row_input && !mm_next) store_block();
         }
     }
 }
