@@ -949,6 +949,52 @@ __device__ __forceinline__ void static_for(F&& f) {
 // MFMA lane layout (16x16x4): A[i][k] in lane i + 16k, B[k][j] in lane
 // j + 16k, D[i][j] in lane j + 16 (i / 4), register i % 4.
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// The accumulation shared by the matrix-core products of one block: init
+// plus the 16 NC steps (d = n / NC, c = n % NC) of A_d B_d in the decimated
+// order above, where step (d, c), lane (alpha, kk) of A reads the skewed
+// filter copy at G + G / 16 + 17 (alpha - kk) with G = GBASE + d - 64 c, and B
+// reads the padded input at a + 16 kk + 64 c - d + 15.  Run by the calling
+// wavefront; D[alpha][a] in lane a + 16 (alpha / 4), register alpha % 4.
+// The operands of a group of kG steps are loaded while the group before it
+// is multiplied; four accumulators keep four products in flight.
+template <int NC, int GBASE>
+__device__ __forceinline__ v4f mm_toeplitz(const FI_SHARED float* ab, const FI_SHARED float* bb, v4f init) {
+    constexpr int kSteps = 16 * NC, kG = 8, kGroups = kSteps / kG;
+    static_assert(kSteps % kG == 0, "whole groups");
+    v4f acc[4];
+    acc[0] = init;
+#pragma unroll
+    for (int u = 1; u < 4; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    float av[2][kG], bv[2][kG];
+    auto load = [&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        static_for<0, kG>([&](auto uc) {
+            constexpr int n = g * kG + decltype(uc)::value;
+            constexpr int d = n / NC, c = n % NC;
+            constexpr int G = GBASE + d - 64 * c;
+            static_assert(G >= 64, "slots of the filter copy stay in range");
+            av[g & 1][n % kG] = ab[G + G / 16];
+            bv[g & 1][n % kG] = bb[64 * c - d + 15];
+        });
+    };
+    load(std::integral_constant<int, 0>{});
+    static_for<0, kGroups>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        // the scheduler keeps the next group's loads ahead of this group's
+        // products
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (g + 1 < kGroups) load(std::integral_constant<int, g + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, kG>([&](auto uc) {
+            constexpr int u = decltype(uc)::value, n = g * kG + u;
+            acc[n & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[g & 1][u], bv[g & 1][u], acc[n & 3], 0, 0, 0);
+        });
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 __device__ __forceinline__ void mm_tile256(const FI_SHARED float* xz, const FI_SHARED float* hsk,
                                            FI_SHARED float* ring) {
     static_assert(kBlk == 256, "the matrix-core tile covers one 256-position block");
@@ -957,50 +1003,29 @@ __device__ __forceinline__ void mm_tile256(const FI_SHARED float* xz, const FI_S
     const int al = l & 15, kk = l >> 4;
     // A of step (d, c), lane (alpha, kk): lag g = 256 + d - 64 c + 16 j with
     // j = alpha - kk; with G = g - 16 j + 64 = 320 + d - 64 c (>= 64), s(g) =
-    // G + G / 16 + 17 j (16 j / 16 = j exactly)
-    const FI_SHARED float* ab = hsk + 17 * (al - kk);
-    // B of step (d, c), lane (a, kk): x[a - d + 16 (4c + kk)] = xz[a + 16 kk + 64 c - d + 15]
-    const FI_SHARED float* bb = xz + al + 16 * kk;
+    // G + G / 16 + 17 j (16 j / 16 = j exactly).  B of step (d, c), lane
+    // (a, kk): x[a - d + 16 (4c + kk)] = xz[a + 16 kk + 64 c - d + 15].
     // The team's first wavefront alone: the others share their SIMDs with
-    // other teams' chains, which matrix work beside them slows down.  The
-    // operands of a group of kG steps are loaded while the group before it
-    // is multiplied; four accumulators keep four products in flight.
-    constexpr int kSteps = 80, kG = 8, kGroups = kSteps / kG;
+    // other teams' chains, which matrix work beside them slows down.
     if (__builtin_amdgcn_readfirstlane(tid) < kWave) {
-        v4f acc[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
-        float av[2][kG], bv[2][kG];
-        auto load = [&](auto gc) {
-            constexpr int g = decltype(gc)::value;
-            static_for<0, kG>([&](auto uc) {
-                constexpr int n = g * kG + decltype(uc)::value;
-                constexpr int d = n / 5, c = n % 5;
-                constexpr int G = 320 + d - 64 * c;
-                av[g & 1][n % kG] = ab[G + G / 16];
-                bv[g & 1][n % kG] = bb[64 * c - d + 15];
-            });
-        };
-        load(std::integral_constant<int, 0>{});
-        static_for<0, kGroups>([&](auto gc) {
-            constexpr int g = decltype(gc)::value;
-            // the scheduler keeps the next group's loads ahead of this
-            // group's products
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (g + 1 < kGroups) load(std::integral_constant<int, g + 1>{});
-            __builtin_amdgcn_sched_barrier(0);
-            static_for<0, kG>([&](auto uc) {
-                constexpr int u = decltype(uc)::value, n = g * kG + u;
-                acc[n & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[g & 1][u], bv[g & 1][u], acc[n & 3], 0, 0, 0);
-            });
-        });
-        __builtin_amdgcn_sched_barrier(0);
-        // D[alpha][a] in lane a + 16 (alpha / 4), register alpha % 4:
+        const v4f y = mm_toeplitz<5, 320>(hsk + 17 * (al - kk), xz + al + 16 * kk, v4f{0.f, 0.f, 0.f, 0.f});
         // position q = a + 16 alpha of the next block
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            ring[al + 16 * (4 * kk + r)] += (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+        for (int r = 0; r < 4; ++r) ring[al + 16 * (4 * kk + r)] += y[r];
     }
+}
+
+// Open loop: a block's own lower triangle (lags 0 .. 255; the inputs are all
+// known, so nothing is serial) as one matrix-core product in the same
+// decimated order, lag d + 16 (alpha - bt): with the filter copy hz holding
+// h[g] for g in [-256, 256) at slot s(g) = (g + 256) + (g + 256) / 16 (zero
+// at negative lags), G = 256 + d - 64 c.  bt = 4c + kk <= 15 suffices (larger
+// bt only meets negative lags): 64 steps.  Returns init + the triangle, by
+// the calling wavefront, in MFMA layout.
+__device__ __forceinline__ v4f mm_triangle256(const FI_SHARED float* xz, const FI_SHARED float* hz, v4f init) {
+    const int l = team_tid() & (kWave - 1);
+    const int al = l & 15, kk = l >> 4;
+    return mm_toeplitz<4, 256>(hz + 17 * (al - kk), xz + al + 16 * kk, init);
 }
 
 constexpr int kTapBatch = 4;         // chain: taps loaded per batch, one batch ahead
@@ -1067,13 +1092,27 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     const int t4_off = d.fftreg - kTapTableBytes;
     FI_SHARED V4* tz = reinterpret_cast<FI_SHARED V4*>(smem_ptr(smem) + t4_off);
     const float tap_scale = CLOSED ? kTanhScale : 1.0f;
+    // Open loop has no chain: the same region holds the filter copy of the
+    // block triangle on the matrix cores, hz[s(g)] = h[g] for g in [-256,
+    // 256), s(g) = (g + 256) + (g + 256) / 16, zero at negative lags and from
+    // L on.
+    FI_SHARED float* hz = reinterpret_cast<FI_SHARED float*>(tz);
+    static_assert((2 * kBlk + 2 * kBlk / 16) * 4 <= kTapTableBytes, "the triangle's filter copy fits");
     auto build_taps4 = [&](const FI_GLOBAL float* hrow) {
-        for (int e = tid; e < kTapTableBytes / 16; e += kTeam) {
-            const int q = e - 3 - kWave;   // lag of the first component
-            float v[4];
+        if constexpr (CLOSED) {
+            for (int e = tid; e < kTapTableBytes / 16; e += kTeam) {
+                const int q = e - 3 - kWave;   // lag of the first component
+                float v[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = (q - j >= 0 && q - j < kBlk && q - j < L) ? tap_scale * hrow[q - j] : 0.f;
-            tz[e] = V4{v[0], v[1], v[2], v[3]};
+                for (int j = 0; j < 4; ++j)
+                    v[j] = (q - j >= 0 && q - j < kBlk && q - j < L) ? tap_scale * hrow[q - j] : 0.f;
+                tz[e] = V4{v[0], v[1], v[2], v[3]};
+            }
+        } else {
+            for (int e = tid; e < 2 * kBlk; e += kTeam) {
+                const int g = e - kBlk;
+                hz[e + e / 16] = (g >= 0 && g < L) ? hrow[g] : 0.f;
+            }
         }
     };
     // the matrix-core tile's zero-padded input block and its filter h[-64,
@@ -1196,64 +1235,85 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     const int64_t pn = base + kWave * k + lane;
                     nx[k] = (nx_in_row && pn < L) ? row[pn] : 0.f;
                 }
-                // tz0[64k - n]: the taps of position 64k + lane for inputs
-                // n .. n+3 (n a multiple of kTapBatch), in two batches
-                static_assert(kTapBatch == 4, "a tap batch is one 16-byte entry");
-                const FI_SHARED V4* tz0 = tz + 3 + kWave + lane;
-                V4 ta[kRegs][2];
-#pragma unroll
-                for (int k = 0; k < kRegs; ++k) ta[k][0] = tz0[kWave * k];
-                float v = 0.f;
                 float xstart = 0.f;
-                if constexpr (CLOSED) {
+                if constexpr (!CLOSED) {
+                    // open loop: every input of the block is known, so its own
+                    // triangle is one matrix-core product (mm_triangle256) on
+                    // top of the ring's accumulators; the inputs go to the
+                    // padded block the product (and the tile of side kBlk at
+                    // the block's end) reads, and y comes back to the lane
+                    // layout through the LDS y buffer
+                    static_assert(kRegs * kWave == kBlk && kBlk == 256, "matrix-core triangle layout");
+                    const int al = lane & 15, kk = lane >> 4;
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) mxz[15 + kWave * k + lane] = xb[k];
+                    v4f init;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) init[r] = accw[al + 16 * (4 * kk + r)];
+                    wave_sync();
+                    const v4f yq = mm_triangle256(mxz, hz, init);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) myb[al + 16 * (4 * kk + r)] = yq[r];
+                    wave_sync();
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) p[k] = myb[kWave * k + lane];
+                } else {
+                    // tz0[64k - n]: the taps of position 64k + lane for inputs
+                    // n .. n+3 (n a multiple of kTapBatch), in two batches
+                    static_assert(kTapBatch == 4, "a tap batch is one 16-byte entry");
+                    const FI_SHARED V4* tz0 = tz + 3 + kWave + lane;
+                    V4 ta[kRegs][2];
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) ta[k][0] = tz0[kWave * k];
+                    float v = 0.f;
 #pragma unroll
                     for (int k = 0; k < kRegs; ++k) p[k] *= kTanhScale;
                     v = readlane(p[0], 0);
                     xstart = xcur;
-                }
-                // one 64-step segment of the chain (steps 64K .. 64K+63)
-                auto segment = [&](auto kc) {
-                    constexpr int K = decltype(kc)::value;
+                    // one 64-step segment of the chain (steps 64K .. 64K+63)
+                    auto segment = [&](auto kc) {
+                        constexpr int K = decltype(kc)::value;
 #pragma unroll
-                    for (int m2 = 0; m2 < kWave; ++m2) {
-                        const int m = kWave * K + m2;
-                        float tv[kRegs];
+                        for (int m2 = 0; m2 < kWave; ++m2) {
+                            const int m = kWave * K + m2;
+                            float tv[kRegs];
 #pragma unroll
-                        for (int k = 0; k < kRegs; ++k) {
-                            const V4 t4 = ta[k][(m / kTapBatch) % 2];
-                            tv[k] = m % 4 == 0 ? t4.x : m % 4 == 1 ? t4.y : m % 4 == 2 ? t4.z : t4.w;
-                        }
-                        // closed loop: the accumulators run in units of c = 2 log2(e)
-                        // (the taps are c h), so tanh(y) = 1 - 2 r with
-                        // r = 1 / (1 + 2^(c y)); v holds position t0+m's accumulator
-                        // with every input but its own pushed (read one step ahead,
-                        // off the serial path), and the serial path of a position is
-                        // c y = v + c h[0] x, exp2, add, rcp, x = 1 - 2 r.  Position
-                        // m's own lag-0 push is the same fma as c y, so its register
-                        // ends equal to it.
-                        const float xm = CLOSED ? xcur : readlane(xb[K], m2);
-                        const float cy = __builtin_fmaf(ch0v, xm, v);
+                            for (int k = 0; k < kRegs; ++k) {
+                                const V4 t4 = ta[k][(m / kTapBatch) % 2];
+                                tv[k] = m % 4 == 0 ? t4.x : m % 4 == 1 ? t4.y : m % 4 == 2 ? t4.z : t4.w;
+                            }
+                            // closed loop: the accumulators run in units of c = 2 log2(e)
+                            // (the taps are c h), so tanh(y) = 1 - 2 r with
+                            // r = 1 / (1 + 2^(c y)); v holds position t0+m's accumulator
+                            // with every input but its own pushed (read one step ahead,
+                            // off the serial path), and the serial path of a position is
+                            // c y = v + c h[0] x, exp2, add, rcp, x = 1 - 2 r.  Position
+                            // m's own lag-0 push is the same fma as c y, so its register
+                            // ends equal to it.
+                            const float xm = CLOSED ? xcur : readlane(xb[K], m2);
+                            const float cy = __builtin_fmaf(ch0v, xm, v);
 #pragma unroll
-                        for (int k = K; k < kRegs; ++k) {
-                            p[k] = __builtin_fmaf(tv[k], xm, p[k]);
-                            pin(p[k]);   // push now: x[t] is then dead after this step
-                        }
-                        if (m % kTapBatch == 0 && m + kTapBatch < kBlk) {
+                            for (int k = K; k < kRegs; ++k) {
+                                p[k] = __builtin_fmaf(tv[k], xm, p[k]);
+                                pin(p[k]);   // push now: x[t] is then dead after this step
+                            }
+                            if (m % kTapBatch == 0 && m + kTapBatch < kBlk) {
+                                __builtin_amdgcn_sched_barrier(0);
+                                const int n = m + kTapBatch;
+#pragma unroll
+                                for (int k = 0; k < kRegs; ++k)
+                                    if (n < kWave * (k + 1)) ta[k][(n / kTapBatch) % 2] = tz0[kWave * k - n];
+                            }
+                            if constexpr (CLOSED) {
+                                if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
+                                xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
+                                if constexpr (BF16) xcur = round_bf16(xcur);
+                            }
                             __builtin_amdgcn_sched_barrier(0);
-                            const int n = m + kTapBatch;
-#pragma unroll
-                            for (int k = 0; k < kRegs; ++k)
-                                if (n < kWave * (k + 1)) ta[k][(n / kTapBatch) % 2] = tz0[kWave * k - n];
                         }
-                        if constexpr (CLOSED) {
-                            if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
-                            xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
-                            if constexpr (BF16) xcur = round_bf16(xcur);
-                        }
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                };
-                for_segments<0>(segment);
+                    };
+                    for_segments<0>(segment);
+                }
                 if constexpr (CLOSED) {
                     // The inputs of the block, one per lane: the register of
                     // position t ended as the same fma as the chain's c y[t], so
