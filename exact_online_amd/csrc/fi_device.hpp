@@ -470,10 +470,12 @@ __device__ __forceinline__ void dit_pass(FI_GLOBAL Cx<T>* sc, int M, int S, TwPt
 // global memory, the in-place Cooley-Tukey stage of ct_stage with run-time
 // sizes: forward (decimation in frequency) stores radix outputs in
 // bit-reversed slot order, the inverse (decimation in time) reads them so;
-// twiddles from the global table.  Two butterflies per thread are in flight.
+// twiddles from the global table.  G butterflies per thread are in flight;
+// M / R is a multiple of kTeam * G, so no load carries a condition (a load
+// under a branch waits for every load issued before it).
 template <int R, bool INV, typename T>
 __device__ __forceinline__ void global_stage(FI_GLOBAL Cx<T>* sc, int M, int S, TwPtr<T> tw) {
-    constexpr int G = 2;
+    constexpr int G = 16 / R;
     const int lane = team_tid();
     const int Q = S / R, NB = M / R;
     const GlobalTw<T> gt{tw};
@@ -486,24 +488,20 @@ __device__ __forceinline__ void global_stage(FI_GLOBAL Cx<T>* sc, int M, int S, 
             const int n = n0 + lane + kTeam * g;
             jj[g] = n % Q;
             off[g] = (n / Q) * S + jj[g];
-            if (n < NB) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) v[g][r] = sc[off[g] + (INV ? rev_r<R>(r) : r) * Q];
-            }
+            for (int r = 0; r < R; ++r) v[g][r] = sc[off[g] + (INV ? rev_r<R>(r) : r) * Q];
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            if (n0 + lane + kTeam * g < NB) {
-                if constexpr (INV) {
-                    twiddle_apply<R, true>(v[g], gt, S, jj[g]);
-                    dft<R, true>(v[g]);
-                } else {
-                    dft<R, false>(v[g]);
-                    twiddle_apply<R, false>(v[g], gt, S, jj[g]);
-                }
-#pragma unroll
-                for (int r = 0; r < R; ++r) sc[off[g] + (INV ? r : rev_r<R>(r)) * Q] = v[g][r];
+            if constexpr (INV) {
+                twiddle_apply<R, true>(v[g], gt, S, jj[g]);
+                dft<R, true>(v[g]);
+            } else {
+                dft<R, false>(v[g]);
+                twiddle_apply<R, false>(v[g], gt, S, jj[g]);
             }
+#pragma unroll
+            for (int r = 0; r < R; ++r) sc[off[g] + (INV ? r : rev_r<R>(r)) * Q] = v[g][r];
         }
     }
     team_sync_global();
@@ -534,7 +532,9 @@ __device__ __forceinline__ void global_dit(FI_GLOBAL Cx<T>* sc, int M, int S0, i
     while (S < S0) { S *= 8; global_stage<8, true>(sc, M, S, tw); }
 }
 
-// Copies n elements between global and LDS (padded) buffers in batches.
+// Copies n elements (a multiple of kTeam * kBatch) between global and LDS
+// (padded) buffers in batches.  The loads carry no per-element condition: a
+// load under a branch waits for every load issued before it.
 template <typename T>
 __device__ __forceinline__ void copy_to_lds(FI_SHARED Cx<T>* lds, const FI_GLOBAL Cx<T>* g, int n) {
     const int lane = team_tid();
@@ -542,15 +542,9 @@ __device__ __forceinline__ void copy_to_lds(FI_SHARED Cx<T>* lds, const FI_GLOBA
     for (int q0 = 0; q0 < n; q0 += kTeam * kBatch) {
         Cx<T> v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int q = q0 + lane + kTeam * u;
-            if (q < n) v[u] = g[q];
-        }
+        for (int u = 0; u < kBatch; ++u) v[u] = g[q0 + lane + kTeam * u];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int q = q0 + lane + kTeam * u;
-            if (q < n) lds[lp(q)] = v[u];
-        }
+        for (int u = 0; u < kBatch; ++u) lds[lp(q0 + lane + kTeam * u)] = v[u];
     }
     team_sync();
 }

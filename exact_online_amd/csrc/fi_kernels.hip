@@ -626,6 +626,148 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
     tile_output(out, i, M / 2, [lds](int m) { return lds[lp(M / 2 + m)]; });
 }
 
+// The forward transform's first two stages of a tile of more than kLdsFftMax
+// points (radix R1 at span M, then radix R2 at span M / R1; R2 = 1: none),
+// fused with the load of its input: inputs r >= R1/2 of every first-stage
+// butterfly are the zero padding (z[n] = 0 for n >= M/2).  Thread item j2 <
+// Q2 = M / (R1 R2) runs the first-stage butterflies j2 + r2 Q2 (r2 < R2),
+// which hold every input of the second-stage butterflies (b, j2), b < R1.
+// Outputs go to the stages' bit-reversed slot order (as global_stage).
+template <int R1, int R2>
+__device__ __forceinline__ void first_pass_load(FI_GLOBAL Cx<float>* sc, const FI_GLOBAL V2* xs, int M,
+                                                TwPtr<float> tw) {
+    constexpr int G = R1 * R2 >= 16 ? 1 : 16 / (R1 * R2);
+    const int lane = team_tid();
+    const int Q1 = M / R1, Q2 = Q1 / R2;   // Q2 a multiple of kTeam * G
+    const GlobalTw<float> gt{tw};
+#pragma unroll 1
+    for (int n0 = 0; n0 < Q2; n0 += kTeam * G) {
+        Cx<float> v[G][R2][R1];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int j2 = n0 + lane + kTeam * g;
+#pragma unroll
+            for (int r2 = 0; r2 < R2; ++r2) {
+#pragma unroll
+                for (int r = 0; r < R1; ++r) {
+                    if (r < R1 / 2) {
+                        const V2 x = xs[j2 + r2 * Q2 + r * Q1];
+                        v[g][r2][r] = Cx<float>{x.x, x.y};
+                    } else {
+                        v[g][r2][r] = Cx<float>{0.f, 0.f};
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int j2 = n0 + lane + kTeam * g;
+#pragma unroll
+            for (int r2 = 0; r2 < R2; ++r2) {
+                dft<R1, false>(v[g][r2]);
+                twiddle_apply<R1, false>(v[g][r2], gt, M, j2 + r2 * Q2);
+            }
+#pragma unroll
+            for (int p = 0; p < R1; ++p) {   // first-stage output p: sub-problem rev(p)
+                const int b = rev_r<R1>(p);
+                if constexpr (R2 == 1) {
+                    sc[b * Q1 + j2] = v[g][0][p];
+                } else {
+                    Cx<float> t[R2];
+#pragma unroll
+                    for (int r2 = 0; r2 < R2; ++r2) t[r2] = v[g][r2][p];
+                    dft<R2, false>(t);
+                    twiddle_apply<R2, false>(t, gt, Q1, j2);
+#pragma unroll
+                    for (int r2 = 0; r2 < R2; ++r2) sc[b * Q1 + j2 + rev_r<R2>(r2) * Q2] = t[r2];
+                }
+            }
+        }
+    }
+    team_sync_global();
+}
+
+// The inverse transform's last two stages of such a tile (radix R2 at span
+// M / R1, then radix R1 at span M), fused with the output.  First-stage
+// butterfly j keeps its outputs r >= R1/2 only: complex points j + r Q1 =
+// M/2 + m with m = j + (r - R1/2) Q1, the tile's outputs i + 2m and i + 2m + 1
+// (the ring for m < (wend - i) / 2, else the row: stored when the sink is its
+// level's first, else added).  Every load of a group is issued before any is
+// used (the row values from clamped indices).
+template <int R1, int R2>
+__device__ __forceinline__ void last_pass_output(const TileSink& s, int64_t i, const FI_GLOBAL Cx<float>* sc,
+                                                 int M, TwPtr<float> tw) {
+    constexpr int G = R1 * R2 >= 16 ? 1 : 16 / (R1 * R2);
+    constexpr int H = R1 / 2;
+    const int lane = team_tid();
+    const int Q1 = M / R1, Q2 = Q1 / R2;   // Q2 a multiple of kTeam * G
+    const int nl = s.wend > i ? (int)((s.wend - i) / 2) : 0;
+    const GlobalTw<float> gt{tw};
+#pragma unroll 1
+    for (int n0 = 0; n0 < Q2; n0 += kTeam * G) {
+        Cx<float> a[G][R1][R2];
+        V2 old[G][R2][H];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int j2 = n0 + lane + kTeam * g;
+#pragma unroll
+            for (int b = 0; b < R1; ++b) {
+#pragma unroll
+                for (int r2 = 0; r2 < R2; ++r2) a[g][b][r2] = sc[b * Q1 + j2 + rev_r<R2>(r2) * Q2];
+            }
+            if (!s.first) {
+#pragma unroll
+                for (int r2 = 0; r2 < R2; ++r2) {
+#pragma unroll
+                    for (int r = 0; r < H; ++r) {
+                        const int m = j2 + r2 * Q2 + r * Q1;
+                        const int64_t o = i + 2 * (int64_t)m;
+                        old[g][r2][r] =
+                            *reinterpret_cast<const FI_GLOBAL V2*>(s.row + (m >= nl && o + 1 < s.L ? o : 0));
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int j2 = n0 + lane + kTeam * g;
+            Cx<float> v[R2][R1];
+#pragma unroll
+            for (int b = 0; b < R1; ++b) {   // sub-problem b feeds first-stage input rev(b)
+                if constexpr (R2 > 1) {
+                    twiddle_apply<R2, true>(a[g][b], gt, Q1, j2);
+                    dft<R2, true>(a[g][b]);
+                }
+#pragma unroll
+                for (int r2 = 0; r2 < R2; ++r2) v[r2][rev_r<R1>(b)] = a[g][b][r2];
+            }
+#pragma unroll
+            for (int r2 = 0; r2 < R2; ++r2) {
+                const int j = j2 + r2 * Q2;
+                twiddle_apply<R1, true>(v[r2], gt, M, j);
+                dft<R1, true>(v[r2]);
+#pragma unroll
+                for (int r = 0; r < H; ++r) {
+                    const int m = j + r * Q1;
+                    const int64_t o = i + 2 * (int64_t)m;
+                    const Cx<float> w = v[r2][H + r];
+                    if (m < nl) {
+                        if (o < s.L) {
+                            s.accw[o & s.wmask] += w.x;
+                            if (o + 1 < s.L) s.accw[(o + 1) & s.wmask] += w.y;
+                        }
+                    } else if (o + 1 < s.L) {
+                        *reinterpret_cast<FI_GLOBAL V2*>(s.row + o) =
+                            s.first ? V2{w.x, w.y} : V2{old[g][r2][r].x + w.x, old[g][r2][r].y + w.y};
+                    } else if (o < s.L) {
+                        s.row[o] = s.first ? w.x : s.row[o] + w.x;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Tiles of more than kLdsFftMax points (the tile of fft_tile below).  The
 // caller synchronises the team afterwards.
 __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL float* xblock, const FI_GLOBAL V2* spec,
@@ -670,9 +812,10 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
         });
         return;
     }
-    // M > 8192: one radix-2 decimation-in-frequency pass fused with the load,
-    // then radix-8 (4, 2) passes over the scratch slot until F = 4096-point
-    // blocks remain; after the blocks' own transforms,
+    // M > 8192: the first decimation-in-frequency stages (radix R1 =
+    // min(M / F, 8), then R2) fused with the load, then radix-8 passes over
+    // the scratch slot until F = 4096-point blocks remain; after the blocks'
+    // own transforms,
     // position p (block p / F) holds frequency brev(p) over log2(M) bits.
     // Block 0 holds octaves 0 .. log2(F)-1 and block 1 octave log2(F): both
     // hold their own partner frequencies and are transformed, multiplied and
@@ -682,24 +825,16 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
     const FI_GLOBAL V2* xs = reinterpret_cast<const FI_GLOBAL V2*>(xblock);
     constexpr int F = kLdsFftMax;
     const int P = M / F;
-    const int half = M >> 1;
-    // first pass fused with the load (upper half is 0), kBatch loads in
-    // flight per thread (half is a multiple of kTeam * kBatch)
-#pragma unroll 1
-    for (int j0 = 0; j0 < half; j0 += kTeam * kBatch) {
-        V2 v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) v[u] = xs[j0 + lane + kTeam * u];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int j = j0 + lane + kTeam * u;
-            const Cx<float> z = {v[u].x, v[u].y};
-            sc[j] = z;
-            sc[j + half] = cmul(z, twiddle<false>(tw, M, j));
-        }
-    }
-    team_sync_global();
-    global_dif(sc, M, half, F, tw);   // radix-8 stages down to F-point blocks
+    // R2 = 2 where M / (R1 F) is twice a power of 8, else 1 (a factor of 4
+    // left over goes to a global stage: 32 values per thread would spill)
+    const int R1 = P < 8 ? P : 8;
+    int R2 = P / R1;
+    while (R2 >= 8) R2 /= 8;
+    if (R2 != 2) R2 = 1;
+    if (R1 == 4) first_pass_load<4, 1>(sc, xs, M, tw);
+    else if (R2 == 1) first_pass_load<8, 1>(sc, xs, M, tw);
+    else first_pass_load<8, 2>(sc, xs, M, tw);
+    global_dif(sc, M, M / (R1 * R2), F, tw);   // radix-8 (4) stages down to F-point blocks
     for (int p = 0; p < P; ++p) {
         FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
         copy_to_lds(lbuf, blk, F);
@@ -763,14 +898,12 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
             copy_from_lds(blk, lbuf, F);
         }
     }
-    global_dit(sc, M, half, F, tw);
-    // last inverse pass (size M) fused with the output; only the upper half
+    global_dit(sc, M, M / (R1 * R2), F, tw);
+    // the last two inverse stages fused with the output; only the upper half
     // (outputs U..2U-1 of the circular convolution) is needed
-    tile_output(out, i, half, [sc, tw, half](int j) {
-        const Cx<float> v0 = sc[j];
-        const Cx<float> v1 = cmul(sc[j + half], twiddle<true>(tw, 2 * half, j));
-        return csub(v0, v1);
-    });
+    if (R1 == 4) last_pass_output<4, 1>(out, i, sc, M, tw);
+    else if (R2 == 1) last_pass_output<8, 1>(out, i, sc, M, tw);
+    else last_pass_output<8, 2>(out, i, sc, M, tw);
 }
 
 // The tile tau(x, [i-U, i), h, [i, i+U)) as the circular convolution of
