@@ -5,7 +5,7 @@ One step = one full pass of the hot path over one batch: fi_run_closed_loop
 on the Hyena-like mixer workload (B=1, D=1024, L=16384, fp32, closed-loop tanh
 feedback, decaying-Gaussian filters with log-uniform tau in [64, 8192]) with
 the inputs already resident in HBM.  Protocol of the pages: warm-ups, then
-the mean over timed runs.  Prints ONE JSON line.
+the mean over timed runs (here 20 and 20 by default).  Prints ONE JSON line.
 
 Also reported:
   roofline      the persistent kernel (k_run, the only kernel of a step):
@@ -160,8 +160,11 @@ def cpu_baseline(w, h, x0, nch: int):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4)
-    ap.add_argument("--warmup", type=int, default=2)
+    # the card's clock settles over the first ten or so passes of a fresh
+    # process (a pass at D=1024, L=16K falls from 0.80 to 0.73 ms), so the
+    # default warm-up is longer than the pages' two runs
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="hyena-d1024-l16k")
     ap.add_argument("--small-tile-max", type=int, default=0)
     ap.add_argument("--cpu-channels", type=int, default=1024)

@@ -532,19 +532,21 @@ __device__ __forceinline__ void global_dit(FI_GLOBAL Cx<T>* sc, int M, int S0, i
     while (S < S0) { S *= 8; global_stage<8, true>(sc, M, S, tw); }
 }
 
-// Copies n elements (a multiple of kTeam * kBatch) between global and LDS
-// (padded) buffers in batches.  The loads carry no per-element condition: a
-// load under a branch waits for every load issued before it.
+// Copies n elements (a multiple of kTeam * 2 kBatch) between global and LDS
+// (padded) buffers in batches of 2 kBatch per thread.  The loads carry no
+// per-element condition: a load under a branch waits for every load issued
+// before it.
 template <typename T>
 __device__ __forceinline__ void copy_to_lds(FI_SHARED Cx<T>* lds, const FI_GLOBAL Cx<T>* g, int n) {
+    constexpr int B = 2 * kBatch;
     const int lane = team_tid();
 #pragma unroll 1
-    for (int q0 = 0; q0 < n; q0 += kTeam * kBatch) {
-        Cx<T> v[kBatch];
+    for (int q0 = 0; q0 < n; q0 += kTeam * B) {
+        Cx<T> v[B];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) v[u] = g[q0 + lane + kTeam * u];
+        for (int u = 0; u < B; ++u) v[u] = g[q0 + lane + kTeam * u];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) lds[lp(q0 + lane + kTeam * u)] = v[u];
+        for (int u = 0; u < B; ++u) lds[lp(q0 + lane + kTeam * u)] = v[u];
     }
     team_sync();
 }

@@ -859,29 +859,24 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
             const int pp = 3 * (1 << a) - 1 - p;
             if (pp < p) continue;
             const int lm = ilog2(M);
+            // every load of a batch (spectrum, scratch, twiddle) is issued
+            // before any is used
 #pragma unroll 1
             for (int k0 = 0; k0 < F; k0 += kTeam * kBatch) {
                 V2 sa[kBatch], sb[kBatch];
+                Cx<float> za[kBatch], zb[kBatch], wf[kBatch];
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u) {
                     const int k = k0 + lane + kTeam * u;
                     sa[u] = spec[(int64_t)p * F + k];
                     sb[u] = spec[(int64_t)pp * F + (F - 1 - k)];
-                }
-                Cx<float> za[kBatch], zb[kBatch];
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int k = k0 + lane + kTeam * u;
                     za[u] = sc[p * F + k];
                     zb[u] = sc[pp * F + (F - 1 - k)];
+                    wf[u] = tw[2 * M + brev_bits(p * F + k, lm)];   // frequency never 0 in blocks >= 2
                 }
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int k = k0 + lane + kTeam * u;
-                    const int fa = brev_bits(p * F + k, lm);   // never 0 in blocks >= 2
-                    untangle_pair(za[u], zb[u], Cx<float>{sa[u].x, sa[u].y}, Cx<float>{sb[u].x, sb[u].y},
-                                  twiddle<false>(tw, 2 * M, fa));
-                }
+                for (int u = 0; u < kBatch; ++u)
+                    untangle_pair(za[u], zb[u], Cx<float>{sa[u].x, sa[u].y}, Cx<float>{sb[u].x, sb[u].y}, wf[u]);
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u) {
                     const int k = k0 + lane + kTeam * u;
