@@ -41,6 +41,8 @@ def _bind(lib):
     lib.fio_open.restype = None
     lib.fio_closed.argtypes = [i64, i64, i64, dp, dp, dp, ip, ip]
     lib.fio_closed.restype = None
+    lib.fio_prompted.argtypes = [i64, i64, i64, i64, dp, dp, dp, ip, ip]
+    lib.fio_prompted.restype = None
     lib.fio_points.argtypes = [i64, dp, dp, i64, ctypes.POINTER(ctypes.c_int64), dp]
     lib.fio_points.restype = None
     lib.fio_round_bf16.argtypes = [ctypes.c_double]
@@ -115,6 +117,27 @@ class Oracle:
             return y[0], x[0]
         return y, x
 
+    def conv_prompted(self, h, prompt, L: int | None = None, bf16: bool = False):
+        """Prompt, then free-running: x[s] = prompt[s] for s < p, x_{t+1} =
+        tanh(y_t) from position p on.  h[L][D], prompt[B][p][D] -> (y[B][L][D],
+        x[B][L][D]) in fp64; ``bf16`` rounds the fed-back x."""
+        h = _f64(h)
+        L = h.shape[0] if L is None else int(L)
+        h = np.ascontiguousarray(h[:L])
+        prompt = _f64(prompt)
+        squeeze = prompt.ndim == 2
+        if squeeze:
+            prompt = prompt[None]
+        B, P, D = prompt.shape
+        assert h.shape == (L, D) and 1 <= P <= L
+        x = np.zeros((B, L, D), dtype=np.float64)
+        x[:, :P, :] = prompt
+        y = np.empty_like(x)
+        self.lib.fio_prompted(B, D, L, P, _p(h), _p(x), _p(y), int(bool(bf16)), self.threads)
+        if squeeze:
+            return y[0], x[0]
+        return y, x
+
     def conv_points(self, h_col, x_col, ts) -> np.ndarray:
         """One channel: y at positions ``ts`` from its filter and input series."""
         h_col = _f64(h_col)
@@ -151,6 +174,10 @@ def conv_open(h, x):
 
 def conv_closed(h, x0, L=None, bf16=False):
     return default().conv_closed(h, x0, L=L, bf16=bf16)
+
+
+def conv_prompted(h, prompt, L=None, bf16=False):
+    return default().conv_prompted(h, prompt, L=L, bf16=bf16)
 
 
 def conv_points(h_col, x_col, ts):

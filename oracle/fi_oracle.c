@@ -27,8 +27,13 @@
  * (Algoritmo 2)"); with bf16 storage the fed-back value is rounded to bf16,
  * nearest-even.
  *
+ * Prompted: the generation task of [FI] "Definizione del Compito" starts from
+ * a prompt x_1 .. x_p.  Here x[b][s][c] is given for s < p and fed back,
+ * x[b][t+1][c] = tanh(y[b][t][c]), from position p on.  p = 1 is the closed
+ * loop and p = L the open loop.
+ *
  * Mutation hooks: building with -DFIO_MUTANT=k plants one deliberate mistake
- * (k = 1..6, listed at each hook).  The test suite builds every mutant on the
+ * (k = 1..7, listed at each hook).  The test suite builds every mutant on the
  * CPU and checks that each one fails at least one pin; the normal build never
  * defines FIO_MUTANT.
  */
@@ -65,12 +70,12 @@ double fio_round_bf16(double v)
 #endif
 }
 
-/* One batch element, channels [c0, c0+cn), all positions.
- * closed == 0: x is read for every position.
- * closed != 0: x[0][.] is read, x[t+1][.] is written from tanh(y[t][.]). */
+/* One batch element, channels [c0, c0+cn), all positions.  x[s][.] is read
+ * for s < p; for t + 1 >= p, x[t+1][.] is written from tanh(y[t][.]) (p = L:
+ * open loop, p = 1: closed loop). */
 static void conv_block(int64_t D, int64_t L, int64_t c0, int64_t cn,
                        const double *h, double *x, double *y,
-                       int closed, int round_bf16)
+                       int64_t p, int round_bf16)
 {
     double acc[FIO_CBLK];
     for (int64_t t = 0; t < L; ++t) {
@@ -98,7 +103,11 @@ static void conv_block(int64_t D, int64_t L, int64_t c0, int64_t cn,
         }
         double *yr = y + t * D + c0;
         for (int64_t k = 0; k < cn; ++k) yr[k] = acc[k];
-        if (closed && t + 1 < L) {
+#if FIO_MUTANT == 7
+        if (t + 2 >= p && t + 1 < L) {  /* mutant 7: feedback starts one position early */
+#else
+        if (t + 1 >= p && t + 1 < L) {
+#endif
             double *xn = x + (t + 1) * D + c0;
             for (int64_t k = 0; k < cn; ++k) {
 #if FIO_MUTANT == 5
@@ -113,7 +122,7 @@ static void conv_block(int64_t D, int64_t L, int64_t c0, int64_t cn,
 }
 
 static void run(int64_t B, int64_t D, int64_t L, const double *h, double *x,
-                double *y, int closed, int round_bf16, int nthreads)
+                double *y, int64_t p, int round_bf16, int nthreads)
 {
     int64_t nblk = (D + FIO_CBLK - 1) / FIO_CBLK;
     int64_t jobs = B * nblk;
@@ -125,7 +134,7 @@ static void run(int64_t B, int64_t D, int64_t L, const double *h, double *x,
         int64_t b = j / nblk, c0 = (j % nblk) * FIO_CBLK;
         int64_t cn = D - c0 < FIO_CBLK ? D - c0 : FIO_CBLK;
         conv_block(D, L, c0, cn, h, x + b * L * D, y + b * L * D,
-                   closed, round_bf16);
+                   p, round_bf16);
     }
     (void)nthreads;
 }
@@ -134,7 +143,7 @@ static void run(int64_t B, int64_t D, int64_t L, const double *h, double *x,
 void fio_open(int64_t B, int64_t D, int64_t L, const double *h,
               const double *x, double *y, int nthreads)
 {
-    run(B, D, L, h, (double *)x, y, 0, 0, nthreads);
+    run(B, D, L, h, (double *)x, y, L, 0, nthreads);
 }
 
 /* Closed loop, free-running.  x_io[B][L][D]: on entry x_io[b][0][c] holds x0;
@@ -143,6 +152,15 @@ void fio_closed(int64_t B, int64_t D, int64_t L, const double *h, double *x_io,
                 double *y, int round_bf16, int nthreads)
 {
     run(B, D, L, h, x_io, y, 1, round_bf16, nthreads);
+}
+
+/* Prompted, free-running after the prompt.  x_io[B][L][D]: on entry
+ * x_io[b][s][c] holds the prompt for s < p (1 <= p <= L); on return every
+ * x_io[b][t][c] holds the input that produced y[b][t][c]. */
+void fio_prompted(int64_t B, int64_t D, int64_t L, int64_t p, const double *h,
+                  double *x_io, double *y, int round_bf16, int nthreads)
+{
+    run(B, D, L, h, x_io, y, p, round_bf16, nthreads);
 }
 
 /* One channel, selected positions: y_k = sum_{s=0}^{t_k} h[t_k - s] x[s],

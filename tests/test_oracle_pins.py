@@ -151,6 +151,72 @@ def test_closed_geometric_recurrence(orc, a):
         np.testing.assert_allclose(y[0, :, c], ref, rtol=1e-10, atol=1e-10)
 
 
+# ------------------------------------------------ closed forms, prompted runs
+# The generation task starts from a prompt x_0 .. x_{p-1}; the feedback
+# x_{t+1} = tanh(y_t) takes over from position p.
+@pytest.mark.parametrize("p", [1, 2, 7, 64])
+def test_prompted_delta0(orc, p):
+    L, D = 150, 2
+    h = np.zeros((L, D)); h[0] = 1.0
+    prompt = _rng(31).standard_normal((1, p, D))
+    y, x = orc.conv_prompted(h, prompt)
+    for c in range(D):
+        for t in range(p):
+            assert y[0, t, c] == prompt[0, t, c] and x[0, t, c] == prompt[0, t, c]
+        v = prompt[0, p - 1, c]
+        for t in range(p, L):
+            v = math.tanh(v)
+            assert y[0, t, c] == v
+
+
+@pytest.mark.parametrize("p,k", [(5, 1), (9, 3), (40, 17)])
+def test_prompted_delta_k(orc, p, k):
+    L, D = 130, 2
+    h = np.zeros((L, D)); h[k] = 1.0
+    prompt = _rng(32).standard_normal((1, p, D))
+    y, x = orc.conv_prompted(h, prompt)
+    for c in range(D):
+        xs = list(prompt[0, :, c]) + [0.0] * (L - p)
+        for t in range(p - 1, L - 1):
+            xs[t + 1] = math.tanh(xs[t - k]) if t >= k else 0.0
+        ys = [xs[t - k] if t >= k else 0.0 for t in range(L)]
+        np.testing.assert_array_equal(x[0, :, c], xs)
+        np.testing.assert_array_equal(y[0, :, c], ys)
+
+
+@pytest.mark.parametrize("p", [1, 3, 100])
+def test_prompted_geometric_recurrence(orc, p):
+    L, D, a = 700, 2, math.exp(-1 / 32.0)
+    h = np.repeat((a ** np.arange(L, dtype=np.float64))[:, None], D, axis=1)
+    prompt = _rng(33).standard_normal((1, p, D))
+    y, _ = orc.conv_prompted(h, prompt)
+    for c in range(D):
+        ref = np.empty(L)
+        for t in range(L):
+            xt = prompt[0, t, c] if t < p else math.tanh(ref[t - 1])
+            ref[t] = (a * ref[t - 1] if t else 0.0) + xt
+        np.testing.assert_allclose(y[0, :, c], ref, rtol=1e-10, atol=1e-10)
+
+
+def test_prompted_full_prompt_is_open_loop(orc):
+    L, D = 300, 3
+    r = _rng(34)
+    h = r.standard_normal((L, D)); x = r.standard_normal((2, L, D))
+    y, xo = orc.conv_prompted(h, x)
+    np.testing.assert_array_equal(xo, x)
+    np.testing.assert_allclose(y, _np_conv(h, x), rtol=1e-12, atol=1e-12)
+
+
+def test_prompted_prefix_is_causal(orc):
+    # the prompt's outputs are the open-loop convolution of the prompt alone
+    L, D, p = 400, 2, 123
+    r = _rng(35)
+    h = r.standard_normal((L, D)) * 0.05
+    prompt = r.standard_normal((1, p, D))
+    y, _ = orc.conv_prompted(h, prompt)
+    np.testing.assert_allclose(y[0, :p], _np_conv(h[:p], prompt[0]), rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------- exact arithmetic
 def test_integer_inputs_are_exact(orc):
     r = random.Random(11)
@@ -260,6 +326,14 @@ def _pin_battery(o) -> list:
         fails.append("closed_geometric")
     if o.round_bf16(1.0 + 3 * 2 ** -8) != 1.0 + 2 ** -6:
         fails.append("bf16_tie")
+    p = 5
+    y, _ = o.conv_prompted(hg, x[:, :p, :])
+    rec = np.empty((2, L, D))
+    for t in range(L):
+        xt = x[:, t] if t < p else np.tanh(rec[:, t - 1])
+        rec[:, t] = (a * rec[:, t - 1] if t else 0.0) + xt
+    if not np.allclose(y, rec, rtol=1e-10, atol=1e-10):
+        fails.append("prompted_geometric")
     return fails
 
 
@@ -267,7 +341,7 @@ def test_unmutated_oracle_passes_battery(orc):
     assert _pin_battery(orc) == []
 
 
-@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6, 7])
 def test_mutants_are_caught(tmp_path, mutant):
     path = oracle_mod.build(tmp_path / f"libfio_m{mutant}.so", mutant=mutant)
     o = oracle_mod.Oracle(oracle_mod.load(path), threads=2)
