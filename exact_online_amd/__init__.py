@@ -5,7 +5,7 @@ gfx950).  The functions keep the C names and only marshal arguments: device
 pointers may be given as integers or as torch CUDA tensors, streams as
 integers (hipStream_t) or torch streams.  Every step of the computation runs
 in the library's HIP kernels; if ``libfi.so`` is missing this module raises at
-import (build it with ``python -m exact_online_amd.build`` or
+import (build it with ``python exact_online_amd/build.py`` or
 ``__graft_entry__.build()``).
 """
 from __future__ import annotations
@@ -17,7 +17,8 @@ __all__ = [
     "FI_F32", "FI_BF16", "FI_FEEDBACK_NONE", "FI_FEEDBACK_TANH",
     "FI_OK", "FI_ERR_INVALID", "FI_ERR_NOMEM", "FI_ERR_HIP", "FI_ERR_STATE", "FI_ERR_UNSUPPORTED",
     "FiError", "fi_config", "fi_tile", "fi_create", "fi_step", "fi_run_closed_loop", "fi_reset",
-    "fi_destroy", "fi_position", "fi_strerror", "fi_tile_at", "Mixer", "EXPORTS", "lib", "LIB_PATH",
+    "fi_destroy", "fi_position", "fi_strerror", "fi_tile_at", "fi_run_prompted", "Mixer", "EXPORTS", "lib",
+    "LIB_PATH",
 ]
 
 FI_F32, FI_BF16 = 0, 1
@@ -28,13 +29,13 @@ FI_OK, FI_ERR_INVALID, FI_ERR_NOMEM, FI_ERR_HIP, FI_ERR_STATE, FI_ERR_UNSUPPORTE
 
 LIB_PATH = Path(__file__).resolve().parent / "libfi.so"
 if not LIB_PATH.exists():
-    raise ImportError(f"{LIB_PATH} is not built: run `python -m exact_online_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built: run `python exact_online_amd/build.py` "
                       "(hipcc, gfx950) before using exact_online_amd")
 
 lib = ctypes.CDLL(str(LIB_PATH))
 
 # every symbol include/fi.h declares
-EXPORTS = ("fi_create", "fi_step", "fi_run_closed_loop", "fi_reset", "fi_destroy",
+EXPORTS = ("fi_create", "fi_step", "fi_run_closed_loop", "fi_run_prompted", "fi_reset", "fi_destroy",
            "fi_position", "fi_strerror", "fi_tile_at")
 
 
@@ -56,6 +57,8 @@ lib.fi_step.argtypes = [_H, ctypes.c_void_p, ctypes.c_void_p]
 lib.fi_step.restype = ctypes.c_int
 lib.fi_run_closed_loop.argtypes = [_H, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
 lib.fi_run_closed_loop.restype = ctypes.c_int
+lib.fi_run_prompted.argtypes = [_H, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+lib.fi_run_prompted.restype = ctypes.c_int
 lib.fi_reset.argtypes = [_H]
 lib.fi_reset.restype = ctypes.c_int
 lib.fi_destroy.argtypes = [_H]
@@ -115,6 +118,10 @@ def fi_run_closed_loop(s: int, x_in, fb: int, y, x_out=None) -> None:
     _check(lib.fi_run_closed_loop(s, _ptr(x_in), int(fb), _ptr(y), _ptr(x_out)), "fi_run_closed_loop")
 
 
+def fi_run_prompted(s: int, x_prompt, p: int, y, x_out=None) -> None:
+    _check(lib.fi_run_prompted(s, _ptr(x_prompt), int(p), _ptr(y), _ptr(x_out)), "fi_run_prompted")
+
+
 def fi_reset(s: int) -> None:
     _check(lib.fi_reset(s), "fi_reset")
 
@@ -151,6 +158,9 @@ class Mixer:
 
     def run(self, x_in, fb, y, x_out=None):
         fi_run_closed_loop(self.handle, x_in, fb, y, x_out)
+
+    def run_prompted(self, x_prompt, p, y, x_out=None):
+        fi_run_prompted(self.handle, x_prompt, p, y, x_out)
 
     def reset(self):
         fi_reset(self.handle)

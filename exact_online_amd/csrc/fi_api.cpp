@@ -21,7 +21,7 @@ struct fi_handle {
     hipStream_t stream;
     int64_t pos;
     int dirty;         // accumulators need zeroing before the next fi_step
-    int run_grid[2];   // persistent-pass grid, [open, closed]
+    int run_grid[fi::kRunModes];   // persistent-pass grid per mode (open, closed, prompted)
 };
 
 namespace {
@@ -118,16 +118,18 @@ int build(fi_handle *s, const void *h) {
     int dev = 0, ncu = 0;
     FI_HIP(hipGetDevice(&dev));
     FI_HIP(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
-    for (int cl = 0; cl < 2; ++cl) {
-        int nb = fi::run_max_blocks_per_cu(d, cl);
+    int64_t slots = 0;
+    for (int mode = 0; mode < fi::kRunModes; ++mode) {
+        int nb = fi::run_max_blocks_per_cu(d, mode);
         if (nb < 1) nb = 1;
         int64_t g = (int64_t)nb * ncu;
         if (g > d.C) g = d.C;
-        s->run_grid[cl] = (int)g;
+        s->run_grid[mode] = (int)g;
+        if (g > slots) slots = g;
     }
     // scratch for FFT tiles larger than LDS: one slot per resident wavefront
-    // of the persistent pass, and as many for the per-step tile kernel
-    int64_t slots = s->run_grid[0] > s->run_grid[1] ? s->run_grid[0] : s->run_grid[1];
+    // of the persistent pass (its largest grid), and as many for the per-step
+    // tile kernel
     d.sc_slots = slots;
     d.sc_stride = d.umax_fft > fi::kLdsFftMax ? d.umax_fft : 0;
     if (d.sc_stride > 0) FI_HIP(dalloc(&d.scratch, (size_t)(slots * d.sc_stride) * 8));
@@ -226,9 +228,21 @@ int fi_run_closed_loop(fi_handle *s, const void *x_in, int32_t fb, float *y, voi
     if (!s || !x_in || !y) return FI_ERR_INVALID;
     if (fb != FI_FEEDBACK_NONE && fb != FI_FEEDBACK_TANH) return FI_ERR_INVALID;
     if (s->pos != 0) return FI_ERR_STATE;
-    const int closed = fb == FI_FEEDBACK_TANH;
+    const int mode = fb == FI_FEEDBACK_TANH ? fi::kRunClosed : fi::kRunOpen;
     // the persistent pass zeroes the accumulator rows it owns itself
-    FI_HIP(fi::launch_run(s->d, x_in, closed, y, x_out, s->run_grid[closed], s->stream));
+    FI_HIP(fi::launch_run(s->d, x_in, mode, 0, y, x_out, s->run_grid[mode], s->stream));
+    s->pos = s->d.L;
+    s->dirty = 1;
+    return FI_OK;
+}
+
+int fi_run_prompted(fi_handle *s, const void *x_prompt, int64_t p, float *y, void *x_out) {
+    if (!s || !x_prompt || !y) return FI_ERR_INVALID;
+    if (p < 1 || p > s->d.L) return FI_ERR_INVALID;
+    if (s->pos != 0) return FI_ERR_STATE;
+    // p = L is the open loop and p = 1 the closed loop (same layouts)
+    const int mode = p == s->d.L ? fi::kRunOpen : p == 1 ? fi::kRunClosed : fi::kRunPrompted;
+    FI_HIP(fi::launch_run(s->d, x_prompt, mode, p, y, x_out, s->run_grid[mode], s->stream));
     s->pos = s->d.L;
     s->dirty = 1;
     return FI_OK;

@@ -72,11 +72,13 @@ hipError_t launch_zero(float *p, int64_t n, hipStream_t st);
 hipError_t launch_step(const DevState &d, int64_t t, const void *x_t, float *y_t, hipStream_t st);
 hipError_t launch_tile(const DevState &d, int64_t i, hipStream_t st);
 
-// the persistent pass over all positions
-hipError_t launch_run(const DevState &d, const void *x_in, int closed, float *y, void *x_out,
+// the persistent pass over all positions: open loop, closed loop, or a
+// prompt of `prompt` given inputs followed by the closed loop
+enum { kRunOpen = 0, kRunClosed = 1, kRunPrompted = 2, kRunModes = 3 };
+hipError_t launch_run(const DevState &d, const void *x_in, int mode, int64_t prompt, float *y, void *x_out,
                       int grid, hipStream_t st);
 int run_lds_bytes(const DevState &d);
-int run_max_blocks_per_cu(const DevState &d, int closed);
+int run_max_blocks_per_cu(const DevState &d, int mode);
 int tile_fft_lds_bytes();
 
 }  // namespace fi

@@ -1166,6 +1166,7 @@ struct RunArgs {
     const void* x_in;
     float* y;
     void* x_out;
+    int64_t prompt;   // prompted runs: the number of given inputs
 };
 
 __device__ __forceinline__ void direct_tile_lds(int64_t i, int U, const FI_SHARED float* xring, int xmask,
@@ -1186,8 +1187,9 @@ __device__ __forceinline__ void direct_tile_lds(int64_t i, int U, const FI_SHARE
 // region: FFT / staging area [fftreg bytes] | (T >= kBlk only) xring[XR] | htap[2T].
 inline int run_lds_floats(const DevState& d) { return d.fftreg / 4 + (d.T >= kBlk ? d.XR + 2 * d.T : 0); }
 
-template <bool CLOSED, bool BF16>
+template <bool CLOSED, bool BF16, bool PROMPT = false>
 __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWaves))) void k_run(RunArgs a) {
+    static_assert(CLOSED || !PROMPT, "a prompted run feeds back after its prompt");
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ Cx<float> s_tw[kTwLds];  // twiddles A[64] = w_64^a, B[64] = w_4096^b, C[4] = w_16384^r
     __shared__ float s_ring[kBlk];      // accumulators of positions [t0, t0+W)
@@ -1206,6 +1208,12 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     const bool chain_wave = __builtin_amdgcn_readfirstlane(tid) < kWave;
     const int wmask = kBlk - 1, xmask = d.XR - 1;
     const int64_t L = d.L, D = d.D;
+    // Positions [0, P) take their input from x_in (x_in[B][P][D]), later ones
+    // the fed-back tanh(y): P = L in open loop, 1 in closed loop, the
+    // prompt's length in a prompted run.  A block whose inputs are all given
+    // has no serial chain and runs as in open loop.
+    const int64_t P = PROMPT ? a.prompt : (CLOSED ? 1 : L);
+    auto open_block = [&](int64_t t) { return !CLOSED || (PROMPT && t + kBlk <= P); };
     const int G = gridDim.x, bid = blockIdx.x;
     // consecutive channels on the same XCD (workgroups go round-robin over
     // the 8 XCDs), so their strided y / x_out rows meet in one L2
@@ -1220,14 +1228,14 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     const int t4_off = d.fftreg - kTapTableBytes;
     FI_SHARED V4* tz = reinterpret_cast<FI_SHARED V4*>(smem_ptr(smem) + t4_off);
     const float tap_scale = CLOSED ? kTanhScale : 1.0f;
-    // Open loop has no chain: the same region holds the filter copy of the
-    // block triangle on the matrix cores, hz[s(g)] = h[g] for g in [-256,
-    // 256), s(g) = (g + 256) + (g + 256) / 16, zero at negative lags and from
-    // L on.
+    // A block with every input given has no chain: the same region then
+    // holds the filter copy of the block triangle on the matrix cores,
+    // hz[s(g)] = h[g] for g in [-256, 256), s(g) = (g + 256) + (g + 256) / 16,
+    // zero at negative lags and from L on (open_form).
     FI_SHARED float* hz = reinterpret_cast<FI_SHARED float*>(tz);
     static_assert((2 * kBlk + 2 * kBlk / 16) * 4 <= kTapTableBytes, "the triangle's filter copy fits");
-    auto build_taps4 = [&](const FI_GLOBAL float* hrow) {
-        if constexpr (CLOSED) {
+    auto build_taps4 = [&](const FI_GLOBAL float* hrow, bool open_form) {
+        if (CLOSED && !open_form) {
             for (int e = tid; e < kTapTableBytes / 16; e += kTeam) {
                 const int q = e - 3 - kWave;   // lag of the first component
                 float v[4];
@@ -1267,7 +1275,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
         for (int q = tid; q < kBlk; q += kTeam) accw[q] = 0.f;
         if (direct)
             for (int q = tid; q < 2 * d.T; q += kTeam) htap[q] = q < L ? hrow[q] : 0.f;
-        build_taps4(hrow);
+        build_taps4(hrow, open_block(0));
         build_mm(hrow);
         team_sync();
         const float ch0v = tap_scale * hrow[0];   // closed loop: c h[0]
@@ -1277,13 +1285,12 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
 #pragma unroll
         for (int k = 0; k < kRegs; ++k) xbn[k] = 0.f;
         if (chain_wave) {
-            if constexpr (CLOSED) {
-                xcur = load_io<BF16>(a.x_in, b * D + c);
-            } else {
+            if constexpr (CLOSED) xcur = load_io<BF16>(a.x_in, b * P * D + c);   // x[0]
+            if constexpr (!CLOSED || PROMPT) {
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) {
                     const int64_t n = kWave * k + lane;
-                    if (n < L) xbn[k] = load_io<BF16>(a.x_in, (b * L + n) * D + c);
+                    if (n < P) xbn[k] = load_io<BF16>(a.x_in, (b * P + n) * D + c);
                 }
             }
             // nothing in flight when the block loop starts, so the waits inside it
@@ -1330,11 +1337,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     xb[k] = xbn[k];
                     p[k] = accw[(kWave * k + lane) & wmask];   // t0 is a multiple of the ring size
                 }
-                if constexpr (!CLOSED) {
+                if constexpr (!CLOSED || PROMPT) {
+                    if (!CLOSED || t0 + kBlk < P) {   // the next block has given inputs
 #pragma unroll
-                    for (int k = 0; k < kRegs; ++k) {
-                        const int64_t n = t0 + kBlk + kWave * k + lane;
-                        xbn[k] = n < L ? load_io<BF16>(a.x_in, (b * L + n) * D + c) : 0.f;
+                        for (int k = 0; k < kRegs; ++k) {
+                            const int64_t n = t0 + kBlk + kWave * k + lane;
+                            xbn[k] = n < P ? load_io<BF16>(a.x_in, (b * P + n) * D + c) : 0.f;
+                        }
                     }
                 }
                 if (stage_spec) {   // Un + 2 entries of 8 bytes, 16 bytes per lane
@@ -1364,8 +1373,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     nx[k] = (nx_in_row && pn < L) ? row[pn] : 0.f;
                 }
                 float xstart = 0.f;
-                if constexpr (!CLOSED) {
-                    // open loop: every input of the block is known, so its own
+                const bool openb = open_block(t0);
+                // a prompted run's block that holds the prompt's end: inputs
+                // below P are given, the rest fed back
+                const bool bnd = PROMPT && t0 < P && P < t0 + kBlk;
+                const int pl = (int)(P - t0);   // given inputs of a boundary block
+                if (openb) {
+                    // every input of the block is known, so its own
                     // triangle is one matrix-core product (mm_triangle256) on
                     // top of the ring's accumulators; the inputs go to the
                     // padded block the product (and the tile of side kBlk at
@@ -1385,7 +1399,15 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     wave_sync();
 #pragma unroll
                     for (int k = 0; k < kRegs; ++k) p[k] = myb[kWave * k + lane];
-                } else {
+                    if constexpr (PROMPT) {
+                        // the prompt ends with this block: the next input is
+                        // the first fed back, as the chain forms it
+                        if (t0 + kBlk == P) {
+                            xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(kTanhScale * readlane(p[kRegs - 1], kWave - 1)), 1.0f);
+                            if constexpr (BF16) xcur = round_bf16(xcur);
+                        }
+                    }
+                } else if constexpr (CLOSED) {
                     // tz0[64k - n]: the taps of position 64k + lane for inputs
                     // n .. n+3 (n a multiple of kTapBatch), in two batches
                     static_assert(kTapBatch == 4, "a tap batch is one 16-byte entry");
@@ -1397,10 +1419,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
 #pragma unroll
                     for (int k = 0; k < kRegs; ++k) p[k] *= kTanhScale;
                     v = readlane(p[0], 0);
+                    if (bnd) xcur = readlane(xb[0], 0);   // x[t0] is given
                     xstart = xcur;
-                    // one 64-step segment of the chain (steps 64K .. 64K+63)
-                    auto segment = [&](auto kc) {
+                    // one 64-step segment of the chain (steps 64K .. 64K+63);
+                    // BND: inputs below P come from xb instead of the feedback
+                    auto segment = [&](auto kc, auto bndc) {
                         constexpr int K = decltype(kc)::value;
+                        constexpr bool BND = decltype(bndc)::value;
 #pragma unroll
                         for (int m2 = 0; m2 < kWave; ++m2) {
                             const int m = kWave * K + m2;
@@ -1436,13 +1461,25 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                                 if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
                                 xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
                                 if constexpr (BF16) xcur = round_bf16(xcur);
+                                if constexpr (BND) {
+                                    if (m + 1 < kBlk && m + 1 < pl)
+                                        xcur = readlane(xb[(m + 1) / kWave], (m + 1) % kWave);
+                                }
                             }
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     };
-                    for_segments<0>(segment);
+                    if constexpr (PROMPT) {
+                        if (bnd) for_segments<0>([&](auto kc) { segment(kc, std::true_type{}); });
+                        else for_segments<0>([&](auto kc) { segment(kc, std::false_type{}); });
+                    } else {
+                        for_segments<0>([&](auto kc) { segment(kc, std::false_type{}); });
+                    }
                 }
-                if constexpr (CLOSED) {
+                if (openb) {
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) xk[k] = xb[k];
+                } else if constexpr (CLOSED) {
                     // The inputs of the block, one per lane: the register of
                     // position t ended as the same fma as the chain's c y[t], so
                     // the same exp2 / rcp / fma on it gives back x[t+1] exactly.
@@ -1457,11 +1494,9 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         const float prev = k == 0 ? xstart : readlane(f[k - 1], kWave - 1);
                         const float sh = __shfl_up(f[k], 1);
                         xk[k] = lane == 0 ? prev : sh;
+                        if (bnd && t0 + kWave * k + lane < P) xk[k] = xb[k];   // given
                         p[k] *= 1.0f / kTanhScale;
                     }
-                } else {
-#pragma unroll
-                    for (int k = 0; k < kRegs; ++k) xk[k] = xb[k];
                 }
                 // Everything this block loaded (staging, next accumulators) was
                 // issued a whole chain ago: wait for it here, before the stores
@@ -1515,7 +1550,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     // and the tap table: rebuild them
                     if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > d.mm_off) {
                         team_sync();
-                        if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > t4_off) build_taps4(hrow);
+                        if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > t4_off) build_taps4(hrow, open_block(i));
                         build_mm(hrow);
                     }
                 }
@@ -1526,6 +1561,14 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 if (!chain_wave) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 team_sync();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                if constexpr (PROMPT) {
+                    // the last block with every input given is done: the
+                    // chain's taps replace the triangle's filter copy
+                    if (open_block(t0) && !open_block(i)) {
+                        build_taps4(hrow, false);
+                        team_sync();
+                    }
+                }
             }
             if (chain_wave && !row_input && !mm_next) store_block();
         }
@@ -1596,28 +1639,30 @@ hipError_t launch_tile(const DevState& d, int64_t i, hipStream_t st) {
 
 int run_lds_bytes(const DevState& d) { return run_lds_floats(d) * (int)sizeof(float); }
 
-int run_max_blocks_per_cu(const DevState& d, int closed) {
+// The persistent pass of a mode (kRunOpen, kRunClosed, kRunPrompted) and
+// storage type.
+static const void* run_kernel(const DevState& d, int mode) {
+    if (mode == kRunClosed) return d.io_bf16 ? (const void*)k_run<true, true> : (const void*)k_run<true, false>;
+    if (mode == kRunPrompted)
+        return d.io_bf16 ? (const void*)k_run<true, true, true> : (const void*)k_run<true, false, true>;
+    return d.io_bf16 ? (const void*)k_run<false, true> : (const void*)k_run<false, false>;
+}
+
+int run_max_blocks_per_cu(const DevState& d, int mode) {
     int nb = 0;
-    const void* fn;
-    if (closed) fn = d.io_bf16 ? (const void*)k_run<true, true> : (const void*)k_run<true, false>;
-    else fn = d.io_bf16 ? (const void*)k_run<false, true> : (const void*)k_run<false, false>;
+    const void* fn = run_kernel(d, mode);
     const int lds = run_lds_bytes(d);
     if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kTeam, lds) != hipSuccess) return 0;
     return nb;
 }
 
-hipError_t launch_run(const DevState& d, const void* x_in, int closed, float* y, void* x_out, int grid,
-                      hipStream_t st) {
-    RunArgs a{d, x_in, y, x_out};
+hipError_t launch_run(const DevState& d, const void* x_in, int mode, int64_t prompt, float* y, void* x_out,
+                      int grid, hipStream_t st) {
+    RunArgs a{d, x_in, y, x_out, prompt};
     const size_t lds = (size_t)run_lds_bytes(d);
-    if (closed) {
-        if (d.io_bf16) hipLaunchKernelGGL((k_run<true, true>), dim3(grid), dim3(kTeam), lds, st, a);
-        else hipLaunchKernelGGL((k_run<true, false>), dim3(grid), dim3(kTeam), lds, st, a);
-    } else {
-        if (d.io_bf16) hipLaunchKernelGGL((k_run<false, true>), dim3(grid), dim3(kTeam), lds, st, a);
-        else hipLaunchKernelGGL((k_run<false, false>), dim3(grid), dim3(kTeam), lds, st, a);
-    }
+    hipLaunchKernelGGL(reinterpret_cast<void (*)(RunArgs)>(const_cast<void*>(run_kernel(d, mode))), dim3(grid),
+                       dim3(kTeam), lds, st, a);
     return hipGetLastError();
 }
 

@@ -118,6 +118,22 @@ int fi_step(fi_handle *s, const void *x_t, float *y_t);
  */
 int fi_run_closed_loop(fi_handle *s, const void *x_in, int32_t fb, float *y, void *x_out);
 
+/*
+ * fi_run_prompted: generation from a prompt ([FI] "Definizione del Compito":
+ * the prompt x_1 .. x_p is given, later inputs are produced one by one), all
+ * L steps in one call from position 0 (else FI_ERR_STATE), leaving the
+ * position at L.  Positions t < p read x_prompt[B][p][D] (io_dtype); from
+ * position p on, x[t] = tanh(y[t-1]) (rounded to bf16, nearest-even, when
+ * io_dtype is FI_BF16).  Every output goes through the same online schedule
+ * as fi_run_closed_loop; p = 1 is its closed loop with x_0 = x_prompt[.][0][.]
+ * and p = L its open loop.  y[B][L][D] (fp32) receives every output; x_out
+ * [B][L][D] (io_dtype), if not NULL, the inputs that produced them (the
+ * prompt's values unchanged).  FI_ERR_INVALID for a NULL handle, x_prompt or
+ * y, or p outside [1, L].  The caller owns x_prompt, y and x_out, which must
+ * stay valid until the stream has passed the call.
+ */
+int fi_run_prompted(fi_handle *s, const void *x_prompt, int64_t p, float *y, void *x_out);
+
 /* fi_reset: position := 0; the accumulators are cleared on the stream before
  * the next fi_step (fi_run_closed_loop clears the rows it uses itself). */
 int fi_reset(fi_handle *s);

@@ -50,6 +50,21 @@ def gpu_run(h_dev, B, D, L, dtype, x_in_dev, closed: bool, T: int = 0, want_x=Tr
     return y, xo
 
 
+def gpu_prompted(h_dev, B, D, L, dtype, prompt_dev, p: int, T: int = 0):
+    """One fi_run_prompted (prompt of p given inputs, then tanh feedback) over
+    a fresh handle; returns (y, x_out) CUDA tensors."""
+    import exact_online_amd as fi
+    t = torch()
+    io = fi.FI_BF16 if dtype == "bf16" else fi.FI_F32
+    y = t.empty((B, L, D), dtype=t.float32, device="cuda")
+    xo = t.empty((B, L, D), dtype=io_torch_dtype(dtype), device="cuda")
+    with fi.Mixer(B, D, L, h_dev, io, T, t.cuda.current_stream()) as m:
+        m.run_prompted(prompt_dev, p, y, xo)
+        t.cuda.synchronize()
+        assert m.position == L
+    return y, xo
+
+
 def gpu_steps(h_dev, B, D, L, dtype, x_dev, T: int = 0):
     """Open loop through fi_step, one position per call."""
     import exact_online_amd as fi

@@ -14,8 +14,8 @@ import pytest
 
 import oracle
 import workloads
-from fi_harness import (boundary_positions, chaos_horizon, columns, gpu_run, gpu_steps, host,
-                        log, rel_l2, to_dev)
+from fi_harness import (boundary_positions, chaos_horizon, columns, gpu_prompted, gpu_run, gpu_steps,
+                        host, log, rel_l2, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,6 +190,94 @@ def test_bf16_open_and_closed():
     assert np.array_equal(orc().round_bf16(xo), xo)     # stored on the bf16 grid
     ytf = orc().conv_open(h, xo)
     assert np.abs(y - ytf).max() <= 1e-4
+
+
+# ----------------------------------------------------------------- prompted
+# A prompt of p given inputs, then x[t+1] = tanh(y[t]) from position p on
+# (fi_run_prompted).  The prompt is the first p inputs of the workload's
+# open-loop series.
+def _prompted_case(w, p, T=0):
+    h = workloads.make_filter(w)
+    prompt = np.ascontiguousarray(workloads.make_x(w)[:, :p, :])
+    y, xo = gpu_prompted(to_dev(h, w.dtype), w.B, w.D, w.L, w.dtype, to_dev(prompt, w.dtype), p, T)
+    return h, prompt, host(y).astype(np.float64), host(xo).astype(np.float64)
+
+
+def _check_prompted(h, prompt, y, xo, bf16):
+    p = prompt.shape[1]
+    assert np.array_equal(xo[:, :p, :], prompt.astype(np.float64))   # the prompt, unchanged
+    want = np.tanh(y[:, p - 1:-1, :])
+    tol = 1e-6
+    if bf16:
+        tol = tol + 2.0 ** -8 * np.abs(want)
+    assert np.all(np.abs(xo[:, p:, :] - want) <= tol)
+    # each output from the inputs that were realised, to the closed-loop bound
+    # (|y| reaches ~10^2 in the long-filter family, so fp32 rounding alone is
+    # ~1e-4 there)
+    ytf = orc().conv_open(h, xo)
+    assert np.abs(y - ytf).max() <= 1e-3
+
+
+@pytest.mark.parametrize("p,T", [(2, 0), (100, 0), (255, 0), (256, 0), (257, 0), (300, 64), (511, 0),
+                                 (512, 0), (700, 0), (1023, 0), (300, 256), (768, 256)])
+def test_prompted_small_mixer(p, T):
+    w = small(B=2, D=5, seed=p)
+    log("case prompted small mixer p", p, "T", T)
+    h, prompt, y, xo = _prompted_case(w, p, T)
+    _check_prompted(h, prompt, y, xo, False)
+    yr, _ = orc().conv_prompted(h, prompt)         # free-running: this family is not chaotic
+    assert np.abs(y - yr).max() <= 1e-3
+
+
+def test_prompted_extremes_are_closed_and_open_loop():
+    w = small(B=2, D=4, L=700)
+    hd = to_dev(workloads.make_filter(w), "f32")
+    x = workloads.make_x(w)
+    log("case prompted p=1 and p=L")
+    y1, x1 = gpu_prompted(hd, w.B, w.D, w.L, "f32", to_dev(np.ascontiguousarray(x[:, :1]), "f32"), 1)
+    yc, xc = gpu_run(hd, w.B, w.D, w.L, "f32", to_dev(np.ascontiguousarray(x[:, 0]), "f32"), closed=True)
+    assert torch.equal(y1, yc) and torch.equal(x1, xc)
+    yl, xl = gpu_prompted(hd, w.B, w.D, w.L, "f32", to_dev(x, "f32"), w.L)
+    yo, _ = gpu_run(hd, w.B, w.D, w.L, "f32", to_dev(x, "f32"), closed=False)
+    assert torch.equal(yl, yo)
+
+
+@pytest.mark.parametrize("L,p", [(16384, 5000), (16384, 8192), (1 << 15, 12345)])
+def test_prompted_long(L, p):
+    # FFT tiles in LDS and (L = 2^15) through global scratch; this family is
+    # chaotic in closed loop, so the check is per step against the realised inputs
+    w = workloads.get("hyena-d1024-l16k").with_(D=4, L=L, B=1, seed=p)
+    log("case prompted long L", L, "p", p)
+    h, prompt, y, xo = _prompted_case(w, p)
+    _check_prompted(h, prompt, y, xo, False)
+
+
+def test_prompted_bf16():
+    w = small(dtype="bf16", B=2, D=8, L=4096)
+    log("case prompted bf16 p 1500")
+    h, prompt, y, xo = _prompted_case(w, 1500)
+    _check_prompted(h, prompt, y, xo, True)
+    assert np.array_equal(orc().round_bf16(xo), xo)
+
+
+def test_prompted_errors():
+    w = small(D=4, L=256)
+    h = to_dev(workloads.make_filter(w), "f32")
+    x = to_dev(workloads.make_x(w), "f32")
+    y = torch.empty((1, 256, 4), device="cuda")
+    with fi.Mixer(1, 4, 256, h, stream=torch.cuda.current_stream()) as m:
+        for p in (0, -1, 257):
+            with pytest.raises(fi.FiError) as e:
+                m.run_prompted(x, p, y)
+            assert e.value.status == fi.FI_ERR_INVALID
+        with pytest.raises(fi.FiError) as e:
+            m.run_prompted(0, 10, y)
+        assert e.value.status == fi.FI_ERR_INVALID
+        m.run_prompted(x, 10, y)
+        with pytest.raises(fi.FiError) as e:
+            m.run_prompted(x, 10, y)
+        assert e.value.status == fi.FI_ERR_STATE
+        torch.cuda.synchronize()
 
 
 # ------------------------------------------------------------------- state
