@@ -50,12 +50,13 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(B, D, L, s_x, s_h, T, closed) -> int:
+def algorithmic_bytes(B, D, L, s_x, s_h, T, closed, fed=None) -> int:
     """Bytes the method moves: every tile of side U reads its x block (U s_x)
     and reads+writes U accumulators (2U*4) per channel, plus the filter data
     per filter channel (taps h[1..2U) for direct tiles, the (U+1)-point complex
-    spectrum for FFT tiles); every step reads the accumulator and x, writes y
-    (and x in closed loop)."""
+    spectrum for FFT tiles); every step reads the accumulator and x, writes y,
+    and writes x where it is fed back (``fed`` positions: all of them in
+    closed loop, none in open loop, those after the prompt in a prompted run)."""
     P = (L - 1).bit_length()
     tot = 0
     for q in range(P):
@@ -63,17 +64,21 @@ def algorithmic_bytes(B, D, L, s_x, s_h, T, closed) -> int:
         n = L // (2 * U)
         Fq = (2 * U - 1) * s_h if U <= T else (U + 1) * 8
         tot += n * (B * D * (U * s_x + 2 * U * 4) + D * Fq)
-    tot += B * D * L * (4 + s_x + 4 + (s_x if closed else 0))
+    if fed is None:
+        fed = L if closed else 0
+    tot += B * D * L * (4 + s_x + 4) + B * D * fed * s_x
     return tot
 
 
-def load_traffic(sha: str, launches_per_step: int = 1):
+def load_traffic(sha: str, workload: str, mode: str):
+    """The committed counter summary's HBM bytes per launch, when it was taken
+    on this kernel source, workload and mode; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != sha:
+    if t.get("kernel_source_sha") != sha or t.get("workload") != workload or t.get("mode", mode) != mode:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -114,7 +119,8 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib
     cw = mean(_counter_rows(copy_write_dir, r"neg"))
     f_scale = nbytes / (cf * 1024.0)
     w_scale = nbytes / (cw * 1024.0)
-    out = {"kernel": "k_run", "workload": "hyena-d1024-l16k", "kernel_source_sha": kernel_source_sha(),
+    out = {"kernel": "k_run", "workload": "hyena-d1024-l16k", "mode": "closed-loop tanh",
+           "kernel_source_sha": kernel_source_sha(),
            "fetch_kib_per_launch": kf, "write_kib_per_launch": kw,
            "copy_bytes": nbytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale": f_scale, "write_scale": w_scale,
@@ -143,17 +149,22 @@ def copy_probe(mib: int, reps: int = 5) -> int:
     return 0
 
 
-def cpu_baseline(w, h, x0, nch: int):
+def cpu_baseline(w, h, x0, nch: int, prompt=None):
     import oracle
     orc = oracle.default()
     nch = min(nch, w.D)
     t0 = time.perf_counter()
-    orc.conv_closed(h[:, :nch], x0[:, :nch])
+    if prompt is None:
+        orc.conv_closed(h[:, :nch], x0[:, :nch])
+        kind = "closed loop"
+    else:
+        orc.conv_prompted(h[:, :nch], prompt[:, :, :nch])
+        kind = f"prompt of {prompt.shape[1]}, then closed loop"
     dt = time.perf_counter() - t0
     scale = (w.B * w.D) / (x0.shape[0] * nch)
     return {"value": w.B * w.L / (dt * scale), "unit": "tokens/s", "cores": orc.threads,
             "kind": "oracle",
-            "sample": f"{nch} of {w.D} channels, all {w.L} positions, closed loop, fp64; "
+            "sample": f"{nch} of {w.D} channels, all {w.L} positions, {kind}, fp64; "
                       f"{dt:.2f} s measured, scaled x{scale:g} (channels are independent)"}
 
 
@@ -169,6 +180,9 @@ def main() -> int:
     ap.add_argument("--small-tile-max", type=int, default=0)
     ap.add_argument("--cpu-channels", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prompt", type=int, default=0, metavar="P",
+                    help="generation from a prompt: the workload's first P open-loop inputs are "
+                         "given (fi_run_prompted), later ones fed back")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--write-traffic", nargs=5,
@@ -210,7 +224,16 @@ def main() -> int:
         return torch.from_numpy(a).cuda()
 
     hd = dev(h)
-    xin = dev(x0) if closed else dev(workloads.make_x(w))
+    P = args.prompt
+    prompt = None
+    if P:
+        if not 1 <= P <= w.L:
+            print(f"--prompt must lie in [1, {w.L}]", file=sys.stderr)
+            return 2
+        prompt = np.ascontiguousarray(workloads.make_x(w)[:, :P, :])
+        xin = dev(prompt)
+    else:
+        xin = dev(x0) if closed else dev(workloads.make_x(w))
     y = torch.empty((w.B, w.L, w.D), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -220,7 +243,10 @@ def main() -> int:
 
     def one():
         m.reset()
-        m.run(xin, fb, y)
+        if P:
+            m.run_prompted(xin, P, y)
+        else:
+            m.run(xin, fb, y)
 
     for _ in range(args.warmup):
         one()
@@ -245,17 +271,20 @@ def main() -> int:
     progress(f"bench: {args.steps} timed passes, {ms_step:.4f} ms/pass, per-pass {['%.4f' % p for p in per]}")
 
     s_x = 2 if w.dtype == "bf16" else 4
-    ab = algorithmic_bytes(w.B, w.D, w.L, s_x, s_x, 128, closed)
+    fed = w.L - P if P else None
+    ab = algorithmic_bytes(w.B, w.D, w.L, s_x, s_x, 128, closed, fed)
+    mode = (f"prompt of {P}, then closed-loop tanh" if P else
+            "closed-loop tanh" if closed else "open loop")
     achieved = ab / (kern_ms * 1e-3) / 1e9
     sha = kernel_source_sha()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(sha),
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(sha, w.name, mode),
                 "kernel": "k_run", "algorithmic_bytes": ab, "kernel_ms": round(kern_ms, 4),
                 "kernel_source_sha": sha}
     cpu = None
     if not args.no_cpu_baseline:
         progress(f"bench: timing the CPU oracle on {args.cpu_channels} channels")
-        cpu = cpu_baseline(w, h, x0, args.cpu_channels)
+        cpu = cpu_baseline(w, h, x0, args.cpu_channels, prompt)
     m.close()
     value = w.B * w.L / (ms_step * 1e-3)
     out = {
@@ -264,7 +293,7 @@ def main() -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "D": w.D, "L": w.L, "io_dtype": w.dtype,
-                   "mode": "closed-loop tanh" if closed else "open loop", "small_tile_max": T,
+                   "mode": mode, "small_tile_max": T,
                    "create_ms": round(create_ms, 1)},
         "roofline": roofline, "cpu_baseline": cpu,
     }
