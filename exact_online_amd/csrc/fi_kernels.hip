@@ -835,63 +835,69 @@ __device__ __forceinline__ void fft_tile_big(int M, int64_t i, const FI_GLOBAL f
     else if (R2 == 1) first_pass_load<8, 1>(sc, xs, M, tw);
     else first_pass_load<8, 2>(sc, xs, M, tw);
     global_dif(sc, M, M / (R1 * R2), F, tw);   // radix-8 (4) stages down to F-point blocks
-    for (int p = 0; p < P; ++p) {
+    for (int p = 0; p < 2; ++p) {
         FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
         copy_to_lds(lbuf, blk, F);
         dif_lds<F, F, float>(LdsIn<float>{lbuf}, lbuf, ltw);
-        if (p <= 1) {
-            const TwGlobalN twn{tw, 2 * M};
-            SpecBatch<kUntangleBatch> sb0;
-            if (p == 0) {
-                sb0.load(spec, 0, F / 2 + 1, PairsAll{});
-                untangle_lds<kUntangleBatch>(lbuf, spec, spec[M], F / 2 + 1, PairsAll{}, 0, ilog2(M), twn, sb0);
-            } else {
-                sb0.load(spec + F, 0, F / 2, PairsMirror{F});
-                untangle_lds<kUntangleBatch>(lbuf, spec + F, spec[M], F / 2, PairsMirror{F}, F, ilog2(M), twn, sb0);
-            }
-            dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        const TwGlobalN twn{tw, 2 * M};
+        SpecBatch<kUntangleBatch> sb0;
+        if (p == 0) {
+            sb0.load(spec, 0, F / 2 + 1, PairsAll{});
+            untangle_lds<kUntangleBatch>(lbuf, spec, spec[M], F / 2 + 1, PairsAll{}, 0, ilog2(M), twn, sb0);
+        } else {
+            sb0.load(spec + F, 0, F / 2, PairsMirror{F});
+            untangle_lds<kUntangleBatch>(lbuf, spec + F, spec[M], F / 2, PairsMirror{F}, F, ilog2(M), twn, sb0);
         }
+        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
         copy_from_lds(blk, lbuf, F);
     }
-    if (P > 2) {
-        for (int p = 2; p < P; ++p) {
-            const int a = 31 - __builtin_clz(p);   // octave of block p: blocks [2^a, 2^(a+1))
-            const int pp = 3 * (1 << a) - 1 - p;
-            if (pp < p) continue;
-            const int lm = ilog2(M);
-            // every load of a batch (spectrum, scratch, twiddle) is issued
-            // before any is used
+    // Blocks p >= 2 pair with the mirror block pp of their octave.  Per pair:
+    // pp's forward transform waits in the scratch, p's stays in LDS; the
+    // pair pass untangles the two (p from LDS, pp's mirrored entries from the
+    // scratch) and p goes back through its inverse transform from LDS; then
+    // pp makes its inverse visit.  Four block reads and four block writes
+    // per pair.
+    const int lm = ilog2(M);
+    for (int p = 2; p < P; ++p) {
+        const int a = 31 - __builtin_clz(p);   // octave of block p: blocks [2^a, 2^(a+1))
+        const int pp = 3 * (1 << a) - 1 - p;
+        if (pp < p) continue;
+        FI_GLOBAL Cx<float>* bp = sc + (int64_t)p * F;
+        FI_GLOBAL Cx<float>* bq = sc + (int64_t)pp * F;
+        copy_to_lds(lbuf, bq, F);
+        dif_lds<F, F, float>(LdsIn<float>{lbuf}, lbuf, ltw);
+        copy_from_lds(bq, lbuf, F);
+        copy_to_lds(lbuf, bp, F);
+        dif_lds<F, F, float>(LdsIn<float>{lbuf}, lbuf, ltw);
+        // every load of a batch (spectrum, scratch, twiddle) is issued
+        // before any is used; each thread's LDS entries are its own
 #pragma unroll 1
-            for (int k0 = 0; k0 < F; k0 += kTeam * kBatch) {
-                V2 sa[kBatch], sb[kBatch];
-                Cx<float> za[kBatch], zb[kBatch], wf[kBatch];
+        for (int k0 = 0; k0 < F; k0 += kTeam * kBatch) {
+            V2 sa[kBatch], sb[kBatch];
+            Cx<float> zb[kBatch], wf[kBatch];
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int k = k0 + lane + kTeam * u;
-                    sa[u] = spec[(int64_t)p * F + k];
-                    sb[u] = spec[(int64_t)pp * F + (F - 1 - k)];
-                    za[u] = sc[p * F + k];
-                    zb[u] = sc[pp * F + (F - 1 - k)];
-                    wf[u] = tw[2 * M + brev_bits(p * F + k, lm)];   // frequency never 0 in blocks >= 2
-                }
+            for (int u = 0; u < kBatch; ++u) {
+                const int k = k0 + lane + kTeam * u;
+                sa[u] = spec[(int64_t)p * F + k];
+                sb[u] = spec[(int64_t)pp * F + (F - 1 - k)];
+                zb[u] = bq[F - 1 - k];
+                wf[u] = tw[2 * M + brev_bits(p * F + k, lm)];   // frequency never 0 in blocks >= 2
+            }
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u)
-                    untangle_pair(za[u], zb[u], Cx<float>{sa[u].x, sa[u].y}, Cx<float>{sb[u].x, sb[u].y}, wf[u]);
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int k = k0 + lane + kTeam * u;
-                    sc[p * F + k] = za[u];
-                    sc[pp * F + (F - 1 - k)] = zb[u];
-                }
+            for (int u = 0; u < kBatch; ++u) {
+                const int k = k0 + lane + kTeam * u;
+                Cx<float> za = lbuf[lp(k)];
+                untangle_pair(za, zb[u], Cx<float>{sa[u].x, sa[u].y}, Cx<float>{sb[u].x, sb[u].y}, wf[u]);
+                lbuf[lp(k)] = za;
+                bq[F - 1 - k] = zb[u];
             }
         }
         team_sync_global();
-        for (int p = 2; p < P; ++p) {
-            FI_GLOBAL Cx<float>* blk = sc + (int64_t)p * F;
-            copy_to_lds(lbuf, blk, F);
-            dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
-            copy_from_lds(blk, lbuf, F);
-        }
+        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        copy_from_lds(bp, lbuf, F);
+        copy_to_lds(lbuf, bq, F);
+        dit_lds<F, ct_smallest(F), float>(lbuf, ltw);
+        copy_from_lds(bq, lbuf, F);
     }
     global_dit(sc, M, M / (R1 * R2), F, tw);
     // the last two inverse stages fused with the output; only the upper half
