@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import workloads
-from fi_harness import (boundary_positions, chaos_horizon, columns, gpu_run, log,
+from fi_harness import (boundary_positions, chaos_horizon, columns, gpu_prompted, gpu_run, log,
                         oracle_points_parallel, rel_l2, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -131,7 +131,49 @@ def closed_full(name, n=NSAMP, free_prefix=4096, free_chans=4):
     return w
 
 
+def prompted_full(name, P, n=NSAMP):
+    """A prompt of the workload's first P open-loop inputs, then the feedback
+    (fi_run_prompted): the recorded inputs hold the prompt unchanged and
+    tanh(y[t-1]) from P on, everywhere; sampled channels teacher-forced."""
+    w = workloads.get(name)
+    bf16 = w.dtype == "bf16"
+    log("case", name, "prompt", P, ": generating inputs")
+    h = workloads.make_filter(w)
+    prompt = np.ascontiguousarray(workloads.make_x(w)[:, :P, :])
+    hd, pd = to_dev(h, w.dtype), to_dev(prompt, w.dtype)
+    log("case", name, "prompt", P, ": GPU pass")
+    y, xo = gpu_prompted(hd, w.B, w.D, w.L, w.dtype, pd, P)
+    assert torch.isfinite(y).all().item()
+    assert torch.equal(xo[:, :P, :], pd)
+    worst = 0.0
+    chunk = max(1, (1 << 26) // w.D)
+    for b in range(w.B):
+        for l0 in range(P - 1, w.L - 1, chunk):
+            l1 = min(w.L - 1, l0 + chunk)
+            want = torch.tanh(y[b, l0:l1].double())
+            err = (xo[b, l0 + 1:l1 + 1].double() - want).abs()
+            if bf16:
+                err = err - 2.0 ** -8 * want.abs()
+            worst = max(worst, err.max().item())
+    log("feedback worst excess", worst)
+    assert worst <= 1e-6
+    chans = sample_channels(w, n)
+    yg, xg = columns(y, chans), columns(xo, chans)
+    del y, xo, hd, pd
+    torch.cuda.empty_cache()
+    log("case", name, "prompt", P, ": teacher-forced oracle on", len(chans), "channels")
+    ref = full_columns(h, chans, xg)
+    err = np.abs(yg - ref).max()
+    log("teacher-forced max abs", err, "prompt part rel l2", rel_l2(yg[:, :P], ref[:, :P]))
+    assert err <= 1e-3
+    assert rel_l2(yg[:, :P], ref[:, :P]) <= 1e-5     # the prompt's outputs are open loop
+
+
 # ------------------------------------------------------------------ D=1024
+def test_hyena_d1024_l16k_prompt_8192():
+    prompted_full("hyena-d1024-l16k", 8192, n=32)
+
+
 def test_hyena_d1024_l16k_closed():
     closed_full("hyena-d1024-l16k", n=32)
 
@@ -147,6 +189,10 @@ def test_b8_d2048_l64k_open():
 
 def test_b8_d2048_l64k_closed():
     closed_full("b8-d2048-l64k", free_prefix=2048)
+
+
+def test_b8_d2048_l64k_prompt_32768():
+    prompted_full("b8-d2048-l64k", 32768)
 
 
 # ------------------------------------------------------------------ bf16, L=128K
