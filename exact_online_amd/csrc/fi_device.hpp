@@ -181,6 +181,26 @@ struct GlobalTw {  // every power read from the global table tw[S + t]
         for (int r = 1; r < R; ++r) w[r] = tw[S + r * k];
     }
 };
+// One global lookup per butterfly, w_S^k; the other powers are products
+// (depth <= 3, as the LDS table's).
+template <typename T>
+struct GlobalTwProd {
+    TwPtr<T> tw;
+    template <int R>
+    __device__ __forceinline__ void powers(int S, int k, Cx<T>* w) const {
+        w[1] = tw[S + k];
+        if constexpr (R >= 4) {
+            w[2] = cmul(w[1], w[1]);
+            w[3] = cmul(w[2], w[1]);
+        }
+        if constexpr (R == 8) {
+            w[4] = cmul(w[2], w[2]);
+            w[5] = cmul(w[4], w[1]);
+            w[6] = cmul(w[4], w[2]);
+            w[7] = cmul(w[4], w[3]);
+        }
+    }
+};
 // Two-level LDS table for S <= 4096: with u = t * 4096 / S,
 // exp(-2 pi i u / 4096) = A[u >> 6] * B[u & 63], A[a] = w_64^a, B[b] = w_4096^b.
 // One lookup per butterfly; the other powers are products (depth <= 3).
@@ -470,7 +490,7 @@ __device__ __forceinline__ void dit_pass(FI_GLOBAL Cx<T>* sc, int M, int S, TwPt
 // global memory, the in-place Cooley-Tukey stage of ct_stage with run-time
 // sizes: forward (decimation in frequency) stores radix outputs in
 // bit-reversed slot order, the inverse (decimation in time) reads them so;
-// twiddles from the global table.  G butterflies per thread are in flight;
+// twiddles from one global table load per butterfly and its products.  G butterflies per thread are in flight;
 // M / R is a multiple of kTeam * G, so no load carries a condition (a load
 // under a branch waits for every load issued before it).
 template <int R, bool INV, typename T>
@@ -478,7 +498,7 @@ __device__ __forceinline__ void global_stage(FI_GLOBAL Cx<T>* sc, int M, int S, 
     constexpr int G = 16 / R;
     const int lane = team_tid();
     const int Q = S / R, NB = M / R;
-    const GlobalTw<T> gt{tw};
+    const GlobalTwProd<T> gt{tw};   // one table load per butterfly
 #pragma unroll 1
     for (int n0 = 0; n0 < NB; n0 += kTeam * G) {
         Cx<T> v[G][R];

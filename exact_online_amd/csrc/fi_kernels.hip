@@ -639,7 +639,7 @@ __device__ __forceinline__ void first_pass_load(FI_GLOBAL Cx<float>* sc, const F
     constexpr int G = R1 * R2 >= 16 ? 1 : 16 / (R1 * R2);
     const int lane = team_tid();
     const int Q1 = M / R1, Q2 = Q1 / R2;   // Q2 a multiple of kTeam * G
-    const GlobalTw<float> gt{tw};
+    const GlobalTwProd<float> gt{tw};   // one table load per butterfly
 #pragma unroll 1
     for (int n0 = 0; n0 < Q2; n0 += kTeam * G) {
         Cx<float> v[G][R2][R1];
@@ -702,7 +702,7 @@ __device__ __forceinline__ void last_pass_output(const TileSink& s, int64_t i, c
     const int lane = team_tid();
     const int Q1 = M / R1, Q2 = Q1 / R2;   // Q2 a multiple of kTeam * G
     const int nl = s.wend > i ? (int)((s.wend - i) / 2) : 0;
-    const GlobalTw<float> gt{tw};
+    const GlobalTwProd<float> gt{tw};   // one table load per butterfly
 #pragma unroll 1
     for (int n0 = 0; n0 < Q2; n0 += kTeam * G) {
         Cx<float> a[G][R1][R2];
