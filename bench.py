@@ -168,6 +168,62 @@ def cpu_baseline(w, h, x0, nch: int, prompt=None):
                       f"{dt:.2f} s measured, scaled x{scale:g} (channels are independent)"}
 
 
+def per_token(args, w, fi, torch) -> int:
+    """The online interface one position per call: fi_step (the red cell and
+    read-out, then the tile that position completes) on the workload's
+    open-loop inputs.  Reports the GPU time of every call (events on the
+    stream around it) and the host wall time per call."""
+    import numpy as np
+
+    import workloads
+    T = args.small_tile_max or fi.FI_DEFAULT_SMALL_TILE_MAX
+    stream = torch.cuda.current_stream()
+    io = fi.FI_BF16 if w.dtype == "bf16" else fi.FI_F32
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(workloads.to_bf16_bits(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    hd = dev(workloads.make_filter(w))
+    xt = dev(np.ascontiguousarray(workloads.make_x(w).transpose(1, 0, 2)))   # [L][B][D]
+    yt = torch.empty((w.L, w.B, w.D), dtype=torch.float32, device="cuda")
+    m = fi.Mixer(w.B, w.D, w.L, hd, io, args.small_tile_max, stream)
+    for _ in range(max(1, args.warmup // 10)):
+        m.reset()
+        for t in range(w.L):
+            m.step(xt[t], yt[t])
+    torch.cuda.synchronize()
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(w.L)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(w.L)]
+    m.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(w.L):
+        e0[t].record(stream)
+        m.step(xt[t], yt[t])
+        e1[t].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(e0, e1)])
+    m.close()
+    pos = np.arange(1, w.L + 1)
+    U = pos & -pos
+    U[-1] = 0   # the last position completes no tile
+    by_u = {}
+    for u in np.unique(U):
+        sel = us[U == u]
+        by_u[str(int(u))] = {"count": int(sel.size), "mean_us": round(float(sel.mean()), 2)}
+    out = {"metric": "fi_step GPU time per token", "unit": "us", "workload": w.name,
+           "B": w.B, "D": w.D, "L": w.L, "io_dtype": w.dtype, "small_tile_max": T,
+           "mean_us": round(float(us.mean()), 2), "median_us": round(float(np.median(us)), 2),
+           "p99_us": round(float(np.percentile(us, 99)), 2), "max_us": round(float(us.max()), 2),
+           "wall_us_per_token": round(wall / w.L * 1e6, 2),
+           "by_tile_side": by_u}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +236,8 @@ def main() -> int:
     ap.add_argument("--small-tile-max", type=int, default=0)
     ap.add_argument("--cpu-channels", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-token", action="store_true",
+                    help="time the online interface fi_step one position per call instead")
     ap.add_argument("--prompt", type=int, default=0, metavar="P",
                     help="generation from a prompt: the workload's first P open-loop inputs are "
                          "given (fi_run_prompted), later ones fed back")
@@ -209,6 +267,9 @@ def main() -> int:
     import workloads
 
     w = workloads.get(args.workload)
+    if args.per_token:
+        torch.cuda.set_device(0)
+        return per_token(args, w, fi, torch)
     T = args.small_tile_max or fi.FI_DEFAULT_SMALL_TILE_MAX
     closed = "closed" in w.modes[0]
     progress(f"bench: workload {w.name} B={w.B} D={w.D} L={w.L} {w.dtype} closed={closed}")
