@@ -108,7 +108,10 @@ int fi_step(fi_handle *s, const void *x_t, float *y_t);
 
 /*
  * fi_run_closed_loop: all L steps in one call, from position 0 (else
- * FI_ERR_STATE); leaves the position at L.  One persistent device pass.
+ * FI_ERR_STATE); leaves the position at L.  One persistent device pass: a
+ * single kernel launch on the handle's stream, which may be captured into a
+ * HIP graph and replayed (the pass clears the state it uses itself; the
+ * handle's position is host state and is not replayed).
  *   fb = FI_FEEDBACK_TANH: x_in is x_0[B][D]; x[t+1] = tanh(y[t]) (rounded to
  *        bf16, nearest-even, when io_dtype is FI_BF16).
  *   fb = FI_FEEDBACK_NONE: x_in is x[B][L][D] (the open-loop inputs, consumed

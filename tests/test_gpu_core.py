@@ -280,6 +280,75 @@ def test_prompted_errors():
         torch.cuda.synchronize()
 
 
+# ------------------------------------------------------------- HIP graphs
+def test_persistent_pass_replays_from_a_captured_graph():
+    """One fi_run_closed_loop / fi_run_prompted / open-loop launch captured on
+    the handle's stream and replayed several times, with eager work and
+    synchronisation between the replays: every replay equals the eager run
+    (the pass clears the rows it owns itself, so it needs no host-side
+    reset between replays)."""
+    w = small(B=2, D=8, L=2048)
+    h = workloads.make_filter(w)
+    x = workloads.make_x(w)
+    hd = to_dev(h, "f32")
+    x0d = to_dev(np.ascontiguousarray(x[:, 0]), "f32")
+    xd = to_dev(x, "f32")
+    pd = to_dev(np.ascontiguousarray(x[:, :700]), "f32")
+    st = torch.cuda.Stream()
+    cases = [("closed", lambda m, y, xo: m.run(x0d, fi.FI_FEEDBACK_TANH, y, xo)),
+             ("open", lambda m, y, xo: m.run(xd, fi.FI_FEEDBACK_NONE, y, xo)),
+             ("prompted", lambda m, y, xo: m.run_prompted(pd, 700, y, xo))]
+    for name, call in cases:
+        log("case graph replay", name)
+        with fi.Mixer(w.B, w.D, w.L, hd, stream=st) as m:
+            y_ref = torch.empty((w.B, w.L, w.D), device="cuda")
+            x_ref = torch.empty_like(y_ref)
+            with torch.cuda.stream(st):
+                call(m, y_ref, x_ref)
+            torch.cuda.synchronize()
+            m.reset()
+            y = torch.empty_like(y_ref)
+            xo = torch.empty_like(y_ref)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st):
+                call(m, y, xo)
+            for _ in range(3):
+                y.fill_(float("nan"))
+                xo.fill_(float("nan"))
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(y, y_ref) and torch.equal(xo, x_ref)
+            del g
+
+
+def test_distinct_handles_are_independent():
+    """Two handles with different filters and sizes, their passes interleaved
+    on one stream, give what each gives alone."""
+    wa = small(B=1, D=6, L=1500, seed=3)
+    wb = small(B=2, D=4, L=900, seed=4)
+    st = torch.cuda.current_stream()
+    ha, hb = to_dev(workloads.make_filter(wa), "f32"), to_dev(workloads.make_filter(wb), "f32")
+    xa, xb = to_dev(workloads.make_x(wa), "f32"), to_dev(workloads.make_x(wb), "f32")
+    ya1 = torch.empty((wa.B, wa.L, wa.D), device="cuda")
+    yb1 = torch.empty((wb.B, wb.L, wb.D), device="cuda")
+    with fi.Mixer(wa.B, wa.D, wa.L, ha, stream=st) as ma:
+        ma.run(xa, fi.FI_FEEDBACK_NONE, ya1)
+    with fi.Mixer(wb.B, wb.D, wb.L, hb, stream=st) as mb:
+        mb.run(xb, fi.FI_FEEDBACK_NONE, yb1)
+    ya2, yb2 = torch.empty_like(ya1), torch.empty_like(yb1)
+    log("case two handles interleaved")
+    with fi.Mixer(wa.B, wa.D, wa.L, ha, stream=st) as ma, fi.Mixer(wb.B, wb.D, wb.L, hb, stream=st) as mb:
+        ma.run(xa, fi.FI_FEEDBACK_NONE, ya2)
+        mb.run(xb, fi.FI_FEEDBACK_NONE, yb2)
+        ma.reset()
+        mb.reset()
+        ma.run(xa, fi.FI_FEEDBACK_NONE, ya2)
+        mb.run(xb, fi.FI_FEEDBACK_NONE, yb2)
+        torch.cuda.synchronize()
+    assert torch.equal(ya1, ya2) and torch.equal(yb1, yb2)
+
+
 # ------------------------------------------------------------------- state
 def test_state_machine_and_determinism():
     w = small(D=4, L=256)
