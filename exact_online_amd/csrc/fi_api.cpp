@@ -218,8 +218,15 @@ int fi_step(fi_handle *s, const void *x_t, float *y_t) {
         FI_HIP(fi::launch_zero(s->d.state, s->d.C * s->d.LS, s->stream));
         s->dirty = 0;
     }
-    FI_HIP(fi::launch_step(s->d, t, x_t, y_t, s->stream));
-    if (t + 1 < s->d.L) FI_HIP(fi::launch_tile(s->d, t + 1, s->stream));
+    const int64_t i = t + 1;
+    const int64_t U = i & -i;
+    if (i < s->d.L && U <= s->d.T) {
+        // one launch: the red cell and the direct tile
+        FI_HIP(fi::launch_step_tile(s->d, t, x_t, y_t, (int)U, s->stream));
+    } else {
+        FI_HIP(fi::launch_step(s->d, t, x_t, y_t, s->stream));
+        if (i < s->d.L) FI_HIP(fi::launch_tile(s->d, i, s->stream));
+    }
     s->pos = t + 1;
     return FI_OK;
 }

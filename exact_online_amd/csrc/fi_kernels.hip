@@ -969,6 +969,38 @@ __global__ void k_step(float* state, const float* hT, int64_t LS, int64_t D, int
     *slot = xv;                                        // the slot now holds x[t]
 }
 
+// The red cell of position t and, in the same launch, the direct tile of
+// side U <= T that position t+1 completes.  Thread (channel, r) computes
+// output r of the tile; it takes x[t] (the tile's last input) from x_t
+// rather than from the row, so it does not wait for the red cell's store,
+// and thread r = 0 also does the red cell.  Same sums in the same order as
+// k_step followed by k_tile_direct.
+template <bool BF16>
+__global__ void k_step_tile(float* state, const float* hT, int64_t LS, int64_t L, int64_t D, int64_t C,
+                            int64_t t, const void* x_t, float* y_t, int U) {
+    const int64_t n = C * (int64_t)U;
+    const int64_t i = t + 1;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t ch = idx / U;
+        const int r = (int)(idx % U);
+        const float* hr = hT + (ch % D) * LS;
+        float* row = state + ch * LS;
+        const float xv = load_io<BF16>(x_t, ch);
+        if (r == 0) {
+            y_t[ch] = __builtin_fmaf(hr[0], xv, row[t]);   // accumulated tiles + red cell
+            row[t] = xv;                                   // the slot now holds x[t]
+        }
+        if (i + r >= L) continue;
+        const float* xr = row + (i - U);
+        const float* hu = hr + U + r;
+        float acc = 0.f;
+        for (int j = 0; j < U - 1; ++j) acc = __builtin_fmaf(xr[j], hu[-j], acc);
+        acc = __builtin_fmaf(xv, hu[-(U - 1)], acc);
+        row[i + r] += acc;
+    }
+}
+
 // Direct Toeplitz tile: acc[i+r] += sum_{j<U} x[i-U+j] h[U+r-j], r in [0, U).
 __global__ void k_tile_direct(float* state, const float* hT, int64_t LS, int64_t L, int64_t D, int64_t C,
                               int64_t i, int U) {
@@ -1625,6 +1657,17 @@ hipError_t launch_step(const DevState& d, int64_t t, const void* x_t, float* y_t
     const int grid = grid_for(d.C, 256, 1 << 30);
     if (d.io_bf16) hipLaunchKernelGGL((k_step<true>), dim3(grid), dim3(256), 0, st, d.state, d.hT, d.LS, d.D, d.C, t, x_t, y_t);
     else hipLaunchKernelGGL((k_step<false>), dim3(grid), dim3(256), 0, st, d.state, d.hT, d.LS, d.D, d.C, t, x_t, y_t);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_tile(const DevState& d, int64_t t, const void* x_t, float* y_t, int U, hipStream_t st) {
+    const int grid = grid_for(d.C * (int64_t)U, 256);
+    if (d.io_bf16)
+        hipLaunchKernelGGL((k_step_tile<true>), dim3(grid), dim3(256), 0, st, d.state, d.hT, d.LS, d.L, d.D, d.C, t,
+                           x_t, y_t, U);
+    else
+        hipLaunchKernelGGL((k_step_tile<false>), dim3(grid), dim3(256), 0, st, d.state, d.hT, d.LS, d.L, d.D, d.C, t,
+                           x_t, y_t, U);
     return hipGetLastError();
 }
 

@@ -110,6 +110,34 @@ def test_delta_filters_hit_every_level(T):
         assert np.array_equal(y[0, :first_fft, c], ref[:first_fft].astype(np.float32)), k
 
 
+@pytest.mark.parametrize("T", [64, 128])
+def test_delta_filters_through_steps(T):
+    """fi_step one position per call (the red cell fused with the small direct
+    tiles, separate launches for the others): h = delta_k gives y[t] =
+    x[t-k], exactly before the first FFT tile (side 2T)."""
+    L = 2048
+    ks = [1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000, 2047]
+    D = len(ks)
+    h = np.zeros((L, D), np.float32)
+    for c, k in enumerate(ks):
+        h[k, c] = 1.0
+    x = np.random.default_rng(6).standard_normal((1, L, D)).astype(np.float32)
+    log("case delta filters through fi_step T", T)
+    y = host(gpu_steps(to_dev(h, "f32"), 1, D, L, "f32", to_dev(x, "f32"), T))
+    for c, k in enumerate(ks):
+        ref = np.zeros(L)
+        ref[k:] = x[0, :L - k, c]
+        assert np.abs(y[0, :, c] - ref).max() <= 2e-5, k
+        assert np.array_equal(y[0, :2 * T, c], ref[:2 * T].astype(np.float32)), k
+
+
+def test_bf16_through_steps():
+    w = small(dtype="bf16", B=2, D=5, L=700)
+    log("case bf16 open through fi_step")
+    y, ref = _open_case(w, 0, via_steps=True)
+    assert rel_l2(y, ref) <= 1e-5
+
+
 @pytest.mark.parametrize("L,T", [(8192, 128), (8192, 0), (512, 256)])
 def test_integer_data(L, T):
     """x, h in {-3..3}: direct tiles are exact; FFT tiles round to the exact
