@@ -70,7 +70,7 @@ hipError_t launch_zero(float *p, int64_t n, hipStream_t st);
 
 // online pieces
 hipError_t launch_step(const DevState &d, int64_t t, const void *x_t, float *y_t, hipStream_t st);
-hipError_t launch_tile(const DevState &d, int64_t i, hipStream_t st);
+hipError_t launch_tile(const DevState &d, int64_t i, hipStream_t st);   // FFT tiles (side > T)
 // the red cell of position t fused with the direct tile of side U <= T that
 // position t+1 completes
 hipError_t launch_step_tile(const DevState &d, int64_t t, const void *x_t, float *y_t, int U, hipStream_t st);

@@ -13,7 +13,7 @@
 //   k_transpose / k_twiddles / k_spectra   fi_create: filter rows, twiddle
 //       tables, and the per-level filter spectra ([FI] "Ottimizzazione della
 //       Memoria": the filter DFT is precomputed for each block size).
-//   k_step, k_tile_direct, k_tile_fft       one online step (fi_step).
+//   k_step_tile; k_step, k_tile_fft         one online step (fi_step).
 //   k_run                                   all L steps in one persistent pass:
 //       one wavefront per channel; no grid-wide synchronisation is ever needed
 //       because channels are independent ([FI] "Definizione Specifica di
@@ -973,8 +973,8 @@ __global__ void k_step(float* state, const float* hT, int64_t LS, int64_t D, int
 // side U <= T that position t+1 completes.  Thread (channel, r) computes
 // output r of the tile; it takes x[t] (the tile's last input) from x_t
 // rather than from the row, so it does not wait for the red cell's store,
-// and thread r = 0 also does the red cell.  Same sums in the same order as
-// k_step followed by k_tile_direct.
+// and thread r = 0 also does the red cell.  Each output is the direct
+// Toeplitz sum acc[i+r] += sum_{j<U} x[i-U+j] h[U+r-j], j ascending.
 template <bool BF16>
 __global__ void k_step_tile(float* state, const float* hT, int64_t LS, int64_t L, int64_t D, int64_t C,
                             int64_t t, const void* x_t, float* y_t, int U) {
@@ -998,23 +998,6 @@ __global__ void k_step_tile(float* state, const float* hT, int64_t LS, int64_t L
         for (int j = 0; j < U - 1; ++j) acc = __builtin_fmaf(xr[j], hu[-j], acc);
         acc = __builtin_fmaf(xv, hu[-(U - 1)], acc);
         row[i + r] += acc;
-    }
-}
-
-// Direct Toeplitz tile: acc[i+r] += sum_{j<U} x[i-U+j] h[U+r-j], r in [0, U).
-__global__ void k_tile_direct(float* state, const float* hT, int64_t LS, int64_t L, int64_t D, int64_t C,
-                              int64_t i, int U) {
-    const int64_t n = C * (int64_t)U;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t ch = idx / U;
-        const int r = (int)(idx % U);
-        if (i + r >= L) continue;
-        const float* xr = state + ch * LS + (i - U);
-        const float* hr = hT + (ch % D) * LS + U + r;
-        float acc = 0.f;
-        for (int j = 0; j < U; ++j) acc = __builtin_fmaf(xr[j], hr[-j], acc);
-        state[ch * LS + i + r] += acc;
     }
 }
 
@@ -1674,15 +1657,11 @@ hipError_t launch_step_tile(const DevState& d, int64_t t, const void* x_t, float
 int tile_fft_lds_bytes() { return (lds_fft_elems(kLdsFftMax) + kTwLds) * (int)sizeof(Cx<float>); }
 
 hipError_t launch_tile(const DevState& d, int64_t i, hipStream_t st) {
-    const int U = (int)(i & -i);
-    if (U <= d.T) {
-        hipLaunchKernelGGL(k_tile_direct, dim3(grid_for(d.C * (int64_t)U, 256)), dim3(256), 0, st, d.state, d.hT,
-                           d.LS, d.L, d.D, d.C, i, U);
-    } else {
-        const int F = U < kLdsFftMax ? U : kLdsFftMax;
-        const int grid = (int)(d.C < d.sc_slots ? d.C : d.sc_slots);
-        hipLaunchKernelGGL(k_tile_fft, dim3(grid), dim3(kTeam), (size_t)(lds_fft_elems(F) + kTwLds) * sizeof(Cx<float>), st, d, i, U);
-    }
+    const int U = (int)(i & -i);   // > T: the direct tiles go with the red cell (k_step_tile)
+    const int F = U < kLdsFftMax ? U : kLdsFftMax;
+    const int grid = (int)(d.C < d.sc_slots ? d.C : d.sc_slots);
+    hipLaunchKernelGGL(k_tile_fft, dim3(grid), dim3(kTeam), (size_t)(lds_fft_elems(F) + kTwLds) * sizeof(Cx<float>), st,
+                       d, i, U);
     return hipGetLastError();
 }
 
