@@ -36,6 +36,7 @@ def test_strerror_and_null_handles():
     fi.fi_destroy(None)  # no-op
     assert fi.lib.fi_step(None, 1, 1) == fi.FI_ERR_INVALID
     assert fi.lib.fi_run_closed_loop(None, 1, 1, 1, None) == fi.FI_ERR_INVALID
+    assert fi.lib.fi_run_prompted(None, 1, 1, 1, None) == fi.FI_ERR_INVALID
     assert fi.lib.fi_reset(None) == fi.FI_ERR_INVALID
 
 
