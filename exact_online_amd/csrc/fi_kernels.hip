@@ -636,7 +636,7 @@ __device__ __forceinline__ void fft_tile_lds(int64_t i, const XIn& xin, SpecP sp
 template <int R1, int R2>
 __device__ __forceinline__ void first_pass_load(FI_GLOBAL Cx<float>* sc, const FI_GLOBAL V2* xs, int M,
                                                 TwPtr<float> tw) {
-    constexpr int G = R1 * R2 >= 16 ? 1 : 16 / (R1 * R2);
+    constexpr int G = R1 * R2 >= 16 ? 2 : 16 / (R1 * R2);
     const int lane = team_tid();
     const int Q1 = M / R1, Q2 = Q1 / R2;   // Q2 a multiple of kTeam * G
     const GlobalTwProd<float> gt{tw};   // one table load per butterfly
