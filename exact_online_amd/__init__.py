@@ -32,6 +32,15 @@ if not LIB_PATH.exists():
     raise ImportError(f"{LIB_PATH} is not built: run `python exact_online_amd/build.py` "
                       "(hipcc, gfx950) before using exact_online_amd")
 
+# PyTorch, when installed, carries its own HIP runtime (same soname as the
+# system one this library links).  Loaded first, torch's runtime is the one
+# the library binds to, so the process has one runtime; the other order
+# loads two, and whichever owns the device leaves the other without it.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 lib = ctypes.CDLL(str(LIB_PATH))
 
 # every symbol include/fi.h declares
