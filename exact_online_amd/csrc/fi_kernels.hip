@@ -14,10 +14,11 @@
 //       tables, and the per-level filter spectra ([FI] "Ottimizzazione della
 //       Memoria": the filter DFT is precomputed for each block size).
 //   k_step_tile; k_step, k_tile_fft         one online step (fi_step).
-//   k_run                                   all L steps in one persistent pass:
-//       one wavefront per channel; no grid-wide synchronisation is ever needed
-//       because channels are independent ([FI] "Definizione Specifica di
-//       LCSM": the mixer is a per-channel Hadamard convolution).
+//   k_run                                   all L steps in one persistent pass
+//       (open loop, closed loop, or a prompt then the closed loop): a team of
+//       two wavefronts per channel; no grid-wide synchronisation is ever
+//       needed because channels are independent ([FI] "Definizione
+//       Specifica di LCSM": the mixer is a per-channel Hadamard convolution).
 #include <type_traits>
 
 #include "fi_device.hpp"

@@ -257,6 +257,16 @@ def test_prompted_small_mixer(p, T):
     assert np.abs(y - yr).max() <= 1e-3
 
 
+@pytest.mark.parametrize("L,p", [(300, 299), (300, 257), (700, 513), (700, 650), (700, 699), (1000, 768)])
+def test_prompted_ragged(L, p):
+    w = small(B=2, D=3, L=L, seed=L + p)
+    log("case prompted ragged L", L, "p", p)
+    h, prompt, y, xo = _prompted_case(w, p)
+    _check_prompted(h, prompt, y, xo, False)
+    yr, _ = orc().conv_prompted(h, prompt)
+    assert np.abs(y - yr).max() <= 1e-3
+
+
 def test_prompted_extremes_are_closed_and_open_loop():
     w = small(B=2, D=4, L=700)
     hd = to_dev(workloads.make_filter(w), "f32")
