@@ -119,3 +119,23 @@ def test_tile_at_rejects_out_of_range():
     for L, i in [(1, 1), (16, 0), (16, 16), (16, -1)]:
         assert fi.lib.fi_tile_at(L, i, ctypes.byref(t)) == fi.FI_ERR_INVALID
     assert fi.lib.fi_tile_at(16, 3, None) == fi.FI_ERR_INVALID
+
+
+# ------------------------------------------------------------------ bench
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_bench_algorithmic_bytes():
+    # D=1024, L=16K, fp32, closed loop, T=128: the per-pass figure the
+    # roofline divides by; a prompt of 8192 feeds back only the later half
+    import bench
+    assert bench.algorithmic_bytes(1, 1024, 16384, 4, 4, 128, True) == 2550915072
+    assert bench.algorithmic_bytes(1, 1024, 16384, 4, 4, 128, True, 16384 - 8192) == 2550915072 - 1024 * 8192 * 4
+    assert bench.algorithmic_bytes(1, 1024, 16384, 4, 4, 128, False) == 2550915072 - 1024 * 16384 * 4
