@@ -16,10 +16,14 @@
  * "Strategia di Tiling (Algoritmo 1)": once position i-1 is complete, with
  * U = largest power of two dividing i, the tile tau(x, [i-U, i), h, [i, i+U))
  * of [FI] "Definizione di Aggregazione di Contribuzione" adds the contribution
- * of x[i-U, i) to y[i, i+U) (clipped to < L).  Tiles of side U <= T (the
- * config's small_tile_max) are direct Toeplitz products; larger ones are FFT
- * circular convolutions of length 2U with precomputed filter spectra ([FI]
- * "Ottimizzazione della Memoria", "Trucco di Convoluzione Circolare").
+ * of x[i-U, i) to y[i, i+U) (clipped to < L).  Small tiles are direct
+ * Toeplitz products, larger ones FFT circular convolutions of length 2U with
+ * precomputed filter spectra ([FI] "Ottimizzazione della Memoria", "Trucco
+ * di Convoluzione Circolare").  fi_step does tiles of side U <= T (the
+ * config's small_tile_max) directly; the persistent pass (fi_run_closed_loop,
+ * fi_run_prompted) does every tile of side < 256 and, for T < 256, the tile
+ * of side 256 directly (on the matrix cores), and the larger ones by FFT.
+ * The results agree to fp32 rounding.
  *
  * Layouts: row-major, channels innermost: h[L][D], x[B][L][D], y[B][L][D],
  * per-step vectors [B][D].  Storage dtype of x and h is the config's io_dtype
