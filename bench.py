@@ -149,23 +149,85 @@ def copy_probe(mib: int, reps: int = 5) -> int:
     return 0
 
 
-def cpu_baseline(w, h, x0, nch: int, prompt=None):
+def host_cpu():
+    """(threads the oracle may use, CPUs this process may run on, CPU model)."""
+    cpus = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = cpus
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        threads = min(threads, int(env))   # the host's share for this job, where one is set
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, cpus, model
+
+
+ORACLE_BUDGET_MACS = 1.4e11   # about 10-30 s of the fp64 brute force on 16 host threads
+
+
+def oracle_sample(C: int, L: int, threads: int, budget: float = ORACLE_BUDGET_MACS):
+    """(channels, prefix length) of the oracle's timed sample: the whole
+    workload when it fits the budget, else as many channels as keep every
+    thread busy (the oracle hands out channels in blocks of 16) over the
+    longest power-of-two prefix that fits.  The brute force costs
+    Lp (Lp + 1) / 2 multiply-adds per channel, so the time extrapolates
+    exactly in channels and in L (L + 1)."""
+    cost = lambda n, l: n * l * (l + 1) / 2.0
+    if cost(C, L) <= budget:
+        return C, L
+    n_min = min(C, 16 * threads)
+    if cost(n_min, L) <= budget:
+        n = int(budget // cost(1, L)) // n_min * n_min
+        return max(n_min, min(n, C)), L
+    lp = L
+    while lp > 1 and cost(n_min, lp) > budget:
+        lp //= 2
+    return n_min, lp
+
+
+def cpu_baseline(w, h, x_in, closed: bool, prompt=None, nch: int = 0, budget: float = ORACLE_BUDGET_MACS):
+    """The oracle (fp64 brute force), in the GPU run's mode, timed on a bounded
+    sample of the workload (``oracle_sample``; ``nch`` forces a channel count)
+    and extrapolated to the whole workload."""
+    import numpy as np
+
     import oracle
-    orc = oracle.default()
-    nch = min(nch, w.D)
+    threads, cpus, model = host_cpu()
+    orc = oracle.Oracle(threads=threads)
+    n, lp = oracle_sample(w.B * w.D, w.L, threads, budget)
+    if nch:
+        n, lp = min(nch, w.B * w.D), w.L
+    # channels (b, c) in row-major order: whole batch rows where they fit
+    nb = max(1, min(w.B, n // w.D))
+    nd = min(w.D, n) if n < w.D else w.D
+    nsamp = nb * nd
+    hs = np.ascontiguousarray(h[:lp, :nd])
     t0 = time.perf_counter()
-    if prompt is None:
-        orc.conv_closed(h[:, :nch], x0[:, :nch])
+    if prompt is not None:
+        p = min(prompt.shape[1], lp)
+        orc.conv_prompted(hs, np.ascontiguousarray(prompt[:nb, :p, :nd]), L=lp)
+        kind = f"prompt of {prompt.shape[1]}, then closed loop"
+    elif closed:
+        orc.conv_closed(hs, np.ascontiguousarray(x_in[:nb, :nd]), L=lp)
         kind = "closed loop"
     else:
-        orc.conv_prompted(h[:, :nch], prompt[:, :, :nch])
-        kind = f"prompt of {prompt.shape[1]}, then closed loop"
+        orc.conv_open(hs, np.ascontiguousarray(x_in[:nb, :lp, :nd]))
+        kind = "open loop"
     dt = time.perf_counter() - t0
-    scale = (w.B * w.D) / (x0.shape[0] * nch)
-    return {"value": w.B * w.L / (dt * scale), "unit": "tokens/s", "cores": orc.threads,
-            "kind": "oracle",
-            "sample": f"{nch} of {w.D} channels, all {w.L} positions, {kind}, fp64; "
-                      f"{dt:.2f} s measured, scaled x{scale:g} (channels are independent)"}
+    scale = (w.B * w.D) / nsamp * (w.L * (w.L + 1)) / (lp * (lp + 1))
+    used = min(threads, -(-nd // 16) * nb)
+    full_s = dt * scale
+    return {"value": w.B * w.L / full_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "seconds": round(full_s, 3), "host_cpus": cpus, "threads_allowed": threads, "cpu_model": model,
+            "sample": f"{nsamp} of {w.B * w.D} channels ({nb} x {nd}), positions [0, {lp}) of {w.L}, {kind}, "
+                      f"fp64; {dt:.2f} s measured, scaled x{scale:.4g} (channels are independent; "
+                      f"the brute force costs L(L+1)/2 per channel)"}
 
 
 def per_token(args, w, fi, torch) -> int:
@@ -234,7 +296,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="hyena-d1024-l16k")
     ap.add_argument("--small-tile-max", type=int, default=0)
-    ap.add_argument("--cpu-channels", type=int, default=1024)
+    ap.add_argument("--mode", choices=("open", "closed"), default=None,
+                    help="open or closed loop (default: the workload's first mode)")
+    ap.add_argument("--cpu-channels", type=int, default=0,
+                    help="time the oracle on this many channels at all positions (default: a sample "
+                         "sized to about 10-30 s, see oracle_sample)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-token", action="store_true",
                     help="time the online interface fi_step one position per call instead")
@@ -271,7 +337,11 @@ def main() -> int:
         torch.cuda.set_device(0)
         return per_token(args, w, fi, torch)
     T = args.small_tile_max or fi.FI_DEFAULT_SMALL_TILE_MAX
-    closed = "closed" in w.modes[0]
+    mode_name = args.mode or w.modes[0]
+    if mode_name not in ("open", "closed"):
+        print(f"--mode must be open or closed", file=sys.stderr)
+        return 2
+    closed = mode_name == "closed"
     progress(f"bench: workload {w.name} B={w.B} D={w.D} L={w.L} {w.dtype} closed={closed}")
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
@@ -294,7 +364,8 @@ def main() -> int:
         prompt = np.ascontiguousarray(workloads.make_x(w)[:, :P, :])
         xin = dev(prompt)
     else:
-        xin = dev(x0) if closed else dev(workloads.make_x(w))
+        xh = x0 if closed else workloads.make_x(w)
+        xin = dev(xh)
     y = torch.empty((w.B, w.L, w.D), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -342,19 +413,20 @@ def main() -> int:
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(sha, w.name, mode),
                 "kernel": "k_run", "algorithmic_bytes": ab, "kernel_ms": round(kern_ms, 4),
                 "kernel_source_sha": sha}
+    m.close()
     cpu = None
     if not args.no_cpu_baseline:
-        progress(f"bench: timing the CPU oracle on {args.cpu_channels} channels")
-        cpu = cpu_baseline(w, h, x0, args.cpu_channels, prompt)
-    m.close()
+        progress("bench: timing the CPU oracle on a sample of the workload")
+        cpu = cpu_baseline(w, h, None if P else xh, closed, prompt, args.cpu_channels)
+        progress(f"bench: oracle {cpu['sample']}")
     value = w.B * w.L / (ms_step * 1e-3)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "D": w.D, "L": w.L, "io_dtype": w.dtype,
-                   "mode": mode, "small_tile_max": T,
+                   "acc_dtype": "f32", "mode": mode, "small_tile_max": T,
                    "create_ms": round(create_ms, 1)},
         "roofline": roofline, "cpu_baseline": cpu,
     }

@@ -49,9 +49,10 @@ EXPORTS = ("fi_create", "fi_step", "fi_run_closed_loop", "fi_run_prompted", "fi_
 
 
 class fi_config(ctypes.Structure):
+    # io_dtype is the C enum fi_dtype (int-sized)
     _fields_ = [("B", ctypes.c_int64), ("D", ctypes.c_int64), ("L", ctypes.c_int64),
-                ("io_dtype", ctypes.c_int32), ("small_tile_max", ctypes.c_int32),
-                ("stream", ctypes.c_void_p)]
+                ("io_dtype", ctypes.c_int32), ("stream", ctypes.c_void_p),
+                ("small_tile_max", ctypes.c_int32)]
 
 
 class fi_tile(ctypes.Structure):
@@ -151,7 +152,8 @@ def fi_tile_at(L: int, i: int) -> fi_tile:
 
 def make_config(B: int, D: int, L: int, io_dtype: int = FI_F32, small_tile_max: int = 0,
                 stream=None) -> fi_config:
-    return fi_config(int(B), int(D), int(L), int(io_dtype), int(small_tile_max), _stream(stream))
+    return fi_config(B=int(B), D=int(D), L=int(L), io_dtype=int(io_dtype), stream=_stream(stream),
+                     small_tile_max=int(small_tile_max))
 
 
 class Mixer:

@@ -59,10 +59,17 @@ void free_state(DevState &d) {
     d.scratch = nullptr;
 }
 
+// A failed hipMalloc also leaves its error as the thread's "last error",
+// which the next launch check (hipGetLastError) would then report as its own:
+// take it back here, so a rejected fi_create leaves no trace for later calls.
 template <typename T>
 hipError_t dalloc(T **p, size_t bytes) {
     void *v = nullptr;
     hipError_t e = hipMalloc(&v, bytes < 256 ? 256 : bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        v = nullptr;
+    }
     *p = static_cast<T *>(v);
     return e;
 }
@@ -160,7 +167,8 @@ int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
     if (out) *out = nullptr;
     if (!cfg || !h || !out) return FI_ERR_INVALID;
     if (cfg->B < 1 || cfg->D < 1 || cfg->L < 1) return FI_ERR_INVALID;
-    if (cfg->io_dtype != FI_F32 && cfg->io_dtype != FI_BF16) return FI_ERR_INVALID;
+    const int dt = static_cast<int>(cfg->io_dtype);   // the caller may store any int there
+    if (dt != FI_F32 && dt != FI_BF16) return FI_ERR_INVALID;
     int T = cfg->small_tile_max == 0 ? FI_DEFAULT_SMALL_TILE_MAX : cfg->small_tile_max;
     if (!is_pow2(T) || T < 64 || T > 256) return FI_ERR_INVALID;
     // sizes: every element count must fit comfortably in int64 and the
@@ -195,7 +203,7 @@ int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
     d.T = T;
     d.W = fi::kRunBlock;        // LDS accumulator ring of the persistent pass: one block
     d.XR = T >= fi::kRunBlock ? T : 0;   // LDS ring of recent inputs, only for its direct tiles
-    d.io_bf16 = cfg->io_dtype == FI_BF16;
+    d.io_bf16 = dt == FI_BF16;
     s->stream = static_cast<hipStream_t>(cfg->stream);
     s->pos = 0;
     s->dirty = 0;
@@ -231,11 +239,12 @@ int fi_step(fi_handle *s, const void *x_t, float *y_t) {
     return FI_OK;
 }
 
-int fi_run_closed_loop(fi_handle *s, const void *x_in, int32_t fb, float *y, void *x_out) {
+int fi_run_closed_loop(fi_handle *s, const void *x_in, fi_feedback fb, float *y, void *x_out) {
     if (!s || !x_in || !y) return FI_ERR_INVALID;
-    if (fb != FI_FEEDBACK_NONE && fb != FI_FEEDBACK_TANH) return FI_ERR_INVALID;
+    const int fbv = static_cast<int>(fb);   // the caller may pass any int
+    if (fbv != FI_FEEDBACK_NONE && fbv != FI_FEEDBACK_TANH) return FI_ERR_INVALID;
     if (s->pos != 0) return FI_ERR_STATE;
-    const int mode = fb == FI_FEEDBACK_TANH ? fi::kRunClosed : fi::kRunOpen;
+    const int mode = fbv == FI_FEEDBACK_TANH ? fi::kRunClosed : fi::kRunOpen;
     // the persistent pass zeroes the accumulator rows it owns itself
     FI_HIP(fi::launch_run(s->d, x_in, mode, 0, y, x_out, s->run_grid[mode], s->stream));
     s->pos = s->d.L;

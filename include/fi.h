@@ -51,14 +51,14 @@ extern "C" {
 
 typedef struct fi_handle fi_handle;  /* opaque; owns all the device memory it allocates */
 
-/* Storage type of x and h. */
-enum { FI_F32 = 0, FI_BF16 = 1 };
+/* Storage type of x and h (y and every accumulation are always fp32). */
+typedef enum { FI_F32 = 0, FI_BF16 = 1 } fi_dtype;
 
 /* Feedback of fi_run_closed_loop. */
-enum {
+typedef enum {
     FI_FEEDBACK_NONE = 0,   /* open loop: x[b][t][c] read from x_in[B][L][D] */
     FI_FEEDBACK_TANH = 1    /* closed loop: x[b][t+1][c] = tanh(y[b][t][c]) */
-};
+} fi_feedback;
 
 enum {
     FI_OK = 0,
@@ -79,11 +79,14 @@ typedef struct {
     int64_t B;               /* batch rows, >= 1 */
     int64_t D;               /* channels per row, >= 1 */
     int64_t L;               /* positions = filter length, >= 1 (any value; tiles clip to < L) */
-    int32_t io_dtype;        /* FI_F32 or FI_BF16 */
-    int32_t small_tile_max;  /* T: largest tile side done as a direct product; 0 = FI_DEFAULT_SMALL_TILE_MAX
-                                (every tile of side >= 128 is then an FFT tile);
-                                otherwise 64, 128 or 256 */
+    fi_dtype io_dtype;       /* FI_F32 or FI_BF16 (an int-sized enum) */
     void *stream;            /* hipStream_t the handle works on; NULL = the null stream */
+    int32_t small_tile_max;  /* T: the largest tile side fi_step does as a direct product, tiles of
+                                side > T being FFT tiles; 0 = FI_DEFAULT_SMALL_TILE_MAX; otherwise
+                                64, 128 or 256.  The persistent pass (fi_run_closed_loop,
+                                fi_run_prompted) does every tile of side < 256 directly whatever T
+                                is; it does the tile of side 256 from LDS when T = 256, else on
+                                the matrix cores, and the larger ones by FFT. */
 } fi_config;
 
 /*
@@ -123,7 +126,7 @@ int fi_step(fi_handle *s, const void *x_t, float *y_t);
  *   y[B][L][D] (fp32) receives every output; x_out[B][L][D] (io_dtype), if not
  *   NULL, receives the inputs that produced them.
  */
-int fi_run_closed_loop(fi_handle *s, const void *x_in, int32_t fb, float *y, void *x_out);
+int fi_run_closed_loop(fi_handle *s, const void *x_in, fi_feedback fb, float *y, void *x_out);
 
 /*
  * fi_run_prompted: generation from a prompt ([FI] "Definizione del Compito":

@@ -74,10 +74,15 @@ def gpu_steps(h_dev, B, D, L, dtype, x_dev, T: int = 0):
     xt = t.empty((B, D), dtype=io_torch_dtype(dtype), device="cuda")
     yt = t.empty((B, D), dtype=t.float32, device="cuda")
     with fi.Mixer(B, D, L, h_dev, io, T, t.cuda.current_stream()) as m:
-        for s in range(L):
-            xt.copy_(x_dev[:, s, :])
-            m.step(xt, yt)
-            y[:, s, :].copy_(yt)
+        if B == 1:
+            # x[0, s, :] and y[0, s, :] are contiguous rows: pass them directly
+            for s in range(L):
+                m.step(x_dev[0, s], y[0, s])
+        else:
+            for s in range(L):
+                xt.copy_(x_dev[:, s, :])
+                m.step(xt, yt)
+                y[:, s, :].copy_(yt)
         t.cuda.synchronize()
         assert m.position == L
     return y

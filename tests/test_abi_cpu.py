@@ -139,3 +139,57 @@ def test_bench_algorithmic_bytes():
     assert bench.algorithmic_bytes(1, 1024, 16384, 4, 4, 128, True) == 2550915072
     assert bench.algorithmic_bytes(1, 1024, 16384, 4, 4, 128, True, 16384 - 8192) == 2550915072 - 1024 * 8192 * 4
     assert bench.algorithmic_bytes(1, 1024, 16384, 4, 4, 128, False) == 2550915072 - 1024 * 16384 * 4
+
+
+def test_config_layout_matches_the_header(tmp_path):
+    """The binding's fi_config has the C struct's size and field offsets, and
+    the enum types are int-sized (a C compiler reads include/fi.h)."""
+    import subprocess
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "fi.h"\n'
+        'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(fi_config),'
+        ' offsetof(fi_config, B), offsetof(fi_config, D), offsetof(fi_config, L),'
+        ' offsetof(fi_config, io_dtype), offsetof(fi_config, stream),'
+        ' offsetof(fi_config, small_tile_max), sizeof(fi_dtype), sizeof(fi_feedback)); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)],
+                   check=True, capture_output=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    C = fi.fi_config
+    want = [ctypes.sizeof(C), C.B.offset, C.D.offset, C.L.offset, C.io_dtype.offset, C.stream.offset,
+            C.small_tile_max.offset, 4, 4]
+    assert got == want
+
+
+def test_run_rejects_unknown_feedback():
+    # the handle is checked first; an unknown feedback value is rejected before
+    # any device work even with a handle (checked on the GPU in the state tests)
+    assert fi.lib.fi_run_closed_loop(None, 1, 7, 1, None) == fi.FI_ERR_INVALID
+
+
+def test_bench_oracle_sample_sizes():
+    """The oracle's timed sample: whole workloads when they fit the budget,
+    else every thread's worth of channels over a power-of-two prefix."""
+    import bench
+    B = bench.ORACLE_BUDGET_MACS
+    assert bench.oracle_sample(16, 1024, 16) == (16, 1024)            # small mixer: whole
+    assert bench.oracle_sample(1024, 16384, 16) == (1024, 16384)      # D=1024, L=16K: whole
+    n, lp = bench.oracle_sample(16384, 65536, 16)
+    assert n == 256 and lp == 32768 and n * lp * (lp + 1) / 2 <= B
+    n, lp = bench.oracle_sample(768, 1 << 20, 16)
+    assert n == 256 and lp < (1 << 20) and n * lp * (lp + 1) / 2 <= B < n * (2 * lp) * (2 * lp + 1) / 2
+
+
+def test_bench_cpu_baseline_small_mixer():
+    import bench
+    import workloads
+    w = workloads.get("mixer-d16-l1k")
+    h = workloads.make_filter(w)
+    for closed, x in ((True, workloads.make_x0(w)), (False, workloads.make_x(w))):
+        cb = bench.cpu_baseline(w, h, x, closed)
+        assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["seconds"] > 0
+        assert cb["cores"] == 1 and cb["host_cpus"] >= 1 and cb["cpu_model"]
+        assert ("closed loop" if closed else "open loop") in cb["sample"]
+        assert "16 of 16 channels" in cb["sample"] and "[0, 1024) of 1024" in cb["sample"]

@@ -93,6 +93,7 @@ def open_full(name, n=NSAMP):
     per = [rel_l2(yg[k], ref[k]) for k in range(len(chans))]
     log("rel l2", err, "worst channel", max(per))
     assert err <= 1e-5
+    assert max(per) <= 1e-5          # an error confined to one channel shows here
     return w, h, x
 
 
@@ -225,13 +226,21 @@ def test_b4_d4096_l128k_bf16_open_sampled():
                                   [np.array([t]) for t in ts])
     ref = np.array([v[0] for v in refs])
     err = rel_l2(yg, ref)
-    log("samples rel l2", err)
+    # per sample: 1e-5 of the Cauchy-Schwarz bound on |y[t]|, the norms of the
+    # filter prefix and of the inputs that reach position t
+    scale = np.array([np.linalg.norm(h[:t + 1, c].astype(np.float64)) *
+                      np.linalg.norm(x[b, :t + 1, c].astype(np.float64)) for b, c, t in zip(bs, cs, ts)])
+    worst = float(np.max(np.abs(yg - ref) / np.maximum(scale, 1e-30)))
+    log("samples rel l2", err, "worst sample / its bound scale", worst)
     assert err <= 1e-5
+    assert worst <= 1e-5
     xw = np.stack([x[b, :, c] for b, c in whole]).astype(np.float64)
     refw = full_columns(h, whole, xw)
     errw = rel_l2(yw, refw)
-    log("whole channels rel l2", errw)
+    perw = [rel_l2(yw[k], refw[k]) for k in range(len(whole))]
+    log("whole channels rel l2", errw, "per channel", perw)
     assert errw <= 1e-5
+    assert max(perw) <= 1e-5
 
 
 # ------------------------------------------------------------------ L=1M power law
