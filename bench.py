@@ -286,6 +286,97 @@ def per_token(args, w, fi, torch) -> int:
     return 0
 
 
+def phases(args, w, fi, torch) -> int:
+    """The phase-timing build (libfi_prof.so): one pass after the warm-ups,
+    then the per-team cycle sums of the chain wavefront's phases (chain
+    segments, the rest of its block work, the barrier after the chain, the
+    block-boundary tiles by side, the stores), and the cumulative time at the
+    start of every block of the first channel (the per-token response of the
+    pages' Figure 2c, at the granularity of a block of 256 positions)."""
+    import numpy as np
+
+    import workloads
+    closed = (args.mode or w.modes[0]) == "closed"
+    stream = torch.cuda.current_stream()
+    io = fi.FI_BF16 if w.dtype == "bf16" else fi.FI_F32
+
+    def dev(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(workloads.to_bf16_bits(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    hd = dev(workloads.make_filter(w))
+    xin = dev(workloads.make_x0(w) if closed else workloads.make_x(w))
+    y = torch.empty((w.B, w.L, w.D), dtype=torch.float32, device="cuda")
+    m = fi.Mixer(w.B, w.D, w.L, hd, io, args.small_tile_max, stream)
+    fb = fi.FI_FEEDBACK_TANH if closed else fi.FI_FEEDBACK_NONE
+    for _ in range(max(1, args.warmup)):
+        m.reset()
+        m.run(xin, fb, y)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m.reset()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    m.run(xin, fb, y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    rec = np.array(fi.fi_profile_read(m.handle), dtype=np.float64)
+    m.close()
+    G, S, N = int(rec[0]), int(rec[1]), int(rec[2])
+    teams = rec[4:4 + G * S].reshape(G, S)
+    mean = teams.mean(axis=0)
+    total = mean[0]
+    blocks = mean[9]
+    mhz = teams[:, 0].max() / (ms * 1e3)   # the slowest team spans the pass
+    out = {"metric": "k_run phase breakdown (phase-timing build)", "workload": w.name,
+           "mode": "closed-loop tanh" if closed else "open loop", "teams": G,
+           "pass_ms": round(ms, 4), "clock_mhz_est": round(mhz, 1),
+           "cycles_per_team": round(total),
+           "share": {}, "chain_cycles_per_position": {}, "tile_cycles_each": {}}
+    names = {1: "setup", 6: "chain_rest", 7: "barrier_after_chain", 8: "stores"}
+    out["chain_rest_parts"] = {"prologue": round(mean[11] / total, 4), "epilogue": round(mean[12] / total, 4),
+                               "of_which_load_wait": round(mean[13] / total, 4)}
+    for k in range(4):
+        names[2 + k] = f"chain_segment_{k}"
+    for k, nm in names.items():
+        out["share"][nm] = round(mean[k] / total, 4)
+    tiles = 0.0
+    for q in range(24):
+        n = mean[40 + q]
+        if n > 0:
+            tiles += mean[16 + q]
+            out["share"][f"tile_{1 << q}"] = round(mean[16 + q] / total, 4)
+            out["tile_cycles_each"][str(1 << q)] = round(mean[16 + q] / n)
+    out["share"]["unaccounted"] = round(1.0 - sum(mean[k] for k in names) / total - tiles / total, 4)
+    if blocks > 0:
+        for k in range(4):
+            out["chain_cycles_per_position"][str(k)] = round(mean[2 + k] / (blocks * 64), 2)
+    ser = rec[4 + G * S:4 + G * S + 8 * N].reshape(N, 8)
+    if N and ser[0, 0] > 0:
+        t_us = (ser[:, 0] - ser[0, 0]) / mhz
+        out["cumulative_us_at_block_start"] = [round(v, 2) for v in t_us.tolist()]
+        out["block"] = 256
+        # the first channel's blocks, by the side of the tile at their end:
+        # mean cycles of each part of the block's timeline
+        parts = ("prologue", "chain", "epilogue_to_load_wait", "rest_of_epilogue", "barrier", "tile", "stores")
+        by = {}
+        for n in range(N):
+            r = ser[n]
+            i = (n + 1) * 256
+            key = str(i & -i) if i < w.L else "last"
+            if r[1] > 0:
+                d = [r[1] - r[0], r[2] - r[1], r[3] - r[2], r[4] - r[3], r[5] - r[4], r[6] - r[5], r[7] - r[6]]
+            else:   # no chain (open loop): everything before the barrier is the block's own work
+                d = [0.0, r[4] - r[0], 0.0, 0.0, r[5] - r[4], r[6] - r[5], r[7] - r[6]]
+            by.setdefault(key, []).append(d)
+        out["first_channel_block_cycles_by_tile"] = {
+            k: dict(zip(parts, [round(float(v)) for v in np.mean(np.array(v), axis=0)])) | {"blocks": len(v)}
+            for k, v in by.items()}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +398,9 @@ def main() -> int:
     ap.add_argument("--prompt", type=int, default=0, metavar="P",
                     help="generation from a prompt: the workload's first P open-loop inputs are "
                          "given (fi_run_prompted), later ones fed back")
+    ap.add_argument("--phases", action="store_true",
+                    help="phase breakdown of one pass from the phase-timing build "
+                         "(python exact_online_amd/build.py --profile)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--write-traffic", nargs=5,
@@ -326,6 +420,13 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe(args.copy_probe)
 
+    if args.phases:
+        prof = os.path.join(ROOT, "exact_online_amd", "libfi_prof.so")
+        if not os.path.exists(prof):
+            print("--phases needs the phase-timing build: python exact_online_amd/build.py --profile",
+                  file=sys.stderr)
+            return 2
+        os.environ["EXACT_ONLINE_AMD_LIB"] = prof
     import numpy as np
     import torch
 
@@ -333,6 +434,9 @@ def main() -> int:
     import workloads
 
     w = workloads.get(args.workload)
+    if args.phases:
+        torch.cuda.set_device(0)
+        return phases(args, w, fi, torch)
     if args.per_token:
         torch.cuda.set_device(0)
         return per_token(args, w, fi, torch)

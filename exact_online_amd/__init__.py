@@ -11,6 +11,7 @@ import (build it with ``python exact_online_amd/build.py`` or
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 
 __all__ = [
@@ -27,7 +28,9 @@ FI_DEFAULT_SMALL_TILE_MAX = 64
 FI_MAX_L = 1 << 25
 FI_OK, FI_ERR_INVALID, FI_ERR_NOMEM, FI_ERR_HIP, FI_ERR_STATE, FI_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 
-LIB_PATH = Path(__file__).resolve().parent / "libfi.so"
+# EXACT_ONLINE_AMD_LIB may name another build of the same library (the
+# phase-timing build libfi_prof.so, for bench.py --phases)
+LIB_PATH = Path(os.environ.get("EXACT_ONLINE_AMD_LIB") or Path(__file__).resolve().parent / "libfi.so")
 if not LIB_PATH.exists():
     raise ImportError(f"{LIB_PATH} is not built: run `python exact_online_amd/build.py` "
                       "(hipcc, gfx950) before using exact_online_amd")
@@ -79,6 +82,11 @@ lib.fi_strerror.argtypes = [ctypes.c_int]
 lib.fi_strerror.restype = ctypes.c_char_p
 lib.fi_tile_at.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(fi_tile)]
 lib.fi_tile_at.restype = ctypes.c_int
+# only in the phase-timing build (include/fi_profile.h)
+HAS_PROFILE = hasattr(lib, "fi_profile_read")
+if HAS_PROFILE:
+    lib.fi_profile_read.argtypes = [_H, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64]
+    lib.fi_profile_read.restype = ctypes.c_int64
 
 
 class FiError(RuntimeError):
@@ -148,6 +156,16 @@ def fi_tile_at(L: int, i: int) -> fi_tile:
     t = fi_tile()
     _check(lib.fi_tile_at(int(L), int(i), ctypes.byref(t)), "fi_tile_at")
     return t
+
+
+def fi_profile_read(s: int):
+    """Phase-timing build only: the last pass's record (a list of ints)."""
+    if not HAS_PROFILE:
+        raise RuntimeError(f"{LIB_PATH} is not the phase-timing build (libfi_prof.so)")
+    n = _check(int(lib.fi_profile_read(s, (ctypes.c_uint64 * 1)(), 0)), "fi_profile_read")
+    buf = (ctypes.c_uint64 * max(n, 1))()
+    _check(int(lib.fi_profile_read(s, buf, n)), "fi_profile_read")
+    return list(buf[:n])
 
 
 def make_config(B: int, D: int, L: int, io_dtype: int = FI_F32, small_tile_max: int = 0,

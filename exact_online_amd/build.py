@@ -10,8 +10,10 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libfi.so"
+PROFILE_LIB = PKG / "libfi_prof.so"   # the phase-timing build (-DFI_PROFILE=1), for bench.py --phases
 SOURCES = [CSRC / "fi_kernels.hip", CSRC / "fi_api.cpp"]
-HEADERS = [ROOT / "include" / "fi.h", CSRC / "fi_internal.h", CSRC / "fi_device.hpp"]
+HEADERS = [ROOT / "include" / "fi.h", ROOT / "include" / "fi_profile.h", CSRC / "fi_internal.h",
+           CSRC / "fi_device.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -43,13 +45,21 @@ def build(verbose: bool = False, out: Path | None = None, extra: list | None = N
     return out
 
 
-def is_stale() -> bool:
-    if not LIB.exists():
+def build_profile(verbose: bool = False) -> Path:
+    """The phase-timing library (not loaded by the product path)."""
+    return build(verbose, out=PROFILE_LIB, extra=["-DFI_PROFILE=1"])
+
+
+def is_stale(lib: Path = LIB) -> bool:
+    if not lib.exists():
         return True
-    t = LIB.stat().st_mtime
+    t = lib.stat().st_mtime
     return any(p.stat().st_mtime > t for p in SOURCES + HEADERS)
 
 
 if __name__ == "__main__":
-    build(verbose=True)
-    print(LIB)
+    if "--profile" in sys.argv[1:]:
+        print(build_profile(verbose=True))
+    else:
+        build(verbose=True)
+        print(LIB)

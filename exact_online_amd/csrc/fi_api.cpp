@@ -13,6 +13,9 @@
 
 #include "fi.h"
 #include "fi_internal.h"
+#if FI_PROFILE
+#include "fi_profile.h"
+#endif
 
 using fi::DevState;
 
@@ -48,10 +51,14 @@ int64_t max_tile(int64_t L) { return L <= 1 ? 0 : ((int64_t)1 << ilog2(L - 1)); 
 
 void free_state(DevState &d) {
     if (d.hT) (void)hipFree(d.hT);
+    if (d.pre) (void)hipFree(d.pre);
+    d.pre = nullptr;
     if (d.state) (void)hipFree(d.state);
     if (d.spec) (void)hipFree(d.spec);
     if (d.twf) (void)hipFree(d.twf);
     if (d.scratch) (void)hipFree(d.scratch);
+    if (d.prof) (void)hipFree(d.prof);
+    d.prof = nullptr;
     d.hT = nullptr;
     d.state = nullptr;
     d.spec = nullptr;
@@ -92,28 +99,12 @@ int build(fi_handle *s, const void *h) {
         smax = q;
     }
     d.F = d.umax_fft > 0 ? (d.umax_fft < fi::kLdsFftMax ? d.umax_fft : fi::kLdsFftMax) : 1;
-    // FFT region of the persistent pass: the largest LDS transform, or the
-    // staging of a tile's input (4U bytes) and, for U <= 1024, its spectrum
-    // (8 (U + 2) bytes) behind that tile's own transform buffer.  Above every
-    // staging area: the data of the tile of side kRunBlock (done on the
-    // matrix cores), then the chain's tap table at the top of the region
-    // (both rebuilt after a tile whose transform reaches them).
-    int staged = 0;
-    for (int q = 0; q < fi::kMaxLevels; ++q) {
-        if (d.spec_off[q] < 0) continue;
-        const int U = 1 << q;
-        int need = 0;
-        if (U == fi::kRunBlock) need = 0;   // the matrix-core tile: its own area
-        else if (U <= 1024) need = fi::lds_fft_elems(U) * 8 + 4 * U + 8 * (U + 2);
-        else if (U <= 2048) need = fi::lds_fft_elems(U) * 8 + 4 * U;
-        if (need > staged) staged = need;
-    }
-    d.mm_off = (staged + 15) / 16 * 16;
-    d.fftreg = fi::lds_fft_elems(d.F) * 8;
-    if (d.mm_off + fi::kMmBytes + fi::kTapTableBytes > d.fftreg)
-        d.fftreg = d.mm_off + fi::kMmBytes + fi::kTapTableBytes;
+    // the persistent pass's LDS FFT / staging region has a fixed layout
+    d.mm_off = fi::kRunMmOff;
+    d.fftreg = fi::kRunFftReg;
 
     FI_HIP(dalloc(&d.hT, (size_t)(d.D * d.LS) * sizeof(float)));
+    FI_HIP(dalloc(&d.pre, (size_t)(d.D * fi::kRunBlock) * sizeof(float)));
     FI_HIP(dalloc(&d.state, (size_t)(d.C * d.LS) * sizeof(float)));
     FI_HIP(dalloc(&d.spec, (size_t)(spec_total > 0 ? spec_total : 1) * 8));
     // twiddles up to 2 umax points (the untangle of the largest tiles uses
@@ -140,8 +131,16 @@ int build(fi_handle *s, const void *h) {
     d.sc_slots = slots;
     d.sc_stride = d.umax_fft > fi::kLdsFftMax ? d.umax_fft : 0;
     if (d.sc_stride > 0) FI_HIP(dalloc(&d.scratch, (size_t)(slots * d.sc_stride) * 8));
+    if (fi::kProfile) {
+        // header, one slot row per team of the largest grid, one entry per block
+        d.prof_n = fi::kProfHeader + slots * fi::kProfSlots +
+                   ((d.L + fi::kRunBlock - 1) / fi::kRunBlock) * fi::kProfSeriesW;
+        FI_HIP(dalloc(&d.prof, (size_t)d.prof_n * 8));
+        FI_HIP(hipMemsetAsync(d.prof, 0, (size_t)d.prof_n * 8, st));
+    }
 
     FI_HIP(fi::launch_transpose(d, h, st));
+    FI_HIP(fi::launch_prefix(d, st));
     void *twd = nullptr;
     FI_HIP(dalloc(&twd, (size_t)((int64_t)2 << smax) * 16));
     hipError_t e = fi::launch_twiddles(twd, d.twf, smax, st);
@@ -304,5 +303,16 @@ int fi_tile_at(int64_t L, int64_t i, fi_tile *out) {
     out->out_hi = i + U < L ? i + U : L;
     return FI_OK;
 }
+
+#if FI_PROFILE
+int64_t fi_profile_read(fi_handle *s, uint64_t *out, int64_t cap) {
+    if (!s || !out || cap < 0) return FI_ERR_INVALID;
+    if (!s->d.prof) return 0;
+    if (hipStreamSynchronize(s->stream) != hipSuccess) return FI_ERR_HIP;
+    const int64_t n = cap < s->d.prof_n ? cap : s->d.prof_n;
+    if (n > 0 && hipMemcpy(out, s->d.prof, (size_t)n * 8, hipMemcpyDeviceToHost) != hipSuccess) return FI_ERR_HIP;
+    return s->d.prof_n;
+}
+#endif
 
 }  // extern "C"

@@ -8,6 +8,34 @@
 namespace fi {
 
 constexpr int kMaxLevels = 40;
+
+// Phase-timing build (hipcc -DFI_PROFILE=1, a separate library; the product
+// build leaves it 0 and carries none of it): each team of the persistent pass
+// sums the cycles (s_memtime) of its chain wavefront's phases and writes them
+// once at the end, plus, for the first team's first channel, the cycle count
+// at the start of every block of 256 positions.
+#ifndef FI_PROFILE
+#define FI_PROFILE 0
+#endif
+constexpr bool kProfile = FI_PROFILE != 0;
+constexpr int kProfSlots = 64;   // cycle sums per team
+constexpr int kProfHeader = 4;   // grid, kProfSlots, blocks in the series, clock source (0 = s_memtime)
+constexpr int kProfSeriesW = 8;  // timestamps per block in the series (see fi_profile.h)
+enum {
+    kPfTotal = 0,      // the team's whole run
+    kPfSetup = 1,      // per channel: LDS tables before the first block
+    kPfSeg = 2,        // + k: segment k of the chain (64 positions each), k < 4
+    kPfChainRest = 6,  // chain wavefront's block work around the segments (loads, recompute, LDS writes)
+    kPfWait = 7,       // the team barrier after the chain
+    kPfStore = 8,      // the block's y / x stores after its tile
+    kPfBlocks = 9,     // blocks run (a count)
+    kPfChannels = 10,  // channels run (a count)
+    kPfPrologue = 11,  // chain wavefront: block start to its first chain step (part of kPfChainRest)
+    kPfEpilogue = 12,  // chain wavefront: last chain step to the barrier (part of kPfChainRest)
+    kPfLoadWait = 13,  // the wait for the block's loads after its chain (part of kPfEpilogue)
+    kPfTile = 16,      // + q: the block-boundary tile of side 2^q, barriers included
+    kPfTileCount = 40  // + q: how many such tiles
+};
 constexpr int kRunBlock = 256;     // positions per block of the persistent pass (= its LDS ring W)
 constexpr int kLdsFftMax = 4096;  // largest complex FFT held in LDS (32 KiB in fp32)
 constexpr int kTwLds = 132;       // LDS twiddle table: w_64^a, w_4096^b (64 each), w_16384^r (4)
@@ -25,6 +53,17 @@ constexpr int lds_fft_elems(int M) { return M + M / 8; }
 constexpr int kMmXFloats = 15 + kRunBlock + 65;
 constexpr int kMmHSlots = (64 + 2 * kRunBlock) + (64 + 2 * kRunBlock) / 16 + 4;
 constexpr int kMmBytes = (kMmXFloats + kMmHSlots + kRunBlock) * 4;
+// The run kernel's FFT / staging region has one fixed layout (compile-time
+// offsets, whatever L is): the staging area of the largest staged tile (side
+// 2048: its transform buffer and input block; smaller tiles also stage their
+// spectrum, which fits below), then the matrix-core tile's data, then the
+// chain's tap table at the top.  Tiles of side >= 4096 transform across all
+// of it (their data and the taps are rebuilt afterwards).
+constexpr int kRunMmOff = (lds_fft_elems(2048) * 8 + 4 * 2048 + 15) / 16 * 16;
+constexpr int kRunFftReg = lds_fft_elems(kLdsFftMax) * 8 > kRunMmOff + kMmBytes + kTapTableBytes
+                               ? lds_fft_elems(kLdsFftMax) * 8
+                               : kRunMmOff + kMmBytes + kTapTableBytes;
+static_assert(lds_fft_elems(1024) * 8 + 4 * 1024 + 8 * (1024 + 2) <= kRunMmOff, "staging of the tiles up to 1024 fits");
 
 // Device state of one handle.  Layouts (rows padded to LS = L rounded up to 64):
 //   hT[D][LS]      filter, one contiguous row per channel c, fp32
@@ -47,10 +86,11 @@ struct DevState {
     int W;                 // LDS accumulator window (positions) of the run kernel
     int XR;                // LDS ring of recent inputs (positions)
     int F;                 // LDS FFT buffer (complex points) of the run kernel
-    int fftreg;            // bytes of the run kernel's LDS FFT / staging region
-    int mm_off;            // bytes: its matrix-core tile data (above the staging areas)
+    int fftreg;            // bytes of the run kernel's LDS FFT / staging region (kRunFftReg)
+    int mm_off;            // bytes: its matrix-core tile data (kRunMmOff)
     int io_bf16;
     float *hT;
+    float *pre;            // [D][kRunBlock]: prefix sums of the closed-loop chain's scaled taps
     float *state;
     void *spec;            // float2
     int64_t spec_off[kMaxLevels];  // element (float2) offset of level q, -1 if none
@@ -59,6 +99,8 @@ struct DevState {
     int64_t sc_stride;     // complex elements per scratch slot
     int64_t sc_slots;
     int umax_fft;          // largest FFT tile side (0 if none)
+    unsigned long long *prof;   // phase-timing build only (else NULL): header, per-team sums, series
+    int64_t prof_n;             // its length in elements
 };
 
 // fi_create helpers (synchronous work on `st`)
@@ -67,6 +109,7 @@ hipError_t launch_twiddles(void *twd, void *twf, int smax, hipStream_t st);
 hipError_t launch_spectra(const DevState &d, int q, void *scd, int64_t scd_stride, int64_t slots,
                           const void *twd, hipStream_t st);
 hipError_t launch_zero(float *p, int64_t n, hipStream_t st);
+hipError_t launch_prefix(const DevState &d, hipStream_t st);
 
 // online pieces
 hipError_t launch_step(const DevState &d, int64_t t, const void *x_t, float *y_t, hipStream_t st);

@@ -139,6 +139,22 @@ __global__ __launch_bounds__(kTeam) void k_spectra(const float* hT, int64_t LS, 
     }
 }
 
+// Per channel c, the prefix sums of the closed-loop chain's scaled taps,
+// pre[c][j] = sum_{l <= j} fl(s h[l][c]) for j < kRunBlock (s = 2 log2(e), the
+// scale of the chain's accumulators; fl the fp32 rounding the chain's taps
+// get), summed in fp64 and rounded once.  The chain that pushes r = (1 - x)/2
+// instead of x adds these to its accumulators at the start of every block.
+__global__ void k_prefix(const float* hT, int64_t LS, int64_t L, int64_t D, float* pre) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= D) return;
+    const float* hr = hT + c * LS;
+    double acc = 0.0;
+    for (int j = 0; j < kRunBlock; ++j) {
+        if (j < L) acc += (double)(kTanhScale * hr[j]);
+        pre[c * kRunBlock + j] = (float)acc;
+    }
+}
+
 __global__ void k_zero(float* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = 0.f;
@@ -1108,9 +1124,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // wavefront; D[alpha][a] in lane a + 16 (alpha / 4), register alpha % 4.
 // The operands of a group of kG steps are loaded while the group before it
 // is multiplied; four accumulators keep four products in flight.
-template <int NC, int GBASE>
+template <int NC, int GBASE, int D0 = 0, int ND = 16>
 __device__ __forceinline__ v4f mm_toeplitz(const FI_SHARED float* ab, const FI_SHARED float* bb, v4f init) {
-    constexpr int kSteps = 16 * NC, kG = 8, kGroups = kSteps / kG;
+    constexpr int kSteps = ND * NC, kG = 8, kGroups = kSteps / kG;
     static_assert(kSteps % kG == 0, "whole groups");
     v4f acc[4];
     acc[0] = init;
@@ -1121,7 +1137,7 @@ __device__ __forceinline__ v4f mm_toeplitz(const FI_SHARED float* ab, const FI_S
         constexpr int g = decltype(gc)::value;
         static_for<0, kG>([&](auto uc) {
             constexpr int n = g * kG + decltype(uc)::value;
-            constexpr int d = n / NC, c = n % NC;
+            constexpr int d = D0 + n / NC, c = n % NC;
             constexpr int G = GBASE + d - 64 * c;
             static_assert(G >= 64, "slots of the filter copy stay in range");
             av[g & 1][n % kG] = ab[G + G / 16];
@@ -1146,8 +1162,8 @@ __device__ __forceinline__ v4f mm_toeplitz(const FI_SHARED float* ab, const FI_S
 }
 
 __device__ __forceinline__ void mm_tile256(const FI_SHARED float* xz, const FI_SHARED float* hsk,
-                                           FI_SHARED float* ring) {
-    static_assert(kBlk == 256, "the matrix-core tile covers one 256-position block");
+                                           FI_SHARED float* ring, FI_SHARED float* part) {
+    static_assert(kBlk == 256 && kTeamWaves == 2, "the matrix-core tile covers one block, on two wavefronts");
     const int tid = team_tid();
     const int l = tid & (kWave - 1);
     const int al = l & 15, kk = l >> 4;
@@ -1155,13 +1171,24 @@ __device__ __forceinline__ void mm_tile256(const FI_SHARED float* xz, const FI_S
     // j = alpha - kk; with G = g - 16 j + 64 = 320 + d - 64 c (>= 64), s(g) =
     // G + G / 16 + 17 j (16 j / 16 = j exactly).  B of step (d, c), lane
     // (a, kk): x[a - d + 16 (4c + kk)] = xz[a + 16 kk + 64 c - d + 15].
-    // The team's first wavefront alone: the others share their SIMDs with
-    // other teams' chains, which matrix work beside them slows down.
-    if (__builtin_amdgcn_readfirstlane(tid) < kWave) {
-        const v4f y = mm_toeplitz<5, 320>(hsk + 17 * (al - kk), xz + al + 16 * kk, v4f{0.f, 0.f, 0.f, 0.f});
+    // The two wavefronts take d < 8 and d >= 8 (40 steps each); the second
+    // hands its partial sums over through LDS (`part`, 256 floats), and the
+    // first adds both to the ring in a fixed order.
+    const bool first = __builtin_amdgcn_readfirstlane(tid) < kWave;
+    const FI_SHARED float* ab = hsk + 17 * (al - kk);
+    const FI_SHARED float* bb = xz + al + 16 * kk;
+    v4f y;
+    if (first) y = mm_toeplitz<5, 320, 0, 8>(ab, bb, v4f{0.f, 0.f, 0.f, 0.f});
+    else y = mm_toeplitz<5, 320, 8, 8>(ab, bb, v4f{0.f, 0.f, 0.f, 0.f});
+    if (!first) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[4 * l + r] = y[r];
+    }
+    team_sync();
+    if (first) {
         // position q = a + 16 alpha of the next block
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ring[al + 16 * (4 * kk + r)] += y[r];
+        for (int r = 0; r < 4; ++r) ring[al + 16 * (4 * kk + r)] += y[r] + part[4 * l + r];
     }
 }
 
@@ -1207,19 +1234,28 @@ __device__ __forceinline__ void direct_tile_lds(int64_t i, int U, const FI_SHARE
 // accumulator ring (separate objects, so the compiler sees that the direct-to-
 // LDS staging loads into the dynamic region never touch them), and a dynamic
 // region: FFT / staging area [fftreg bytes] | (T >= kBlk only) xring[XR] | htap[2T].
-inline int run_lds_floats(const DevState& d) { return d.fftreg / 4 + (d.T >= kBlk ? d.XR + 2 * d.T : 0); }
+inline int run_lds_floats(const DevState& d) { return kRunFftReg / 4 + (d.T >= kBlk ? d.XR + 2 * d.T : 0); }
 
 template <bool CLOSED, bool BF16, bool PROMPT = false>
 __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWaves))) void k_run(RunArgs a) {
     static_assert(CLOSED || !PROMPT, "a prompted run feeds back after its prompt");
+    // The fp32 closed loop's chain pushes r = 1 / (1 + 2^(c y)) = (1 - x) / 2
+    // rather than x = tanh(y) = 1 - 2 r: with the taps -2 c h and, added to
+    // every position's accumulator at the start of its block, the prefix sums
+    // of the taps c h (the "1" of every input of the block that reaches it),
+    // the accumulators hold the same sums, and x = 1 - 2 r is no longer on
+    // the serial path.  (bf16 storage rounds x itself, and a prompted run
+    // pushes given inputs: both keep pushing x.)
+    constexpr bool RPUSH = CLOSED && !BF16 && !PROMPT;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ Cx<float> s_tw[kTwLds];  // twiddles A[64] = w_64^a, B[64] = w_4096^b, C[4] = w_16384^r
     __shared__ float s_ring[kBlk];      // accumulators of positions [t0, t0+W)
+    __shared__ float s_pre[RPUSH ? kBlk : 1];   // the chain's tap prefix sums (RPUSH)
     const DevState& d = a.d;
     FI_SHARED Cx<float>* lbuf = smem_ptr(reinterpret_cast<Cx<float>*>(smem));
     FI_SHARED Cx<float>* twl = smem_ptr(s_tw);
     FI_SHARED float* accw = smem_ptr(s_ring);
-    FI_SHARED float* xring = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.fftreg);  // direct tiles only
+    FI_SHARED float* xring = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + kRunFftReg);  // direct tiles only
     FI_SHARED float* htap = xring + d.XR;    // h[0 .. 2T), direct tiles only
     const bool direct = d.T >= kBlk;
     const int tid = threadIdx.x;
@@ -1247,9 +1283,10 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     // 0 (s = c in closed loop, see below, else 1), tz[q + 3] = (hz[q],
     // hz[q-1], hz[q-2], hz[q-3]) holds the taps of four consecutive chain
     // steps in one 16-byte read.
-    const int t4_off = d.fftreg - kTapTableBytes;
+    constexpr int t4_off = kRunFftReg - kTapTableBytes;
     FI_SHARED V4* tz = reinterpret_cast<FI_SHARED V4*>(smem_ptr(smem) + t4_off);
     const float tap_scale = CLOSED ? kTanhScale : 1.0f;
+    const float chain_scale = RPUSH ? -2.0f * kTanhScale : tap_scale;   // the chain's taps
     // A block with every input given has no chain: the same region then
     // holds the filter copy of the block triangle on the matrix cores,
     // hz[s(g)] = h[g] for g in [-256, 256), s(g) = (g + 256) + (g + 256) / 16,
@@ -1263,7 +1300,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 float v[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    v[j] = (q - j >= 0 && q - j < kBlk && q - j < L) ? tap_scale * hrow[q - j] : 0.f;
+                    v[j] = (q - j >= 0 && q - j < kBlk && q - j < L) ? chain_scale * hrow[q - j] : 0.f;
                 tz[e] = V4{v[0], v[1], v[2], v[3]};
             }
         } else {
@@ -1277,7 +1314,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     // 512) at slots (g + 64) + (g + 64) / 16 (zero at g < 0 and g >= L):
     // built when a channel starts and after a tile whose transform reaches
     // them
-    FI_SHARED float* mxz = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + d.mm_off);
+    FI_SHARED float* mxz = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + kRunMmOff);
     FI_SHARED float* mhs = mxz + kMmXFloats;
     FI_SHARED float* myb = mhs + kMmHSlots;   // the block's y, for the other wavefronts' stores
     auto build_mm = [&](const FI_GLOBAL float* hrow) {
@@ -1288,26 +1325,49 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
         }
     };
     fill_lds_twiddles(twl);
+    // Phase timing (profile build only; kProfile is false in the product
+    // build and all of this folds away): the chain wavefront's cycle sums,
+    // per-level tile sums and counts in LDS.
+    __shared__ unsigned long long s_pf[kProfile ? 2 * 24 : 1];
+    [[maybe_unused]] unsigned long long pf_t0 = 0, pf_tb = 0, pf_tc = 0, pf_td = 0, pf_te = 0;
+    [[maybe_unused]] unsigned long long pf_setup = 0, pf_chain = 0, pf_wait = 0, pf_store = 0;
+    [[maybe_unused]] unsigned long long pf_blocks = 0, pf_chans = 0;
+    [[maybe_unused]] unsigned long long pf_s0 = 0, pf_s1 = 0, pf_pro = 0, pf_epi = 0, pf_vm = 0;
+    [[maybe_unused]] unsigned long long pf_seg[kRegs] = {};
+    if constexpr (kProfile) {
+        pf_t0 = clock64();
+        for (int q = tid; q < 2 * 24; q += kTeam) s_pf[q] = 0;
+    }
 
     for (int64_t ch = ch0; ch < d.C; ch += G) {
         const int64_t b = ch / D, c = ch % D;
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         const FI_GLOBAL float* hrow = gmem(d.hT + c * d.LS);
+        if constexpr (kProfile) {
+            pf_tb = clock64();
+            pf_chans += 1;
+        }
         team_sync();   // the previous channel's last chain is done with the taps and the ring
         for (int q = tid; q < kBlk; q += kTeam) accw[q] = 0.f;
         if (direct)
             for (int q = tid; q < 2 * d.T; q += kTeam) htap[q] = q < L ? hrow[q] : 0.f;
         build_taps4(hrow, open_block(0));
         build_mm(hrow);
+        if constexpr (RPUSH) {
+            const FI_GLOBAL float* pr = gmem(d.pre + c * kBlk);
+            for (int q = tid; q < kBlk; q += kTeam) s_pre[q] = pr[q];
+        }
         team_sync();
-        const float ch0v = tap_scale * hrow[0];   // closed loop: c h[0]
+        const float ch0v = chain_scale * hrow[0];   // closed loop: c h[0] (RPUSH: -2 c h[0])
 
         float xcur = 0.f;        // closed loop: x at the next position (uniform)
+        float rcur = 0.f;        // RPUSH: (1 - x) / 2 at the next position (uniform)
         float xbn[kRegs];        // open loop: inputs of the next block
 #pragma unroll
         for (int k = 0; k < kRegs; ++k) xbn[k] = 0.f;
         if (chain_wave) {
             if constexpr (CLOSED) xcur = load_io<BF16>(a.x_in, b * P * D + c);   // x[0]
+            if constexpr (RPUSH) rcur = (1.0f - xcur) * 0.5f;
             if constexpr (!CLOSED || PROMPT) {
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) {
@@ -1319,8 +1379,36 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             // only cover what each block issues
             __builtin_amdgcn_s_waitcnt(0x0F70);
         }
+        if constexpr (kProfile) pf_setup += clock64() - pf_tb;
+        // y and x_out of a block go out during the next block's chain (their
+        // addresses are D floats apart per position, so each store touches 64
+        // lines; issued between the chain's transcendentals they cost next to
+        // nothing): the chain wavefront leaves them in LDS (myb, mxz) and
+        // stores them from there, as the last use of that LDS before it
+        // rewrites it.  Lane l writes position t0 + 64 k + l of column c.
+        const uint32_t ylane = (uint32_t)lane * (uint32_t)D;
+        bool defer_prev = false;   // the previous block's y / x_out wait in LDS
+        auto store_deferred = [&](int64_t tp) {
+            const bool full = tp + kBlk <= L;
+#pragma unroll
+            for (int k = 0; k < kRegs; ++k) {
+                const float yv = myb[kWave * k + lane];
+                const float xv = mxz[15 + kWave * k + lane];
+                const int64_t ob = (b * L + tp + kWave * k) * D + c;   // uniform
+                if (full || tp + kWave * k + lane < L) {
+                    (yout + ob)[ylane] = yv;
+                    if (a.x_out) store_io<BF16>(a.x_out, ob + ylane, xv);
+                }
+            }
+        };
         for (int64_t t0 = 0; t0 < L; t0 += kBlk) {
             float p[kRegs], xk[kRegs];
+            [[maybe_unused]] unsigned long long pf_tw = 0;
+            if constexpr (kProfile) {
+                pf_tb = clock64();
+                pf_s0 = pf_s1 = pf_tw = 0;
+                pf_blocks += 1;
+            }
             // the next tile's spectrum and older input block go straight to the
             // idle LDS FFT region while the chain runs
             const int64_t inext = t0 + kBlk;
@@ -1338,21 +1426,43 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             // (x is the tile's input there) and the other wavefronts, idle
             // during that tile, store the block
             auto store_block = [&]() {
+                const bool full = t0 + kBlk <= L;
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) {
-                    const int64_t tl = t0 + kWave * k + lane;
-                    if (tl < L) {
-                        const int64_t o = (b * L + tl) * D + c;
-                        yout[o] = p[k];
-                        if (a.x_out) store_io<BF16>(a.x_out, o, xk[k]);
-                        row[tl] = xk[k];  // the slot of a consumed accumulator now holds x
+                    if (full || t0 + kWave * k + lane < L) {
+                        const int64_t ob = (b * L + t0 + kWave * k) * D + c;   // uniform
+                        (yout + ob)[ylane] = p[k];
+                        if (a.x_out) store_io<BF16>(a.x_out, ob + ylane, xk[k]);
+                        row[t0 + kWave * k + lane] = xk[k];  // the slot of a consumed accumulator now holds x
                     }
                 }
             };
+            if (!chain_wave) {
+                // The other wavefront, idle during the chain, stages the next
+                // tile's spectrum and the older part of its input block
+                // straight into the idle LDS FFT region, and waits for them
+                // before the barrier that ends the chain.
+                if (stage_spec) {   // Un + 2 entries of 8 bytes, 16 bytes per lane
+                    const FI_GLOBAL V4* sp = reinterpret_cast<const FI_GLOBAL V4*>(
+                        gmem(static_cast<const V2*>(d.spec)) + d.spec_off[ilog2(Un)] + c * (int64_t)(Un + 2));
+                    FI_SHARED V4* sd = reinterpret_cast<FI_SHARED V4*>(sst);
+                    const int n16 = (Un + 2) / 2;
+                    for (int k = 0; k < n16; k += kWave)
+                        if (k + lane < n16)
+                            __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(sp + k + lane), (FI_SHARED void*)(sd + k), 16, 0, 0);
+                }
+                if (stage_x) {
+                    for (int k = 0; k < Un - kBlk; k += kWave)
+                        __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(row + (inext - Un) + k + lane),
+                                                         (FI_SHARED void*)(xst + k), 4, 0, 0);
+                }
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            }
             if (chain_wave) {
                 // the serial chain goes first wherever it shares a SIMD with
                 // another team's tile work
                 __builtin_amdgcn_s_setprio(2);
+                if (defer_prev) store_deferred(t0 - kBlk);
                 float xb[kRegs];
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) {
@@ -1367,20 +1477,6 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                             xbn[k] = n < P ? load_io<BF16>(a.x_in, (b * P + n) * D + c) : 0.f;
                         }
                     }
-                }
-                if (stage_spec) {   // Un + 2 entries of 8 bytes, 16 bytes per lane
-                    const FI_GLOBAL V4* sp = reinterpret_cast<const FI_GLOBAL V4*>(
-                        gmem(static_cast<const V2*>(d.spec)) + d.spec_off[ilog2(Un)] + c * (int64_t)(Un + 2));
-                    FI_SHARED V4* sd = reinterpret_cast<FI_SHARED V4*>(sst);
-                    const int n16 = (Un + 2) / 2;
-                    for (int k = 0; k < n16; k += kWave)
-                        if (k + lane < n16)
-                            __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(sp + k + lane), (FI_SHARED void*)(sd + k), 16, 0, 0);
-                }
-                if (stage_x) {
-                    for (int k = 0; k < Un - kBlk; k += kWave)
-                        __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(row + (inext - Un) + k + lane),
-                                                         (FI_SHARED void*)(xst + k), 4, 0, 0);
                 }
                 // The accumulators of the next block's positions, from the row:
                 // some earlier tile left them outside its ring exactly when a bit
@@ -1439,10 +1535,16 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     for (int k = 0; k < kRegs; ++k) ta[k][0] = tz0[kWave * k];
                     float v = 0.f;
 #pragma unroll
-                    for (int k = 0; k < kRegs; ++k) p[k] *= kTanhScale;
+                    for (int k = 0; k < kRegs; ++k) {
+                        if constexpr (RPUSH) p[k] = __builtin_fmaf(p[k], kTanhScale, s_pre[kWave * k + lane]);
+                        else p[k] *= kTanhScale;
+                    }
                     v = readlane(p[0], 0);
                     if (bnd) xcur = readlane(xb[0], 0);   // x[t0] is given
-                    xstart = xcur;
+                    // the block's first input as recorded: the given x[0], or
+                    // 1 - 2 r as the previous block's recomputation forms it
+                    if constexpr (RPUSH) xstart = t0 == 0 ? xcur : __builtin_fmaf(-2.0f, rcur, 1.0f);
+                    else xstart = xcur;
                     // one 64-step segment of the chain (steps 64K .. 64K+63);
                     // BND: inputs below P come from xb instead of the feedback
                     auto segment = [&](auto kc, auto bndc) {
@@ -1465,8 +1567,16 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                             // c y = v + c h[0] x, exp2, add, rcp, x = 1 - 2 r.  Position
                             // m's own lag-0 push is the same fma as c y, so its register
                             // ends equal to it.
-                            const float xm = CLOSED ? xcur : readlane(xb[K], m2);
+                            // RPUSH: the pushed value is r of the previous position
+                            // (x = 1 - 2 r), the taps are -2 c h, and the serial path
+                            // is c y = v + (-2 c h[0]) r, exp2, add, rcp
+                            const float xm = RPUSH ? rcur : CLOSED ? xcur : readlane(xb[K], m2);
                             const float cy = __builtin_fmaf(ch0v, xm, v);
+                            // the exponential goes first; the read of the next
+                            // accumulator (a scalar register) then sits two
+                            // instructions before its use, clear of the wait
+                            // states a scalar written by the vector unit needs
+                            [[maybe_unused]] const float ey = CLOSED ? __builtin_amdgcn_exp2f(cy) : 0.f;
 #pragma unroll
                             for (int k = K; k < kRegs; ++k) {
                                 p[k] = __builtin_fmaf(tv[k], xm, p[k]);
@@ -1481,8 +1591,15 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                             }
                             if constexpr (CLOSED) {
                                 if (m + 1 < kBlk) v = readlane(p[(m + 1) / kWave], (m + 1) % kWave);
-                                xcur = __builtin_fmaf(-2.0f, tanh_rcp_scaled(cy), 1.0f);
-                                if constexpr (BF16) xcur = round_bf16(xcur);
+                                __builtin_amdgcn_sched_barrier(0);
+                                // r = 1 / (1 + 2^(c y)), tanh(y) = 1 - 2 r
+                                const float rr = __builtin_amdgcn_rcpf(1.0f + ey);
+                                if constexpr (RPUSH) {
+                                    rcur = rr;
+                                } else {
+                                    xcur = __builtin_fmaf(-2.0f, rr, 1.0f);
+                                    if constexpr (BF16) xcur = round_bf16(xcur);
+                                }
                                 if constexpr (BND) {
                                     if (m + 1 < kBlk && m + 1 < pl)
                                         xcur = readlane(xb[(m + 1) / kWave], (m + 1) % kWave);
@@ -1491,11 +1608,23 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     };
+                    auto timed = [&](auto kc, auto bndc) {
+                        [[maybe_unused]] unsigned long long ts = 0;
+                        if constexpr (kProfile) {
+                            ts = clock64();
+                            if (decltype(kc)::value == 0) pf_s0 = ts;
+                        }
+                        segment(kc, bndc);
+                        if constexpr (kProfile) {
+                            pf_s1 = clock64();
+                            pf_seg[decltype(kc)::value] += pf_s1 - ts;
+                        }
+                    };
                     if constexpr (PROMPT) {
-                        if (bnd) for_segments<0>([&](auto kc) { segment(kc, std::true_type{}); });
-                        else for_segments<0>([&](auto kc) { segment(kc, std::false_type{}); });
+                        if (bnd) for_segments<0>([&](auto kc) { timed(kc, std::true_type{}); });
+                        else for_segments<0>([&](auto kc) { timed(kc, std::false_type{}); });
                     } else {
-                        for_segments<0>([&](auto kc) { segment(kc, std::false_type{}); });
+                        for_segments<0>([&](auto kc) { timed(kc, std::false_type{}); });
                     }
                 }
                 if (openb) {
@@ -1524,44 +1653,69 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 // issued a whole chain ago: wait for it here, before the stores
                 // below (stores count in the same counter, and their
                 // acknowledgement is not needed before the tile).
+                [[maybe_unused]] unsigned long long pf_w0 = 0;
+                if constexpr (kProfile) pf_w0 = clock64();
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                if constexpr (kProfile) {
+                    pf_tw = clock64();
+                    pf_vm += pf_tw - pf_w0;
+                }
                 // p now holds y of the block (lane m's accumulator stopped
                 // changing at step m: later pushes carry a zero tap there)
 #pragma unroll
-                for (int k = 0; k < kRegs; ++k) {
-                    const int64_t tl = t0 + kWave * k + lane;
-                    if (direct) xring[tl & xmask] = xk[k];
-                    if (stage_x) xst[Un - kBlk + kWave * k + lane] = xk[k];   // completes the staged input block
-                    if (mm_next) {
+                for (int k = 0; k < kRegs; ++k) accw[kWave * k + lane] = nx[k];   // the ring now holds the next block
+                if (direct) {
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) xring[(t0 + kWave * k + lane) & xmask] = xk[k];
+                }
+                if (stage_x) {   // completes the staged input block
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) xst[Un - kBlk + kWave * k + lane] = xk[k];
+                }
+                if (row_input) {
+                    // the next tile reads its input block from the row, and
+                    // its transform reaches the LDS copies: store it all now
+                    store_block();
+                } else {
+                    // the matrix-core tile's input and what the next block
+                    // stores; the input history (the slot of a consumed
+                    // accumulator now holds x), read by later tiles
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) {
                         mxz[15 + kWave * k + lane] = xk[k];
                         myb[kWave * k + lane] = p[k];
                     }
-                    accw[(kWave * k + lane) & wmask] = nx[k];  // slot of position t now holds position t + W
+                    FI_GLOBAL float* rb = row + t0;
+                    if (t0 + kBlk <= L) {
+#pragma unroll
+                        for (int k = 0; k < kRegs; ++k) rb[kWave * k + lane] = xk[k];
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < kRegs; ++k)
+                            if (t0 + kWave * k + lane < L) rb[kWave * k + lane] = xk[k];
+                    }
                 }
-                if (row_input) store_block();
                 __builtin_amdgcn_s_setprio(0);
             }
             // the whole team sees the block's LDS writes and its stores
+            if constexpr (kProfile) pf_tc = clock64();
             team_sync_global();
+            if constexpr (kProfile) {
+                pf_td = clock64();
+                pf_chain += pf_tc - pf_tb;
+                pf_wait += pf_td - pf_tc;
+                if (pf_s0 > pf_tb) {   // the block ran a chain
+                    pf_pro += pf_s0 - pf_tb;
+                    pf_epi += pf_tc - pf_s1;
+                }
+            }
             const int64_t i = t0 + kBlk;
             if (i < L) {
                 const int U = (int)(i & -i);
                 if (U <= d.T) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
                 } else if (U == kBlk) {
-                    if (!chain_wave) {
-                        static_assert(kTeamWaves == 2, "one wavefront stores the block");
-#pragma unroll
-                        for (int k = 0; k < kRegs; ++k) {
-                            const int64_t tl = t0 + kWave * k + lane;   // < i < L
-                            const int64_t o = (b * L + tl) * D + c;
-                            const float xv = mxz[15 + kWave * k + lane];
-                            yout[o] = myb[kWave * k + lane];
-                            if (a.x_out) store_io<BF16>(a.x_out, o, xv);
-                            row[tl] = xv;
-                        }
-                    }
-                    mm_tile256(mxz, mhs, accw);
+                    mm_tile256(mxz, mhs, accw, reinterpret_cast<FI_SHARED float*>(lbuf));
                 } else {
                     const int q = ilog2(U);
                     const FI_GLOBAL V2* spec =
@@ -1570,7 +1724,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                              stage_x, xst, stage_spec, sst);
                     // the transform buffer reached the matrix-core tile's data
                     // and the tap table: rebuild them
-                    if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > d.mm_off) {
+                    if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > kRunMmOff) {
                         team_sync();
                         if (lds_fft_elems(U < kLdsFftMax ? U : kLdsFftMax) * 8 > t4_off) build_taps4(hrow, open_block(i));
                         build_mm(hrow);
@@ -1592,7 +1746,68 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     }
                 }
             }
-            if (chain_wave && !row_input && !mm_next) store_block();
+            if constexpr (kProfile) {
+                pf_te = clock64();
+                if (i < L && chain_wave && lane == 0) {
+                    const int q = ilog2(i & -i);
+                    s_pf[q] += pf_te - pf_td;
+                    s_pf[24 + q] += 1;
+                }
+            }
+            defer_prev = !row_input;
+            if constexpr (kProfile) {
+                const unsigned long long tf = clock64();
+                pf_store += tf - pf_te;
+                // the first team's first channel: the block's timeline
+                if (bid == 0 && ch == ch0 && chain_wave && lane == 0 && d.prof) {
+                    unsigned long long* o =
+                        d.prof + kProfHeader + (int64_t)G * kProfSlots + (t0 / kBlk) * kProfSeriesW;
+                    o[0] = pf_tb;
+                    o[1] = pf_s0;
+                    o[2] = pf_s1;
+                    o[3] = pf_tw;
+                    o[4] = pf_tc;
+                    o[5] = pf_td;
+                    o[6] = pf_te;
+                    o[7] = tf;
+                }
+            }
+        }
+        // the last block's outputs (no block follows it)
+        if (chain_wave && defer_prev) store_deferred((L - 1) / kBlk * kBlk);
+    }
+    if constexpr (kProfile) {
+        const unsigned long long total = clock64() - pf_t0;
+        team_sync();
+        if (chain_wave && lane == 0 && d.prof) {
+            unsigned long long* o = d.prof + kProfHeader + (int64_t)bid * kProfSlots;
+            for (int k = 0; k < kProfSlots; ++k) o[k] = 0;
+            unsigned long long segs = 0;
+#pragma unroll
+            for (int k = 0; k < kRegs; ++k) {
+                o[kPfSeg + k] = pf_seg[k];
+                segs += pf_seg[k];
+            }
+            o[kPfTotal] = total;
+            o[kPfSetup] = pf_setup;
+            o[kPfChainRest] = pf_chain - segs;
+            o[kPfWait] = pf_wait;
+            o[kPfStore] = pf_store;
+            o[kPfBlocks] = pf_blocks;
+            o[kPfChannels] = pf_chans;
+            o[kPfPrologue] = pf_pro;
+            o[kPfEpilogue] = pf_epi;
+            o[kPfLoadWait] = pf_vm;
+            for (int q = 0; q < 24; ++q) {
+                o[kPfTile + q] = s_pf[q];
+                o[kPfTileCount + q] = s_pf[24 + q];
+            }
+            if (bid == 0) {
+                d.prof[0] = (unsigned long long)G;
+                d.prof[1] = kProfSlots;
+                d.prof[2] = (unsigned long long)((L + kBlk - 1) / kBlk);
+                d.prof[3] = 0;
+            }
         }
     }
 }
@@ -1629,6 +1844,11 @@ hipError_t launch_spectra(const DevState& d, int q, void* scd, int64_t scd_strid
     V2* spec = static_cast<V2*>(d.spec) + d.spec_off[q];
     hipLaunchKernelGGL(k_spectra, dim3(grid), dim3(kTeam), lds, st, d.hT, d.LS, d.L, d.D, M, spec,
                        static_cast<Cx<double>*>(scd), scd_stride, static_cast<const Cx<double>*>(twd));
+    return hipGetLastError();
+}
+
+hipError_t launch_prefix(const DevState& d, hipStream_t st) {
+    hipLaunchKernelGGL(k_prefix, dim3(grid_for(d.D, 256, 1 << 30)), dim3(256), 0, st, d.hT, d.LS, d.L, d.D, d.pre);
     return hipGetLastError();
 }
 
