@@ -18,7 +18,8 @@ __all__ = [
     "FI_F32", "FI_BF16", "FI_FEEDBACK_NONE", "FI_FEEDBACK_TANH",
     "FI_OK", "FI_ERR_INVALID", "FI_ERR_NOMEM", "FI_ERR_HIP", "FI_ERR_STATE", "FI_ERR_UNSUPPORTED",
     "FiError", "fi_config", "fi_tile", "fi_create", "fi_step", "fi_run_closed_loop", "fi_reset",
-    "fi_destroy", "fi_position", "fi_strerror", "fi_tile_at", "fi_run_prompted", "Mixer", "EXPORTS", "lib",
+    "fi_destroy", "fi_position", "fi_strerror", "fi_tile_at", "fi_run_prompted", "fi_conv_static", "Mixer",
+    "EXPORTS", "lib",
     "LIB_PATH",
 ]
 
@@ -48,7 +49,8 @@ lib = ctypes.CDLL(str(LIB_PATH))
 
 # every symbol include/fi.h declares
 EXPORTS = ("fi_create", "fi_step", "fi_run_closed_loop", "fi_run_prompted", "fi_reset", "fi_destroy",
-           "fi_position", "fi_strerror", "fi_tile_at")
+           "fi_position", "fi_strerror", "fi_tile_at", "fi_conv_static")
+FI_STATIC_WORKSPACE_BYTES = 64 << 20
 
 
 class fi_config(ctypes.Structure):
@@ -82,6 +84,9 @@ lib.fi_strerror.argtypes = [ctypes.c_int]
 lib.fi_strerror.restype = ctypes.c_char_p
 lib.fi_tile_at.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(fi_tile)]
 lib.fi_tile_at.restype = ctypes.c_int
+lib.fi_conv_static.argtypes = [ctypes.POINTER(fi_config), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                               ctypes.c_void_p, ctypes.c_void_p]
+lib.fi_conv_static.restype = ctypes.c_int
 # only in the phase-timing build (include/fi_profile.h)
 HAS_PROFILE = hasattr(lib, "fi_profile_read")
 if HAS_PROFILE:
@@ -156,6 +161,12 @@ def fi_tile_at(L: int, i: int) -> fi_tile:
     t = fi_tile()
     _check(lib.fi_tile_at(int(L), int(i), ctypes.byref(t)), "fi_tile_at")
     return t
+
+
+def fi_conv_static(cfg: fi_config, h, x_in, fb: int, y, x_out=None) -> None:
+    """The no-allocation one-shot run (fixed per-device workspace)."""
+    _check(lib.fi_conv_static(ctypes.byref(cfg), _ptr(h), _ptr(x_in), int(fb), _ptr(y), _ptr(x_out)),
+           "fi_conv_static")
 
 
 def fi_profile_read(s: int):

@@ -81,9 +81,17 @@ hipError_t dalloc(T **p, size_t bytes) {
     return e;
 }
 
-int build(fi_handle *s, const void *h) {
+// Sizes of a handle's device buffers (bytes) and its persistent-pass grid.
+struct Plan {
+    size_t hT, pre, state, spec, twf, scratch, twd, scd, prof;
+    int smax;            // twiddle tables up to 2^smax points
+    int64_t scd_slots;   // fp64 spectrum scratch slots (levels above LDS only)
+};
+
+// Fills the layout fields of s->d (levels, spectra offsets, grid, scratch
+// slots) and the buffer sizes; no device memory is touched.
+int plan(fi_handle *s, Plan &pl) {
     DevState &d = s->d;
-    hipStream_t st = s->stream;
     const int64_t umax = max_tile(d.L);
     // FFT levels: T < U <= umax
     int64_t spec_total = 0;
@@ -102,15 +110,16 @@ int build(fi_handle *s, const void *h) {
     // the persistent pass's LDS FFT / staging region has a fixed layout
     d.mm_off = fi::kRunMmOff;
     d.fftreg = fi::kRunFftReg;
-
-    FI_HIP(dalloc(&d.hT, (size_t)(d.D * d.LS) * sizeof(float)));
-    FI_HIP(dalloc(&d.pre, (size_t)(d.D * fi::kRunBlock) * sizeof(float)));
-    FI_HIP(dalloc(&d.state, (size_t)(d.C * d.LS) * sizeof(float)));
-    FI_HIP(dalloc(&d.spec, (size_t)(spec_total > 0 ? spec_total : 1) * 8));
     // twiddles up to 2 umax points (the untangle of the largest tiles uses
     // w_2U^k)
     smax += 1;
-    FI_HIP(dalloc(&d.twf, (size_t)((int64_t)2 << smax) * 8));
+    pl.smax = smax;
+    pl.hT = (size_t)(d.D * d.LS) * sizeof(float);
+    pl.pre = (size_t)(d.D * fi::kRunBlock) * sizeof(float);
+    pl.state = (size_t)(d.C * d.LS) * sizeof(float);
+    pl.spec = (size_t)(spec_total > 0 ? spec_total : 1) * 8;
+    pl.twf = (size_t)((int64_t)2 << smax) * 8;
+    pl.twd = (size_t)((int64_t)2 << smax) * 16;
 
     // persistent-pass grid: every resident wavefront slot, at most one per channel
     int dev = 0, ncu = 0;
@@ -130,27 +139,52 @@ int build(fi_handle *s, const void *h) {
     // tile kernel
     d.sc_slots = slots;
     d.sc_stride = d.umax_fft > fi::kLdsFftMax ? d.umax_fft : 0;
-    if (d.sc_stride > 0) FI_HIP(dalloc(&d.scratch, (size_t)(slots * d.sc_stride) * 8));
+    pl.scratch = (size_t)(slots * d.sc_stride) * 8;
+    pl.scd_slots = d.D < 1024 ? d.D : 1024;
+    pl.scd = d.umax_fft > fi::kLdsFftMax ? (size_t)(pl.scd_slots * d.umax_fft) * 16 : 0;
+    pl.prof = 0;
     if (fi::kProfile) {
         // header, one slot row per team of the largest grid, one entry per block
         d.prof_n = fi::kProfHeader + slots * fi::kProfSlots +
                    ((d.L + fi::kRunBlock - 1) / fi::kRunBlock) * fi::kProfSeriesW;
-        FI_HIP(dalloc(&d.prof, (size_t)d.prof_n * 8));
-        FI_HIP(hipMemsetAsync(d.prof, 0, (size_t)d.prof_n * 8, st));
+        pl.prof = (size_t)d.prof_n * 8;
     }
+    return FI_OK;
+}
 
-    FI_HIP(fi::launch_transpose(d, h, st));
-    FI_HIP(fi::launch_prefix(d, st));
-    void *twd = nullptr;
-    FI_HIP(dalloc(&twd, (size_t)((int64_t)2 << smax) * 16));
-    hipError_t e = fi::launch_twiddles(twd, d.twf, smax, st);
-    void *scd = nullptr;
-    int64_t scd_slots = d.D < 1024 ? d.D : 1024;
-    if (e == hipSuccess && d.umax_fft > fi::kLdsFftMax)
-        e = dalloc(&scd, (size_t)(scd_slots * d.umax_fft) * 16);
+// The one-time precompute on the stream: filter rows, tap prefix sums,
+// twiddles, per-level spectra, and zeroed accumulator rows.
+hipError_t init_state(const DevState &d, const Plan &pl, const void *h, void *twd, void *scd, hipStream_t st) {
+    hipError_t e = fi::launch_transpose(d, h, st);
+    if (e == hipSuccess) e = fi::launch_prefix(d, st);
+    if (e == hipSuccess) e = fi::launch_twiddles(twd, d.twf, pl.smax, st);
     for (int q = 0; e == hipSuccess && q < fi::kMaxLevels; ++q)
-        if (d.spec_off[q] >= 0) e = fi::launch_spectra(d, q, scd, d.umax_fft, scd_slots, twd, st);
+        if (d.spec_off[q] >= 0) e = fi::launch_spectra(d, q, scd, d.umax_fft, pl.scd_slots, twd, st);
     if (e == hipSuccess) e = fi::launch_zero(d.state, d.C * d.LS, st);
+    return e;
+}
+
+int build(fi_handle *s, const void *h) {
+    DevState &d = s->d;
+    hipStream_t st = s->stream;
+    Plan pl;
+    const int rc = plan(s, pl);
+    if (rc != FI_OK) return rc;
+    FI_HIP(dalloc(&d.hT, pl.hT));
+    FI_HIP(dalloc(&d.pre, pl.pre));
+    FI_HIP(dalloc(&d.state, pl.state));
+    FI_HIP(dalloc(&d.spec, pl.spec));
+    FI_HIP(dalloc(&d.twf, pl.twf));
+    if (pl.scratch > 0) FI_HIP(dalloc(&d.scratch, pl.scratch));
+    if (pl.prof > 0) {
+        FI_HIP(dalloc(&d.prof, pl.prof));
+        FI_HIP(hipMemsetAsync(d.prof, 0, pl.prof, st));
+    }
+    void *twd = nullptr, *scd = nullptr;
+    FI_HIP(dalloc(&twd, pl.twd));
+    hipError_t e = hipSuccess;
+    if (pl.scd > 0) e = dalloc(&scd, pl.scd);
+    if (e == hipSuccess) e = init_state(d, pl, h, twd, scd, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (scd) (void)hipFree(scd);
     (void)hipFree(twd);
@@ -158,13 +192,9 @@ int build(fi_handle *s, const void *h) {
     return FI_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
-    if (out) *out = nullptr;
-    if (!cfg || !h || !out) return FI_ERR_INVALID;
+// Validation shared by fi_create and fi_conv_static; fills the handle's
+// configuration fields.
+int configure(const fi_config *cfg, fi_handle *s) {
     if (cfg->B < 1 || cfg->D < 1 || cfg->L < 1) return FI_ERR_INVALID;
     const int dt = static_cast<int>(cfg->io_dtype);   // the caller may store any int there
     if (dt != FI_F32 && dt != FI_BF16) return FI_ERR_INVALID;
@@ -190,8 +220,6 @@ int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
         return FI_ERR_HIP;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FI_ERR_UNSUPPORTED;
 
-    fi_handle *s = new (std::nothrow) fi_handle();
-    if (!s) return FI_ERR_NOMEM;
     std::memset(&s->d, 0, sizeof(s->d));
     DevState &d = s->d;
     d.B = cfg->B;
@@ -206,10 +234,27 @@ int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
     s->stream = static_cast<hipStream_t>(cfg->stream);
     s->pos = 0;
     s->dirty = 0;
-    int rc = build(s, h);
+    return FI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fi_create(const fi_config *cfg, const void *h, fi_handle **out) {
+    if (out) *out = nullptr;
+    if (!cfg || !h || !out) return FI_ERR_INVALID;
+    fi_handle *s = new (std::nothrow) fi_handle();
+    if (!s) return FI_ERR_NOMEM;
+    int rc = configure(cfg, s);
+    if (rc != FI_OK) {
+        delete s;
+        return rc;
+    }
+    rc = build(s, h);
     if (rc != FI_OK) {
         (void)hipStreamSynchronize(s->stream);
-        free_state(d);
+        free_state(s->d);
         delete s;
         return rc;
     }
@@ -263,6 +308,45 @@ int fi_run_prompted(fi_handle *s, const void *x_prompt, int64_t p, float *y, voi
     return FI_OK;
 }
 
+int fi_conv_static(const fi_config *cfg, const void *h, const void *x_in, fi_feedback fb, float *y,
+                   void *x_out) {
+    if (!cfg || !h || !x_in || !y) return FI_ERR_INVALID;
+    const int fbv = static_cast<int>(fb);   // the caller may pass any int
+    if (fbv != FI_FEEDBACK_NONE && fbv != FI_FEEDBACK_TANH) return FI_ERR_INVALID;
+    fi_handle s;   // host-side only: its device buffers are carved from the workspace
+    int rc = configure(cfg, &s);
+    if (rc != FI_OK) return rc;
+    Plan pl;
+    rc = plan(&s, pl);
+    if (rc != FI_OK) return rc;
+    DevState &d = s.d;
+    // carve every buffer, 256-byte aligned, out of the device's workspace
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) / 256 * 256;
+        return o;
+    };
+    const size_t o_hT = take(pl.hT), o_pre = take(pl.pre), o_state = take(pl.state), o_spec = take(pl.spec),
+                 o_twf = take(pl.twf), o_sc = take(pl.scratch), o_twd = take(pl.twd), o_scd = take(pl.scd);
+    void *base = nullptr;
+    size_t cap = 0;
+    FI_HIP(fi::static_scratch(&base, &cap));
+    if (off > cap) return FI_ERR_UNSUPPORTED;   // beyond FI_STATIC_WORKSPACE_BYTES
+    char *b = static_cast<char *>(base);
+    d.hT = reinterpret_cast<float *>(b + o_hT);
+    d.pre = reinterpret_cast<float *>(b + o_pre);
+    d.state = reinterpret_cast<float *>(b + o_state);
+    d.spec = b + o_spec;
+    d.twf = b + o_twf;
+    d.scratch = pl.scratch > 0 ? b + o_sc : nullptr;
+    d.prof = nullptr;
+    FI_HIP(init_state(d, pl, h, b + o_twd, pl.scd > 0 ? b + o_scd : nullptr, s.stream));
+    const int mode = fbv == FI_FEEDBACK_TANH ? fi::kRunClosed : fi::kRunOpen;
+    FI_HIP(fi::launch_run(d, x_in, mode, 0, y, x_out, s.run_grid[mode], s.stream));
+    return FI_OK;
+}
+
 int fi_reset(fi_handle *s) {
     if (!s) return FI_ERR_INVALID;
     s->pos = 0;
@@ -285,7 +369,9 @@ const char *fi_strerror(int status) {
         case FI_ERR_INVALID: return "invalid argument";
         case FI_ERR_NOMEM: return "device out of memory";
         case FI_ERR_STATE: return "call not allowed at the handle's position";
-        case FI_ERR_UNSUPPORTED: return "unsupported (needs a gfx950 device)";
+        case FI_ERR_UNSUPPORTED:
+            return "unsupported (needs a gfx950 device; L <= FI_MAX_L; for fi_conv_static, buffers within "
+                   "FI_STATIC_WORKSPACE_BYTES)";
         case FI_ERR_HIP:
             std::snprintf(g_errbuf, sizeof g_errbuf, "HIP error: %s", hipGetErrorString(g_last_hip));
             return g_errbuf;

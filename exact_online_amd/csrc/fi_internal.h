@@ -103,6 +103,11 @@ struct DevState {
     int64_t prof_n;             // its length in elements
 };
 
+// The fixed device workspace of fi_conv_static (per device, never freed):
+// its device address on the current device, looked up once per device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch(void **ptr, size_t *bytes);
+
 // fi_create helpers (synchronous work on `st`)
 hipError_t launch_transpose(const DevState &d, const void *h, hipStream_t st);
 hipError_t launch_twiddles(void *twd, void *twf, int smax, hipStream_t st);

@@ -19,6 +19,7 @@
 //       two wavefronts per channel; no grid-wide synchronisation is ever
 //       needed because channels are independent ([FI] "Definizione
 //       Specifica di LCSM": the mixer is a per-channel Hadamard convolution).
+#include <mutex>
 #include <type_traits>
 
 #include "fi_device.hpp"
@@ -1810,6 +1811,34 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             }
         }
     }
+}
+
+// ======================================================= static workspace
+// The device memory of fi_conv_static, the entry point for callers that
+// cannot allocate: one fixed array per device, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in for the symbol): it looks up the device address once per device
+// and hands that out.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr, size_t* bytes) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* per_device[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    *bytes = kStaticScratchBytes;
+    return hipSuccess;
 }
 
 // ================================================================ launchers

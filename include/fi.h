@@ -144,6 +144,31 @@ int fi_run_closed_loop(fi_handle *s, const void *x_in, fi_feedback fb, float *y,
  */
 int fi_run_prompted(fi_handle *s, const void *x_prompt, int64_t p, float *y, void *x_out);
 
+/*
+ * fi_conv_static: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fi_create + fi_run_closed_loop + fi_destroy in one call that allocates
+ * nothing.  Same arguments and results as those calls: cfg, h[L][D]
+ * (io_dtype) as for fi_create; x_in, fb, y, x_out as for fi_run_closed_loop.
+ * The handle's device buffers (filter rows, accumulator rows, spectra,
+ * twiddles, FFT scratch) are carved from one fixed workspace of
+ * FI_STATIC_WORKSPACE_BYTES per device, a static device array the library
+ * holds until the process ends; no hipMalloc, hipFree or other allocating
+ * call is made.  Their size is about 4 LS (D + B D) + 8 D L bytes (LS = L
+ * rounded up to 64) plus twiddle tables and, when L > 8192, FFT scratch of
+ * 8 * min(B D, resident teams) * (largest tile side) bytes; larger problems
+ * get FI_ERR_UNSUPPORTED and nothing is launched.  Asynchronous on
+ * cfg->stream (nothing is synchronised): the caller keeps h, x_in, y and
+ * x_out valid until the stream has passed the call.  Every call on a device
+ * uses that device's one workspace: calls that overlap on one device (on
+ * different streams, or from different threads) race and give undefined
+ * results; calls in order on one stream are safe.  Errors as fi_create and
+ * fi_run_closed_loop (FI_ERR_INVALID, FI_ERR_UNSUPPORTED, FI_ERR_HIP).
+ */
+#define FI_STATIC_WORKSPACE_BYTES (64LL << 20)
+int fi_conv_static(const fi_config *cfg, const void *h, const void *x_in, fi_feedback fb, float *y,
+                   void *x_out);
+
 /* fi_reset: position := 0; the accumulators are cleared on the stream before
  * the next fi_step (fi_run_closed_loop clears the rows it uses itself). */
 int fi_reset(fi_handle *s);
