@@ -47,6 +47,8 @@ def _bind(lib):
     lib.fio_points.restype = None
     lib.fio_round_bf16.argtypes = [ctypes.c_double]
     lib.fio_round_bf16.restype = ctypes.c_double
+    lib.fio_stack.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, dp, ctypes.c_double, ip, ip, dp, dp, ip]
+    lib.fio_stack.restype = None
     lib.fio_mutant.argtypes = []
     lib.fio_mutant.restype = ctypes.c_int
     return lib
@@ -149,6 +151,44 @@ class Oracle:
                             ts.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(y))
         return y
 
+    ACTS = {"gelu": 0, "tanh": 1, "identity": 2}
+
+    def conv_stack(self, rho, w1, w2, x, noise=None, sigma: float = 0.0, act: str = "gelu",
+                   teacher_forced: bool = False):
+        """The multi-layer stack (page "Flash Inference: Inferenza in Tempo
+        Quasi-Lineare per Modelli di Sequenza a Convoluzione Lunga e Oltre",
+        sections "Algoritmo di Inferenza LCSM (Algoritmo 2)" and
+        "Configurazione Sperimentale": MLP + GELU blocks, a sampler adding
+        noise).  rho[M][L][D], w1 and w2 [M][D][D] (row j = output j).
+        teacher_forced: x[B][L][D] is the whole input sequence; otherwise
+        x[B][D] (or x[B][L][D] with only x[:, 0] read) starts the feedback
+        x[t+1] = a^M[t] + sigma noise[t].  Returns (y = a^M [B][L][D], x
+        [B][L][D]) in fp64."""
+        rho = _f64(rho)
+        w1 = _f64(w1)
+        w2 = _f64(w2)
+        M, L, D = rho.shape
+        assert w1.shape == (M, D, D) and w2.shape == (M, D, D)
+        x = _f64(x)
+        if x.ndim == 2:
+            B = x.shape[0]
+            xx = np.zeros((B, L, D))
+            xx[:, 0, :] = x
+        else:
+            B = x.shape[0]
+            assert x.shape == (B, L, D)
+            xx = x.copy()
+        nz = None
+        if noise is not None:
+            nz = _f64(noise)
+            assert nz.shape == (B, L, D)
+        y = np.empty((B, L, D))
+        work = np.empty(B * ((M + 1) * L * D + 2 * D))
+        self.lib.fio_stack(B, D, L, M, _p(rho), _p(w1), _p(w2), _p(xx),
+                           _p(nz) if nz is not None else None, float(sigma), self.ACTS[act],
+                           int(bool(teacher_forced)), _p(y), _p(work), self.threads)
+        return y, xx
+
     def round_bf16(self, v) -> np.ndarray:
         v = np.asarray(v, dtype=np.float64)
         return np.vectorize(self.lib.fio_round_bf16, otypes=[np.float64])(v)
@@ -186,3 +226,7 @@ def conv_points(h_col, x_col, ts):
 
 def round_bf16(v):
     return default().round_bf16(v)
+
+
+def conv_stack(rho, w1, w2, x, noise=None, sigma=0.0, act="gelu", teacher_forced=False):
+    return default().conv_stack(rho, w1, w2, x, noise, sigma, act, teacher_forced)

@@ -33,7 +33,7 @@
  * loop and p = L the open loop.
  *
  * Mutation hooks: building with -DFIO_MUTANT=k plants one deliberate mistake
- * (k = 1..7, listed at each hook).  The test suite builds every mutant on the
+ * (k = 1..12, listed at each hook; 8..12 are in the multi-layer stack).  The test suite builds every mutant on the
  * CPU and checks that each one fails at least one pin; the normal build never
  * defines FIO_MUTANT.
  */
@@ -175,6 +175,119 @@ void fio_points(int64_t L, const double *h, const double *x, int64_t n,
             for (int64_t s = 0; s <= tk; ++s) acc += h[tk - s] * x[s];
         y[k] = acc;
     }
+}
+
+/* ------------------------------------------------------------------ stack
+ * The multi-layer LCSM of [FI] "Algoritmo di Inferenza LCSM (Algoritmo 2)"
+ * and "Architettura del Modello" (a_i of layer l = block_l(mixer_l(a of layer
+ * l-1)_i)), with the synthetic blocks of [FI] "Configurazione Sperimentale"
+ * (MLP + GELU) and a sampler that adds given noise, 0-indexed: layers
+ * l = 0..M-1, a^0 = x (the stack's input sequence), and for every position t
+ *
+ *   z^l_t[c]   = sum_{s=0}^{t} rho^l[t-s][c] * a^l_s[c]         (the mixer)
+ *   a^{l+1}_t  = W2^l act(W1^l z^l_t)                           (the block)
+ *   x_{t+1}    = a^M_t + sigma * noise[t]                       (the sampler)
+ *
+ * act(v) = GELU(v) = v (1 + erf(v / sqrt 2)) / 2 (act_kind 0), tanh (1) or
+ * the identity (2); W1^l, W2^l are D x D, row j holding the weights of
+ * output j.  teacher_forced != 0: x is given at every position and only y is
+ * computed; otherwise x[0] is given and the rest is fed back.  Layouts:
+ * rho[M][L][D], w1 and w2 [M][D][D], x, noise (or NULL), y [B][L][D]; y
+ * receives a^M.  Plain fp64, every sum in ascending index. */
+static double act_fn(double v, int kind)
+{
+#if FIO_MUTANT == 11
+    if (kind == 0)   /* mutant 11: the tanh approximation of GELU */
+        return 0.5 * v * (1.0 + tanh(0.7978845608028654 * (v + 0.044715 * v * v * v)));
+#endif
+    if (kind == 0) return 0.5 * v * (1.0 + erf(v / sqrt(2.0)));
+    if (kind == 1) return tanh(v);
+    return v;
+}
+
+static void stack_row(int64_t D, int64_t L, int64_t M, const double *rho, const double *w1,
+                      const double *w2, double *x, const double *noise, double sigma, int act_kind,
+                      int teacher_forced, double *y, double *a /* [M+1][L][D] work */,
+                      double *z /* [D] */, double *hb /* [D] */)
+{
+    for (int64_t t = 0; t < L; ++t) {
+        for (int64_t c = 0; c < D; ++c) a[t * D + c] = x[t * D + c];   /* a^0_t */
+        for (int64_t l = 0; l < M; ++l) {
+#if FIO_MUTANT == 9
+            const double *r = rho;                         /* mutant 9: layer 0's filter everywhere */
+#else
+            const double *r = rho + l * L * D;
+#endif
+            const double *al = a + l * L * D;
+            for (int64_t c = 0; c < D; ++c) {
+                double acc = 0.0;
+                for (int64_t s = 0; s <= t; ++s) acc += r[(t - s) * D + c] * al[s * D + c];
+                z[c] = acc;
+            }
+            const double *W1 = w1 + l * D * D, *W2 = w2 + l * D * D;
+            double *an = a + (l + 1) * L * D + t * D;
+#if FIO_MUTANT == 8
+            /* mutant 8: both products before the activation */
+            for (int64_t j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < D; ++k) acc += W1[j * D + k] * z[k];
+                hb[j] = acc;
+            }
+            for (int64_t j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < D; ++k) acc += W2[j * D + k] * hb[k];
+                an[j] = act_fn(acc, act_kind);
+            }
+#else
+            for (int64_t j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < D; ++k) acc += W1[j * D + k] * z[k];
+                hb[j] = act_fn(acc, act_kind);
+            }
+            for (int64_t j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < D; ++k) acc += W2[j * D + k] * hb[k];
+#if FIO_MUTANT == 12
+                an[j] = z[j];                              /* mutant 12: the next layer reads the mixer output */
+                (void)acc;
+#else
+                an[j] = acc;
+#endif
+            }
+#endif
+        }
+        const double *aM = a + M * L * D + t * D;
+        for (int64_t c = 0; c < D; ++c) y[t * D + c] = aM[c];
+        if (!teacher_forced && t + 1 < L) {
+            for (int64_t c = 0; c < D; ++c) {
+#if FIO_MUTANT == 10
+                const double nz = noise && t + 1 < L ? noise[(t + 1) * D + c] : 0.0;  /* mutant 10: noise of t+1 */
+#else
+                const double nz = noise ? noise[t * D + c] : 0.0;
+#endif
+                x[(t + 1) * D + c] = aM[c] + sigma * nz;
+            }
+        }
+    }
+}
+
+/* The stack over B batch rows (independent; the weights and filters are
+ * shared).  work: [B][(M+1) L D + 2 D] doubles supplied by the caller. */
+void fio_stack(int64_t B, int64_t D, int64_t L, int64_t M, const double *rho, const double *w1,
+               const double *w2, double *x, const double *noise, double sigma, int act_kind,
+               int teacher_forced, double *y, double *work, int nthreads)
+{
+    const int64_t wsz = (M + 1) * L * D + 2 * D;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t b = 0; b < B; ++b) {
+        double *wk = work + b * wsz;
+        stack_row(D, L, M, rho, w1, w2, x + b * L * D, noise ? noise + b * L * D : NULL, sigma, act_kind,
+                  teacher_forced, y + b * L * D, wk, wk + (M + 1) * L * D, wk + (M + 1) * L * D + D);
+    }
+    (void)nthreads;
 }
 
 int fio_mutant(void) { return FIO_MUTANT; }

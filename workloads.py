@@ -159,3 +159,91 @@ def make_x0(w: Workload, B: int | None = None, D: int | None = None) -> np.ndarr
     rng = np.random.default_rng([w.seed, 2])
     x0 = rng.standard_normal((B, D), dtype=np.float32)
     return round_to_bf16(x0) if w.dtype == "bf16" else x0
+
+
+# ---------------------------------------------------------------- the stack
+@dataclasses.dataclass(frozen=True)
+class StackWorkload:
+    """The multi-layer synthetic LCSM of the page's experiments (M layers,
+    each a long-convolution mixer followed by an MLP + GELU block, and a
+    sampler that adds noise).  Recipe, fixed here:
+
+    * layer l's filter ``rho[l][j][c] = N(0,1) exp(-j / tau_c) / sqrt(S_c)``
+      with tau_c log-uniform in ``tau`` per layer and channel and
+      ``S_c = sum_j exp(-2 j / tau_c)`` (so a white input keeps unit
+      variance through the mixer), from ``default_rng([seed, 10, l])``: tau
+      first, then the Gaussians in row chunks;
+    * ``W1[l], W2[l]`` (D x D, row j = output j) ``N(0, 2/D)`` (the usual
+      scale for GELU/ReLU layers, so the blocks neither die out nor blow
+      up) from ``default_rng([seed, 11])`` and ``([seed, 12])``, layer by
+      layer;
+    * ``x0[B][D] ~ N(0,1)`` from ``([seed, 13])``; the sampler's noise
+      ``noise[B][L][D] ~ N(0,1)`` from ``([seed, 14])``, scaled by ``sigma``.
+    All arrays float32."""
+    name: str
+    B: int
+    D: int
+    L: int
+    M: int
+    tau: tuple = (16.0, 4096.0)
+    sigma: float = 0.1
+    seed: int = 0
+
+    def with_(self, **kw) -> "StackWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+STACKS = {
+    # small: every output checkable against the full oracle in seconds
+    "stack-m3-d32-l1k": StackWorkload("stack-m3-d32-l1k", 2, 32, 1024, 3),
+    # the pages' Hyena sweep at its smallest width and depth (M = 18, D = 256)
+    "stack-m18-d256-l16k": StackWorkload("stack-m18-d256-l16k", 1, 256, 16384, 18),
+}
+
+
+def get_stack(name: str) -> StackWorkload:
+    return STACKS[name]
+
+
+def make_stack_filters(w: StackWorkload) -> np.ndarray:
+    """rho[M][L][D] (float32)."""
+    rho = np.empty((w.M, w.L, w.D), dtype=np.float32)
+    lo, hi = w.tau
+    j_all = np.arange(w.L, dtype=np.float64)
+    for l in range(w.M):
+        rng = np.random.default_rng([w.seed, 10, l])
+        taus = np.exp(rng.uniform(math.log(lo), math.log(hi), size=w.D))
+        norm = 1.0 / np.sqrt(np.sum(np.exp(-2.0 * j_all[:, None] / taus[None, :]), axis=0))
+        for r0 in range(0, w.L, _ROWS):
+            r1 = min(w.L, r0 + _ROWS)
+            g = rng.standard_normal((r1 - r0, w.D), dtype=np.float32)
+            env = np.exp(-j_all[r0:r1, None] / taus[None, :]) * norm[None, :]
+            rho[l, r0:r1] = (g.astype(np.float64) * env).astype(np.float32)
+    return rho
+
+
+def make_stack_weights(w: StackWorkload):
+    """(W1[M][D][D], W2[M][D][D]) float32, N(0, 2/D)."""
+    out = []
+    for k in (11, 12):
+        rng = np.random.default_rng([w.seed, k])
+        W = np.empty((w.M, w.D, w.D), dtype=np.float32)
+        for l in range(w.M):
+            W[l] = (rng.standard_normal((w.D, w.D), dtype=np.float32).astype(np.float64)
+                    * math.sqrt(2.0 / w.D)).astype(np.float32)
+        out.append(W)
+    return out[0], out[1]
+
+
+def make_stack_x0(w: StackWorkload) -> np.ndarray:
+    return np.random.default_rng([w.seed, 13]).standard_normal((w.B, w.D), dtype=np.float32)
+
+
+def make_stack_noise(w: StackWorkload) -> np.ndarray:
+    rng = np.random.default_rng([w.seed, 14])
+    nz = np.empty((w.B, w.L, w.D), dtype=np.float32)
+    for b in range(w.B):
+        for r0 in range(0, w.L, _ROWS):
+            r1 = min(w.L, r0 + _ROWS)
+            nz[b, r0:r1] = rng.standard_normal((r1 - r0, w.D), dtype=np.float32)
+    return nz
