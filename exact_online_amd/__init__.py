@@ -19,7 +19,7 @@ __all__ = [
     "FI_OK", "FI_ERR_INVALID", "FI_ERR_NOMEM", "FI_ERR_HIP", "FI_ERR_STATE", "FI_ERR_UNSUPPORTED",
     "FiError", "fi_config", "fi_tile", "fi_create", "fi_step", "fi_run_closed_loop", "fi_reset",
     "fi_destroy", "fi_position", "fi_strerror", "fi_tile_at", "fi_run_prompted", "fi_conv_static", "Mixer",
-    "EXPORTS", "lib",
+    "fi_stack_config", "fi_stack_create", "fi_stack_run", "fi_stack_destroy", "Stack", "EXPORTS", "lib",
     "LIB_PATH",
 ]
 
@@ -49,7 +49,9 @@ lib = ctypes.CDLL(str(LIB_PATH))
 
 # every symbol include/fi.h declares
 EXPORTS = ("fi_create", "fi_step", "fi_run_closed_loop", "fi_run_prompted", "fi_reset", "fi_destroy",
-           "fi_position", "fi_strerror", "fi_tile_at", "fi_conv_static")
+           "fi_position", "fi_strerror", "fi_tile_at", "fi_conv_static", "fi_stack_create", "fi_stack_run",
+           "fi_stack_destroy")
+FI_ACT_GELU, FI_ACT_TANH, FI_ACT_IDENTITY = 0, 1, 2
 FI_STATIC_WORKSPACE_BYTES = 64 << 20
 
 
@@ -58,6 +60,12 @@ class fi_config(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("D", ctypes.c_int64), ("L", ctypes.c_int64),
                 ("io_dtype", ctypes.c_int32), ("stream", ctypes.c_void_p),
                 ("small_tile_max", ctypes.c_int32)]
+
+
+class fi_stack_config(ctypes.Structure):
+    # act is the C enum fi_activation (int-sized)
+    _fields_ = [("B", ctypes.c_int64), ("D", ctypes.c_int64), ("L", ctypes.c_int64), ("M", ctypes.c_int64),
+                ("act", ctypes.c_int32), ("stream", ctypes.c_void_p), ("small_tile_max", ctypes.c_int32)]
 
 
 class fi_tile(ctypes.Structure):
@@ -87,6 +95,13 @@ lib.fi_tile_at.restype = ctypes.c_int
 lib.fi_conv_static.argtypes = [ctypes.POINTER(fi_config), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                ctypes.c_void_p, ctypes.c_void_p]
 lib.fi_conv_static.restype = ctypes.c_int
+lib.fi_stack_create.argtypes = [ctypes.POINTER(fi_stack_config), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.POINTER(_H)]
+lib.fi_stack_create.restype = ctypes.c_int
+lib.fi_stack_run.argtypes = [_H, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+lib.fi_stack_run.restype = ctypes.c_int
+lib.fi_stack_destroy.argtypes = [_H]
+lib.fi_stack_destroy.restype = None
 # only in the phase-timing build (include/fi_profile.h)
 HAS_PROFILE = hasattr(lib, "fi_profile_read")
 if HAS_PROFILE:
@@ -167,6 +182,50 @@ def fi_conv_static(cfg: fi_config, h, x_in, fb: int, y, x_out=None) -> None:
     """The no-allocation one-shot run (fixed per-device workspace)."""
     _check(lib.fi_conv_static(ctypes.byref(cfg), _ptr(h), _ptr(x_in), int(fb), _ptr(y), _ptr(x_out)),
            "fi_conv_static")
+
+
+def fi_stack_create(cfg: fi_stack_config, rho, w1, w2) -> int:
+    out = _H()
+    _check(lib.fi_stack_create(ctypes.byref(cfg), _ptr(rho), _ptr(w1), _ptr(w2), ctypes.byref(out)),
+           "fi_stack_create")
+    return int(out.value)
+
+
+def fi_stack_run(s: int, x0, noise, sigma: float, y, x_out=None) -> None:
+    _check(lib.fi_stack_run(s, _ptr(x0), _ptr(noise), float(sigma), _ptr(y), _ptr(x_out)), "fi_stack_run")
+
+
+def fi_stack_destroy(s) -> None:
+    lib.fi_stack_destroy(s)
+
+
+class Stack:
+    """Owning wrapper of one layer stack (marshalling only)."""
+
+    def __init__(self, B, D, L, M, rho, w1, w2, act=FI_ACT_GELU, small_tile_max=0, stream=None):
+        self.cfg = fi_stack_config(B=int(B), D=int(D), L=int(L), M=int(M), act=int(act), stream=_stream(stream),
+                                   small_tile_max=int(small_tile_max))
+        self.handle = fi_stack_create(self.cfg, rho, w1, w2)
+
+    def run(self, x0, y, x_out=None, noise=None, sigma=0.0):
+        fi_stack_run(self.handle, x0, noise, sigma, y, x_out)
+
+    def close(self):
+        if self.handle:
+            fi_stack_destroy(self.handle)
+            self.handle = 0
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def fi_profile_read(s: int):

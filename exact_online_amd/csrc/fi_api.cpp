@@ -102,7 +102,7 @@ int plan(fi_handle *s, Plan &pl) {
         const int64_t U = (int64_t)1 << q;
         if (U <= d.T) continue;
         d.spec_off[q] = spec_total;
-        spec_total += d.D * (U + 2);
+        spec_total += d.DF * (U + 2);
         d.umax_fft = (int)U;
         smax = q;
     }
@@ -114,7 +114,7 @@ int plan(fi_handle *s, Plan &pl) {
     // w_2U^k)
     smax += 1;
     pl.smax = smax;
-    pl.hT = (size_t)(d.D * d.LS) * sizeof(float);
+    pl.hT = (size_t)(d.DF * d.LS) * sizeof(float);
     pl.pre = (size_t)(d.D * fi::kRunBlock) * sizeof(float);
     pl.state = (size_t)(d.C * d.LS) * sizeof(float);
     pl.spec = (size_t)(spec_total > 0 ? spec_total : 1) * 8;
@@ -140,7 +140,7 @@ int plan(fi_handle *s, Plan &pl) {
     d.sc_slots = slots;
     d.sc_stride = d.umax_fft > fi::kLdsFftMax ? d.umax_fft : 0;
     pl.scratch = (size_t)(slots * d.sc_stride) * 8;
-    pl.scd_slots = d.D < 1024 ? d.D : 1024;
+    pl.scd_slots = d.DF < 1024 ? d.DF : 1024;
     pl.scd = d.umax_fft > fi::kLdsFftMax ? (size_t)(pl.scd_slots * d.umax_fft) * 16 : 0;
     pl.prof = 0;
     if (fi::kProfile) {
@@ -227,6 +227,8 @@ int configure(const fi_config *cfg, fi_handle *s) {
     d.L = cfg->L;
     d.C = C;
     d.LS = LS;
+    d.fset = cfg->B;   // one filter set, shared by every batch row
+    d.DF = cfg->D;
     d.T = T;
     d.W = fi::kRunBlock;        // LDS accumulator ring of the persistent pass: one block
     d.XR = T >= fi::kRunBlock ? T : 0;   // LDS ring of recent inputs, only for its direct tiles
@@ -377,6 +379,129 @@ const char *fi_strerror(int status) {
             return g_errbuf;
         default: return "unknown status";
     }
+}
+
+// ------------------------------------------------------------------ stack
+}  // extern "C"
+
+struct fi_stack {
+    fi_handle h;   // the M B D channels (layer, b, c); filter rows per layer
+    int64_t B, M;
+    int act;
+    float *w1t, *w2t, *xnext;
+};
+
+namespace {
+void free_stack(fi_stack *s) {
+    free_state(s->h.d);
+    if (s->w1t) (void)hipFree(s->w1t);
+    if (s->w2t) (void)hipFree(s->w2t);
+    if (s->xnext) (void)hipFree(s->xnext);
+    s->w1t = s->w2t = s->xnext = nullptr;
+}
+
+int build_stack(fi_stack *s, const float *rho, const float *w1, const float *w2) {
+    DevState &d = s->h.d;
+    hipStream_t st = s->h.stream;
+    Plan pl;
+    int rc = plan(&s->h, pl);
+    if (rc != FI_OK) return rc;
+    FI_HIP(dalloc(&d.hT, pl.hT));
+    FI_HIP(dalloc(&d.pre, pl.pre));
+    FI_HIP(dalloc(&d.state, pl.state));
+    FI_HIP(dalloc(&d.spec, pl.spec));
+    FI_HIP(dalloc(&d.twf, pl.twf));
+    if (pl.scratch > 0) FI_HIP(dalloc(&d.scratch, pl.scratch));
+    const int64_t D = d.D, L = d.L, M = s->M;
+    FI_HIP(dalloc(&s->w1t, (size_t)(M * D * D) * sizeof(float)));
+    FI_HIP(dalloc(&s->w2t, (size_t)(M * D * D) * sizeof(float)));
+    FI_HIP(dalloc(&s->xnext, (size_t)(s->B * D) * sizeof(float)));
+    for (int64_t l = 0; l < M; ++l) {
+        // layer l's filter rows, and its weights with output index innermost
+        FI_HIP(fi::launch_transpose_f32(rho + l * L * D, d.hT + l * D * d.LS, L, D, d.LS, st));
+        FI_HIP(fi::launch_transpose_f32(w1 + l * D * D, s->w1t + l * D * D, D, D, D, st));
+        FI_HIP(fi::launch_transpose_f32(w2 + l * D * D, s->w2t + l * D * D, D, D, D, st));
+    }
+    void *twd = nullptr, *scd = nullptr;
+    FI_HIP(dalloc(&twd, pl.twd));
+    hipError_t e = hipSuccess;
+    if (pl.scd > 0) e = dalloc(&scd, pl.scd);
+    if (e == hipSuccess) e = fi::launch_twiddles(twd, d.twf, pl.smax, st);
+    for (int q = 0; e == hipSuccess && q < fi::kMaxLevels; ++q)
+        if (d.spec_off[q] >= 0) e = fi::launch_spectra(d, q, scd, d.umax_fft, pl.scd_slots, twd, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (scd) (void)hipFree(scd);
+    (void)hipFree(twd);
+    if (e != hipSuccess) return hip_fail(e);
+    return FI_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int fi_stack_create(const fi_stack_config *cfg, const float *rho, const float *w1, const float *w2,
+                    fi_stack **out) {
+    if (out) *out = nullptr;
+    if (!cfg || !rho || !w1 || !w2 || !out) return FI_ERR_INVALID;
+    const int act = static_cast<int>(cfg->act);
+    if (act != FI_ACT_GELU && act != FI_ACT_TANH && act != FI_ACT_IDENTITY) return FI_ERR_INVALID;
+    const int64_t lim = (int64_t)1 << 31;
+    if (cfg->M < 1 || cfg->B < 1 || cfg->M >= lim || cfg->B >= lim || cfg->M > lim / cfg->B) return FI_ERR_INVALID;
+    if (cfg->D > ((int64_t)1 << 16)) return FI_ERR_UNSUPPORTED;   // the blocks' weights: D x D per layer
+    fi_config c;
+    std::memset(&c, 0, sizeof(c));
+    c.B = cfg->M * cfg->B;   // rows (layer, b)
+    c.D = cfg->D;
+    c.L = cfg->L;
+    c.io_dtype = FI_F32;
+    c.stream = cfg->stream;
+    c.small_tile_max = cfg->small_tile_max;
+    fi_stack *s = new (std::nothrow) fi_stack();
+    if (!s) return FI_ERR_NOMEM;
+    int rc = configure(&c, &s->h);
+    if (rc != FI_OK) {
+        delete s;
+        return rc;
+    }
+    s->B = cfg->B;
+    s->M = cfg->M;
+    s->act = act;
+    s->h.d.fset = cfg->B;            // B rows per layer share its filter rows
+    s->h.d.DF = cfg->M * cfg->D;     // filter rows: (layer, c)
+    rc = build_stack(s, rho, w1, w2);
+    if (rc != FI_OK) {
+        (void)hipStreamSynchronize(s->h.stream);
+        free_stack(s);
+        delete s;
+        return rc;
+    }
+    *out = s;
+    return FI_OK;
+}
+
+int fi_stack_run(fi_stack *s, const float *x0, const float *noise, float sigma, float *y, float *x_out) {
+    if (!s || !x0 || !y) return FI_ERR_INVALID;
+    const DevState &d = s->h.d;
+    hipStream_t st = s->h.stream;
+    // the tiles add into the rows: every run starts from cleared rows
+    FI_HIP(fi::launch_zero(d.state, d.C * d.LS, st));
+    for (int64_t t = 0; t < d.L; ++t) {
+        FI_HIP(fi::launch_stack_serial(d, s->B, s->M, s->w1t, s->w2t, x0, noise, sigma, s->act, s->xnext, y,
+                                       x_out, t, st));
+        const int64_t i = t + 1;
+        if (i >= d.L) break;
+        const int64_t U = i & -i;
+        if (U <= d.T) FI_HIP(fi::launch_tile_direct(d, i, (int)U, st));
+        else FI_HIP(fi::launch_tile(d, i, st));
+    }
+    return FI_OK;
+}
+
+void fi_stack_destroy(fi_stack *s) {
+    if (!s) return;
+    (void)hipStreamSynchronize(s->h.stream);
+    free_stack(s);
+    delete s;
 }
 
 int fi_tile_at(int64_t L, int64_t i, fi_tile *out) {

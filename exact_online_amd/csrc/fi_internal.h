@@ -82,6 +82,10 @@ static_assert(lds_fft_elems(1024) * 8 + 4 * 1024 + 8 * (1024 + 2) <= kRunMmOff, 
 //   scratch        [slots][sc_stride] complex fp32 for FFTs larger than LDS
 struct DevState {
     int64_t B, D, L, C, LS;
+    // Channels are (set, b, c): `fset` batch rows share one set of D filter
+    // rows.  The single mixer has one set (fset = B, DF = D); the layer stack
+    // has one per layer (DF = M D filter rows).
+    int64_t fset, DF;
     int T;                 // largest tile side done directly
     int W;                 // LDS accumulator window (positions) of the run kernel
     int XR;                // LDS ring of recent inputs (positions)
@@ -122,6 +126,18 @@ hipError_t launch_tile(const DevState &d, int64_t i, hipStream_t st);   // FFT t
 // the red cell of position t fused with the direct tile of side U <= T that
 // position t+1 completes
 hipError_t launch_step_tile(const DevState &d, int64_t t, const void *x_t, float *y_t, int U, hipStream_t st);
+
+// the layer stack: one position of every layer's red cell and block for
+// every batch row, then the tile all layers' channels need at t + 1
+struct StackArgs;
+hipError_t launch_stack_serial(const DevState &d, int64_t B, int64_t M, const float *w1t, const float *w2t,
+                               const float *x0, const float *noise, float sigma, int act, float *xnext,
+                               float *y, float *x_out, int64_t t, hipStream_t st);
+hipError_t launch_tile_direct(const DevState &d, int64_t i, int U, hipStream_t st);
+// a plain fp32 transpose: dst[c][r] = src[r][c], r < rows, c < cols (row
+// stride of dst: ld >= rows, entries [rows, ld) zeroed)
+hipError_t launch_transpose_f32(const float *src, float *dst, int64_t rows, int64_t cols, int64_t ld,
+                                hipStream_t st);
 
 // the persistent pass over all positions: open loop, closed loop, or a
 // prompt of `prompt` given inputs followed by the closed loop

@@ -1046,7 +1046,8 @@ __global__ __launch_bounds__(kTeam) void k_tile_fft(DevState d, int64_t i, int U
     for (int64_t ch = blockIdx.x; ch < d.C; ch += gridDim.x) {
         FI_GLOBAL float* row = gmem(d.state + ch * d.LS);
         FI_GLOBAL Cx<float>* sc = gmem(static_cast<Cx<float>*>(d.scratch)) + (int64_t)blockIdx.x * d.sc_stride;
-        fft_tile(U, i, row, spec + (ch % d.D) * (int64_t)(U + 2), lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl,
+        const int64_t frow = (ch / (d.fset * d.D)) * d.D + ch % d.D;   // the channel's filter row
+        fft_tile(U, i, row, spec + frow * (int64_t)(U + 2), lbuf, sc, gmem(static_cast<const Cx<float>*>(d.twf)), twl,
                  reinterpret_cast<FI_SHARED float*>(lbuf), i, 0, d.L, false, false, nullptr, false, nullptr);
         team_sync_global();
     }
@@ -1813,6 +1814,131 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     }
 }
 
+// ======================================================== the layer stack
+// The multi-layer model of [FI] "Algoritmo di Inferenza LCSM (Algoritmo 2)":
+// layer l mixes its input sequence a^l (a^0 = x) with its filter rho^l, and
+// its block maps the mixer output to the next layer's input,
+// a^{l+1} = W2^l act(W1^l z^l) (the synthetic MLP + GELU blocks of [FI]
+// "Configurazione Sperimentale"); the sampler feeds x[t+1] = a^M[t] +
+// sigma noise[t] back.  Per position, the red cells and blocks of all layers
+// run in order in one launch (k_stack_serial, a workgroup per batch row), and
+// then the gray tiles of all layers in one launch ([FI] "Parallelizzazione
+// Cross-Layer (Algoritmo 3)"): channels are (layer, b, c), each a row of the
+// state like a single mixer's, with layer l's filter rows.
+struct StackArgs {
+    DevState d;
+    int64_t B, M;
+    const float* w1t;    // [M][D][D]: w1t[(l D + k) D + j] = W1^l[j][k]
+    const float* w2t;
+    const float* x0;     // [B][D]
+    const float* noise;  // [B][L][D] or NULL
+    float sigma;
+    int act;             // 0 GELU, 1 tanh, 2 identity
+    float* xnext;        // [B][D]: the next position's input
+    float* y;            // [B][L][D]: a^M
+    float* x_out;        // [B][L][D] or NULL: x
+    int64_t t;
+};
+
+constexpr int kStackThreads = 1024;
+
+__device__ __forceinline__ float stack_act(float v, int act) {
+    if (act == 0) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+    if (act == 1) return tanhf(v);
+    return v;
+}
+
+// out[j] = act(sum_k WT[k][j] in[k]) for j < D, by the whole workgroup: G =
+// NT / D groups of D threads each sum a contiguous range of k (the weights of
+// consecutive j are contiguous, so a wavefront's loads coalesce), and the
+// groups' partial sums are added in group order.
+__device__ __forceinline__ void stack_gemv(const FI_GLOBAL float* WT, const float* in, float* out, float* part,
+                                           int64_t D, int act) {
+    const int tid = threadIdx.x;
+    const int G = D >= kStackThreads ? 1 : (int)(kStackThreads / D);
+    if (G == 1) {
+        for (int64_t j = tid; j < D; j += kStackThreads) {
+            float acc = 0.f;
+            for (int64_t k = 0; k < D; ++k) acc = __builtin_fmaf(WT[k * D + j], in[k], acc);
+            out[j] = stack_act(acc, act);
+        }
+        __syncthreads();
+        return;
+    }
+    const int g = tid / (int)D, j = tid % (int)D;
+    if (g < G) {
+        const int64_t k0 = D * g / G, k1 = D * (g + 1) / G;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int64_t k = k0; k < k1; ++k) acc = __builtin_fmaf(WT[k * D + j], in[k], acc);
+        part[g * D + j] = acc;
+    }
+    __syncthreads();
+    for (int64_t jj = tid; jj < D; jj += kStackThreads) {
+        float acc = 0.f;
+        for (int gg = 0; gg < G; ++gg) acc += part[gg * D + jj];
+        out[jj] = stack_act(acc, act);
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kStackThreads) void k_stack_serial(StackArgs a) {
+    extern __shared__ float sm[];
+    const DevState& d = a.d;
+    const int64_t b = blockIdx.x, D = d.D, L = d.L, LS = d.LS, t = a.t, B = a.B;
+    float* av = sm;                 // the current layer's input a^l_t
+    float* zv = sm + D;             // its mixer output z^l_t
+    float* hv = sm + 2 * D;         // act(W1 z)
+    float* part = sm + 3 * D;       // partial sums of the products
+    const int tid = threadIdx.x;
+    for (int64_t c = tid; c < D; c += kStackThreads) {
+        const float xv = t == 0 ? a.x0[b * D + c] : a.xnext[b * D + c];
+        av[c] = xv;
+        if (t == 0 && a.x_out) a.x_out[(b * L) * D + c] = xv;
+    }
+    __syncthreads();
+    for (int64_t l = 0; l < a.M; ++l) {
+        // the red cell: the tiles' accumulation plus the lag-0 term; the row
+        // keeps the input as history
+        for (int64_t c = tid; c < D; c += kStackThreads) {
+            float* row = d.state + ((l * B + b) * D + c) * LS;
+            zv[c] = __builtin_fmaf(d.hT[(l * D + c) * LS], av[c], row[t]);
+            row[t] = av[c];
+        }
+        __syncthreads();
+        stack_gemv(gmem(a.w1t + l * D * D), zv, hv, part, D, a.act);
+        stack_gemv(gmem(a.w2t + l * D * D), hv, av, part, D, 2);
+    }
+    for (int64_t c = tid; c < D; c += kStackThreads) {
+        const float v = av[c];
+        a.y[(b * L + t) * D + c] = v;
+        if (t + 1 < L) {
+            const float xn = a.noise ? __builtin_fmaf(a.sigma, a.noise[(b * L + t) * D + c], v) : v;
+            a.xnext[b * D + c] = xn;
+            if (a.x_out) a.x_out[(b * L + t + 1) * D + c] = xn;
+        }
+    }
+}
+
+// A direct tile of side U (every channel): acc[i + r] += sum_{j<U} x[i-U+j]
+// h[U+r-j], j ascending, the inputs read from the channel's row history.
+__global__ void k_tile_direct(DevState d, int64_t i, int U) {
+    const int64_t n = d.C * (int64_t)U;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t ch = idx / U;
+        const int r = (int)(idx % U);
+        if (i + r >= d.L) continue;
+        const int64_t frow = (ch / (d.fset * d.D)) * d.D + ch % d.D;
+        const float* hu = d.hT + frow * d.LS + U + r;
+        float* row = d.state + ch * d.LS;
+        const float* xr = row + (i - U);
+        float acc = 0.f;
+        for (int j = 0; j < U; ++j) acc = __builtin_fmaf(xr[j], hu[-j], acc);
+        row[i + r] += acc;
+    }
+}
+
 // ======================================================= static workspace
 // The device memory of fi_conv_static, the entry point for callers that
 // cannot allocate: one fixed array per device, held until the process ends.
@@ -1869,9 +1995,9 @@ hipError_t launch_spectra(const DevState& d, int q, void* scd, int64_t scd_strid
     const int F = M < kLdsFftMax ? M : kLdsFftMax;
     const size_t lds = (size_t)lds_fft_elems(F) * sizeof(Cx<double>);
     if (lds > 65536) (void)hipFuncSetAttribute((const void*)k_spectra, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    const int grid = (int)(d.D < slots ? d.D : slots);
+    const int grid = (int)(d.DF < slots ? d.DF : slots);
     V2* spec = static_cast<V2*>(d.spec) + d.spec_off[q];
-    hipLaunchKernelGGL(k_spectra, dim3(grid), dim3(kTeam), lds, st, d.hT, d.LS, d.L, d.D, M, spec,
+    hipLaunchKernelGGL(k_spectra, dim3(grid), dim3(kTeam), lds, st, d.hT, d.LS, d.L, d.DF, M, spec,
                        static_cast<Cx<double>*>(scd), scd_stride, static_cast<const Cx<double>*>(twd));
     return hipGetLastError();
 }
@@ -1901,6 +2027,29 @@ hipError_t launch_step_tile(const DevState& d, int64_t t, const void* x_t, float
     else
         hipLaunchKernelGGL((k_step_tile<false>), dim3(grid), dim3(256), 0, st, d.state, d.hT, d.LS, d.L, d.D, d.C, t,
                            x_t, y_t, U);
+    return hipGetLastError();
+}
+
+hipError_t launch_stack_serial(const DevState& d, int64_t B, int64_t M, const float* w1t, const float* w2t,
+                               const float* x0, const float* noise, float sigma, int act, float* xnext, float* y,
+                               float* x_out, int64_t t, hipStream_t st) {
+    StackArgs a{d, B, M, w1t, w2t, x0, noise, sigma, act, xnext, y, x_out, t};
+    const int64_t G = d.D >= kStackThreads ? 1 : kStackThreads / d.D;
+    const size_t lds = (size_t)(3 * d.D + (G > 1 ? G * d.D : 0)) * sizeof(float);
+    if (lds > 65536) (void)hipFuncSetAttribute((const void*)k_stack_serial, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(k_stack_serial, dim3((unsigned)B), dim3(kStackThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_direct(const DevState& d, int64_t i, int U, hipStream_t st) {
+    hipLaunchKernelGGL(k_tile_direct, dim3(grid_for(d.C * (int64_t)U, 256)), dim3(256), 0, st, d, i, U);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_f32(const float* src, float* dst, int64_t rows, int64_t cols, int64_t ld, hipStream_t st) {
+    const int64_t gy = (ld + 63) / 64;
+    dim3 grid((unsigned)((cols + 63) / 64), (unsigned)(gy < 32768 ? gy : 32768));
+    hipLaunchKernelGGL((k_transpose<false>), grid, dim3(256), 0, st, static_cast<const void*>(src), dst, rows, cols, ld);
     return hipGetLastError();
 }
 

@@ -169,6 +169,49 @@ int fi_run_prompted(fi_handle *s, const void *x_prompt, int64_t p, float *y, voi
 int fi_conv_static(const fi_config *cfg, const void *h, const void *x_in, fi_feedback fb, float *y,
                    void *x_out);
 
+/*
+ * The layer stack ([FI] "Algoritmo di Inferenza LCSM (Algoritmo 2)",
+ * "Parallelizzazione Cross-Layer (Algoritmo 3)"): M layers, each a long
+ * convolution mixer (filter rho^l[L][D], per channel) followed by a block
+ * (the synthetic MLP + GELU block of [FI] "Configurazione Sperimentale"),
+ * and a sampler that feeds the last layer's output back with added noise.
+ * 0-indexed, for every batch row b and position t, with a^0 = x:
+ *   z^l_t[c]  = sum_{s<=t} rho^l[t-s][c] a^l_s[c]
+ *   a^{l+1}_t = W2^l act(W1^l z^l_t)          (W row j = output j, D x D)
+ *   x_{t+1}   = a^M_t + sigma noise[t]
+ * The mixers run the relaxed tiling of fi_step on all M B D channels (red
+ * cells and blocks of all layers in order at each position, then the gray
+ * tiles of all layers in one launch).  fp32 storage and arithmetic.
+ */
+typedef struct fi_stack fi_stack;   /* opaque; owns its device memory */
+typedef enum { FI_ACT_GELU = 0, FI_ACT_TANH = 1, FI_ACT_IDENTITY = 2 } fi_activation;
+typedef struct {
+    int64_t B;                /* batch rows, >= 1 */
+    int64_t D;                /* channels (the blocks are D x D), 1 <= D <= 65536 */
+    int64_t L;                /* positions = filter length, >= 1 */
+    int64_t M;                /* layers, >= 1 */
+    fi_activation act;        /* the blocks' activation: GELU (exact, erf), tanh or identity */
+    void *stream;             /* hipStream_t; NULL = the null stream */
+    int32_t small_tile_max;   /* T as in fi_config (0 = default) */
+} fi_stack_config;
+
+/* fi_stack_create: copies rho[M][L][D], w1[M][D][D] and w2[M][D][D] (device
+ * pointers, fp32; W[l][j][k] is the weight of input k in output j) and
+ * precomputes every layer's filter spectra.  Synchronous.  Errors as
+ * fi_create (FI_ERR_INVALID for an unknown act or M < 1). */
+int fi_stack_create(const fi_stack_config *cfg, const float *rho, const float *w1, const float *w2,
+                    fi_stack **out);
+
+/* fi_stack_run: generates all L positions from x0[B][D]: y[B][L][D]
+ * receives a^M_t, x_out[B][L][D] (or NULL) the inputs x_t; noise[B][L][D]
+ * (or NULL: no noise) is scaled by sigma.  Asynchronous on the stream (two
+ * launches per position); each call starts from position 0.  Device
+ * pointers, owned by the caller until the stream has passed the call. */
+int fi_stack_run(fi_stack *s, const float *x0, const float *noise, float sigma, float *y, float *x_out);
+
+/* fi_stack_destroy: synchronise the stream and free everything; NULL is a no-op. */
+void fi_stack_destroy(fi_stack *s);
+
 /* fi_reset: position := 0; the accumulators are cleared on the stream before
  * the next fi_step (fi_run_closed_loop clears the rows it uses itself). */
 int fi_reset(fi_handle *s);

@@ -193,3 +193,34 @@ def test_bench_cpu_baseline_small_mixer():
         assert cb["cores"] == 1 and cb["host_cpus"] >= 1 and cb["cpu_model"]
         assert ("closed loop" if closed else "open loop") in cb["sample"]
         assert "16 of 16 channels" in cb["sample"] and "[0, 1024) of 1024" in cb["sample"]
+
+
+def test_stack_config_layout_matches_the_header(tmp_path):
+    import subprocess
+    src = tmp_path / "layout_stack.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "fi.h"\n'
+        'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(fi_stack_config),'
+        ' offsetof(fi_stack_config, B), offsetof(fi_stack_config, D), offsetof(fi_stack_config, L),'
+        ' offsetof(fi_stack_config, M), offsetof(fi_stack_config, act), offsetof(fi_stack_config, stream),'
+        ' offsetof(fi_stack_config, small_tile_max)); return 0; }\n')
+    exe = tmp_path / "layout_stack"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)],
+                   check=True, capture_output=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    C = fi.fi_stack_config
+    assert got == [ctypes.sizeof(C), C.B.offset, C.D.offset, C.L.offset, C.M.offset, C.act.offset,
+                   C.stream.offset, C.small_tile_max.offset]
+
+
+@pytest.mark.parametrize("kw", [dict(M=0), dict(act=3), dict(B=0), dict(D=0), dict(L=0)])
+def test_stack_create_rejects_invalid(kw):
+    base = dict(B=1, D=4, L=16, M=2, act=0, stream=None, small_tile_max=0)
+    base.update(kw)
+    cfg = fi.fi_stack_config(**base)
+    out = ctypes.c_void_p(123)
+    st = fi.lib.fi_stack_create(ctypes.byref(cfg), 0x1000, 0x1000, 0x1000, ctypes.byref(out))
+    assert st == fi.FI_ERR_INVALID and out.value is None
+    assert fi.lib.fi_stack_run(None, 1, None, 0.0, 1, None) == fi.FI_ERR_INVALID
+    fi.fi_stack_destroy(None)

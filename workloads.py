@@ -173,10 +173,13 @@ class StackWorkload:
       ``S_c = sum_j exp(-2 j / tau_c)`` (so a white input keeps unit
       variance through the mixer), from ``default_rng([seed, 10, l])``: tau
       first, then the Gaussians in row chunks;
-    * ``W1[l], W2[l]`` (D x D, row j = output j) ``N(0, 2/D)`` (the usual
-      scale for GELU/ReLU layers, so the blocks neither die out nor blow
-      up) from ``default_rng([seed, 11])`` and ``([seed, 12])``, layer by
-      layer;
+    * ``W1[l], W2[l]`` (D x D, row j = output j) ``N(0, 1/D)`` from
+      ``default_rng([seed, 11])`` and ``([seed, 12])``, layer by layer.  The
+      blocks have no normalisation, so the fed-back loop is stable only
+      when a block shrinks its input: at N(0, 2/D) the loop resonates at
+      the filters' peak frequencies and grows without bound (|y| ~ 1e5 by
+      t = 3000 at M = 2); at N(0, 1/D) it stays bounded, and a deep stack
+      (M = 18) damps the signal to ~1e-7, leaving the sampler's noise;
     * ``x0[B][D] ~ N(0,1)`` from ``([seed, 13])``; the sampler's noise
       ``noise[B][L][D] ~ N(0,1)`` from ``([seed, 14])``, scaled by ``sigma``.
     All arrays float32."""
@@ -223,14 +226,14 @@ def make_stack_filters(w: StackWorkload) -> np.ndarray:
 
 
 def make_stack_weights(w: StackWorkload):
-    """(W1[M][D][D], W2[M][D][D]) float32, N(0, 2/D)."""
+    """(W1[M][D][D], W2[M][D][D]) float32, N(0, 1/D)."""
     out = []
     for k in (11, 12):
         rng = np.random.default_rng([w.seed, k])
         W = np.empty((w.M, w.D, w.D), dtype=np.float32)
         for l in range(w.M):
             W[l] = (rng.standard_normal((w.D, w.D), dtype=np.float32).astype(np.float64)
-                    * math.sqrt(2.0 / w.D)).astype(np.float32)
+                    * math.sqrt(1.0 / w.D)).astype(np.float32)
         out.append(W)
     return out[0], out[1]
 
