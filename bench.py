@@ -377,6 +377,72 @@ def phases(args, w, fi, torch) -> int:
     return 0
 
 
+def stack_bench(args, fi, torch) -> int:
+    """The layer stack (fi_stack_run): M mixers with MLP + GELU blocks and the
+    sampler feeding noise back, one position per step over the whole
+    sequence.  Reports generated tokens/s (B L per pass), the time per
+    position, and the oracle's stack on a prefix of the same workload."""
+    import numpy as np
+
+    import workloads
+    w = workloads.get_stack(args.stack)
+    progress(f"bench: stack {w.name} B={w.B} D={w.D} L={w.L} M={w.M}")
+    stream = torch.cuda.current_stream()
+    rho = workloads.make_stack_filters(w)
+    w1, w2 = workloads.make_stack_weights(w)
+    x0 = workloads.make_stack_x0(w)
+    nz = workloads.make_stack_noise(w)
+    dv = [torch.from_numpy(a).cuda() for a in (rho, w1, w2, x0, nz)]
+    y = torch.empty((w.B, w.L, w.D), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s = fi.Stack(w.B, w.D, w.L, w.M, dv[0], dv[1], dv[2], fi.FI_ACT_GELU, args.small_tile_max, stream)
+    create_ms = (time.perf_counter() - t0) * 1e3
+    for k in range(args.warmup):
+        s.run(dv[3], y, None, dv[4], w.sigma)
+    torch.cuda.synchronize()
+    progress(f"bench: stack create {create_ms:.1f} ms, {args.warmup} warm-up passes done")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        s.run(dv[3], y, None, dv[4], w.sigma)
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    per = [a.elapsed_time(b) for a, b in evs]
+    ms = sum(per) / len(per)
+    assert torch.isfinite(y).all().item(), "non-finite output"
+    s.close()
+    progress(f"bench: stack {args.steps} timed passes, {ms:.3f} ms/pass")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # the oracle's stack is O(M D t) per position t: time a prefix of
+        # about 10-30 s and report its positions per second
+        P = min(w.L, 1024)
+        orc = oracle.default()
+        t1 = time.perf_counter()
+        orc.conv_stack(rho[:, :P], w1, w2, x0, noise=nz[:, :P], sigma=np.float32(w.sigma), act="gelu")
+        sec = time.perf_counter() - t1
+        cpu = {"value": round(w.B * P / sec, 2), "unit": "tokens/s", "cores": min(w.B, orc.threads),
+               "kind": "oracle", "cpu_model": host_cpu(),
+               "sample": f"the first {P} of {w.L} positions, all {w.B} batch rows and {w.M} layers, "
+                         f"{sec:.1f} s (one thread per batch row; later positions cost more, "
+                         f"so the full sequence runs slower than this rate)"}
+        progress(f"bench: oracle {cpu['sample']}")
+    out = {"metric": "stack tokens/sec (B·L/s), M mixers + MLP/GELU blocks + sampler", "value":
+           round(w.B * w.L / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "B": w.B, "D": w.D, "L": w.L, "M": w.M, "act": "gelu",
+                      "sigma": w.sigma, "us_per_position": round(ms * 1e3 / w.L, 2),
+                      "host_wall_ms_per_pass": round(wall * 1e3, 2), "create_ms": round(create_ms, 1)},
+           "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +467,8 @@ def main() -> int:
     ap.add_argument("--phases", action="store_true",
                     help="phase breakdown of one pass from the phase-timing build "
                          "(python exact_online_amd/build.py --profile)")
+    ap.add_argument("--stack", default="", metavar="NAME",
+                    help="time the layer stack workload NAME (e.g. stack-m18-d256-l16k) instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--write-traffic", nargs=5,
@@ -433,6 +501,9 @@ def main() -> int:
     import exact_online_amd as fi
     import workloads
 
+    if args.stack:
+        torch.cuda.set_device(0)
+        return stack_bench(args, fi, torch)
     w = workloads.get(args.workload)
     if args.phases:
         torch.cuda.set_device(0)

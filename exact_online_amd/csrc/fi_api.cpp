@@ -386,18 +386,20 @@ const char *fi_strerror(int status) {
 
 struct fi_stack {
     fi_handle h;   // the M B D channels (layer, b, c); filter rows per layer
-    int64_t B, M;
-    int act;
-    float *w1t, *w2t, *xnext;
+    fi::StackChain sc;
+    float *w1, *w2t, *xnext, *hist;
+    void *part;    // tagged partial products
+    void *sync;    // the failure mark
+    uint32_t tag0; // the next run's tag base
 };
 
 namespace {
 void free_stack(fi_stack *s) {
     free_state(s->h.d);
-    if (s->w1t) (void)hipFree(s->w1t);
-    if (s->w2t) (void)hipFree(s->w2t);
-    if (s->xnext) (void)hipFree(s->xnext);
-    s->w1t = s->w2t = s->xnext = nullptr;
+    for (void *p : {(void *)s->w1, (void *)s->w2t, (void *)s->xnext, s->part, (void *)s->hist, s->sync})
+        if (p) (void)hipFree(p);
+    s->w1 = s->w2t = s->xnext = s->hist = nullptr;
+    s->part = s->sync = nullptr;
 }
 
 int build_stack(fi_stack *s, const float *rho, const float *w1, const float *w2) {
@@ -412,16 +414,30 @@ int build_stack(fi_stack *s, const float *rho, const float *w1, const float *w2)
     FI_HIP(dalloc(&d.spec, pl.spec));
     FI_HIP(dalloc(&d.twf, pl.twf));
     if (pl.scratch > 0) FI_HIP(dalloc(&d.scratch, pl.scratch));
-    const int64_t D = d.D, L = d.L, M = s->M;
-    FI_HIP(dalloc(&s->w1t, (size_t)(M * D * D) * sizeof(float)));
+    fi::StackChain &sc = s->sc;
+    const int64_t D = d.D, L = d.L, M = sc.M;
+    FI_HIP(dalloc(&s->w1, (size_t)(M * D * D) * sizeof(float)));
     FI_HIP(dalloc(&s->w2t, (size_t)(M * D * D) * sizeof(float)));
-    FI_HIP(dalloc(&s->xnext, (size_t)(s->B * D) * sizeof(float)));
+    FI_HIP(dalloc(&s->xnext, (size_t)(sc.B * D) * sizeof(float)));
+    const size_t part_bytes = (size_t)(2 * sc.P * sc.B * D) * sizeof(unsigned long long);
+    FI_HIP(dalloc(&s->part, part_bytes));
+    FI_HIP(dalloc(&s->hist, (size_t)(M * sc.B * D) * sizeof(float)));
+    FI_HIP(dalloc(&s->sync, 256));
+    FI_HIP(hipMemcpyAsync(s->w1, w1, (size_t)(M * D * D) * sizeof(float), hipMemcpyDeviceToDevice, st));
     for (int64_t l = 0; l < M; ++l) {
-        // layer l's filter rows, and its weights with output index innermost
+        // layer l's filter rows, and W2 with its output index innermost
         FI_HIP(fi::launch_transpose_f32(rho + l * L * D, d.hT + l * D * d.LS, L, D, d.LS, st));
-        FI_HIP(fi::launch_transpose_f32(w1 + l * D * D, s->w1t + l * D * D, D, D, D, st));
         FI_HIP(fi::launch_transpose_f32(w2 + l * D * D, s->w2t + l * D * D, D, D, D, st));
     }
+    // tag 0 is never awaited: cleared words are never taken for a partial
+    FI_HIP(fi::launch_zero(static_cast<float *>(s->part), (int64_t)(part_bytes / sizeof(float)), st));
+    FI_HIP(fi::launch_zero(static_cast<float *>(s->sync), 64, st));
+    sc.w1 = s->w1;
+    sc.w2t = s->w2t;
+    sc.xnext = s->xnext;
+    sc.part = static_cast<unsigned long long *>(s->part);
+    sc.hist = s->hist;
+    sc.fail = static_cast<int *>(s->sync);
     void *twd = nullptr, *scd = nullptr;
     FI_HIP(dalloc(&twd, pl.twd));
     hipError_t e = hipSuccess;
@@ -447,7 +463,8 @@ int fi_stack_create(const fi_stack_config *cfg, const float *rho, const float *w
     if (act != FI_ACT_GELU && act != FI_ACT_TANH && act != FI_ACT_IDENTITY) return FI_ERR_INVALID;
     const int64_t lim = (int64_t)1 << 31;
     if (cfg->M < 1 || cfg->B < 1 || cfg->M >= lim || cfg->B >= lim || cfg->M > lim / cfg->B) return FI_ERR_INVALID;
-    if (cfg->D > ((int64_t)1 << 16)) return FI_ERR_UNSUPPORTED;   // the blocks' weights: D x D per layer
+    if (cfg->D > fi::kChainMaxD) return FI_ERR_UNSUPPORTED;   // a D-vector of a block in LDS
+    if (cfg->L > 0 && cfg->M > fi::kChainMaxTags / cfg->L) return FI_ERR_UNSUPPORTED;   // L M tags per run
     fi_config c;
     std::memset(&c, 0, sizeof(c));
     c.B = cfg->M * cfg->B;   // rows (layer, b)
@@ -463,9 +480,11 @@ int fi_stack_create(const fi_stack_config *cfg, const float *rho, const float *w
         delete s;
         return rc;
     }
-    s->B = cfg->B;
-    s->M = cfg->M;
-    s->act = act;
+    s->sc.B = cfg->B;
+    s->sc.M = cfg->M;
+    s->sc.act = act;
+    s->sc.P = (int)(cfg->D < fi::kChainMaxWorkgroups ? cfg->D : fi::kChainMaxWorkgroups);
+    s->tag0 = 0;
     s->h.d.fset = cfg->B;            // B rows per layer share its filter rows
     s->h.d.DF = cfg->M * cfg->D;     // filter rows: (layer, c)
     rc = build_stack(s, rho, w1, w2);
@@ -483,14 +502,24 @@ int fi_stack_run(fi_stack *s, const float *x0, const float *noise, float sigma, 
     if (!s || !x0 || !y) return FI_ERR_INVALID;
     const DevState &d = s->h.d;
     hipStream_t st = s->h.stream;
-    // the tiles add into the rows: every run starts from cleared rows
+    // a barrier of an earlier run that waited past its limit fails the handle
+    int failed = 0;
+    FI_HIP(hipMemcpyAsync(&failed, s->sc.fail, sizeof(int), hipMemcpyDeviceToHost, st));
+    FI_HIP(hipStreamSynchronize(st));
+    if (failed) return hip_fail(hipErrorLaunchTimeOut);
+    // the tiles add into the rows; this run's words carry tags after the
+    // last run's
     FI_HIP(fi::launch_zero(d.state, d.C * d.LS, st));
+    const uint32_t tag0 = s->tag0;
+    s->tag0 = tag0 + (uint32_t)(d.L * s->sc.M);
+    const int64_t fuse_max = d.T < fi::kChainFuseMax ? d.T : fi::kChainFuseMax;
     for (int64_t t = 0; t < d.L; ++t) {
-        FI_HIP(fi::launch_stack_serial(d, s->B, s->M, s->w1t, s->w2t, x0, noise, sigma, s->act, s->xnext, y,
-                                       x_out, t, st));
         const int64_t i = t + 1;
-        if (i >= d.L) break;
         const int64_t U = i & -i;
+        const bool tile = i < d.L;
+        const int fuse = tile && U <= fuse_max ? (int)U : 0;
+        FI_HIP(fi::launch_stack_chain(d, s->sc, x0, noise, sigma, y, x_out, t, tag0, fuse, st));
+        if (!tile || fuse) continue;
         if (U <= d.T) FI_HIP(fi::launch_tile_direct(d, i, (int)U, st));
         else FI_HIP(fi::launch_tile(d, i, st));
     }

@@ -128,11 +128,32 @@ hipError_t launch_tile(const DevState &d, int64_t i, hipStream_t st);   // FFT t
 hipError_t launch_step_tile(const DevState &d, int64_t t, const void *x_t, float *y_t, int U, hipStream_t st);
 
 // the layer stack: one position of every layer's red cell and block for
-// every batch row, then the tile all layers' channels need at t + 1
-struct StackArgs;
-hipError_t launch_stack_serial(const DevState &d, int64_t B, int64_t M, const float *w1t, const float *w2t,
-                               const float *x0, const float *noise, float sigma, int act, float *xnext,
-                               float *y, float *x_out, int64_t t, hipStream_t st);
+// every batch row over P workgroups that pass tagged partial products, then
+// (fused when its side is <= kChainFuseMax) the tile all layers' channels
+// need at t + 1
+#ifndef FI_CHAIN_FUSE
+#define FI_CHAIN_FUSE 16
+#endif
+#ifndef FI_CHAIN_WORKGROUPS
+#define FI_CHAIN_WORKGROUPS 16
+#endif
+constexpr int kChainFuseMax = FI_CHAIN_FUSE;
+constexpr int kChainMaxWorkgroups = FI_CHAIN_WORKGROUPS;
+constexpr int kChainStageBytes = 96 * 1024;   // LDS for the vectors and the staged accumulators
+constexpr int64_t kChainMaxD = 8192;           // a D-vector of a block in LDS
+constexpr int64_t kChainMaxTags = (int64_t)1 << 30;   // L M per run: tags of two runs never meet
+struct StackChain {
+    int64_t B, M;
+    int act, P;
+    const float *w1, *w2t;
+    float *xnext, *hist;
+    unsigned long long *part;
+    int *fail;
+};
+int stack_chain_lds_bytes(int64_t B, int64_t D, int64_t M, int P, int *pre);
+hipError_t launch_stack_chain(const DevState &d, const StackChain &sc, const float *x0, const float *noise,
+                              float sigma, float *y, float *x_out, int64_t t, unsigned tag0, int fuse_u,
+                              hipStream_t st);
 hipError_t launch_tile_direct(const DevState &d, int64_t i, int U, hipStream_t st);
 // a plain fp32 transpose: dst[c][r] = src[r][c], r < rows, c < cols (row
 // stride of dst: ld >= rows, entries [rows, ld) zeroed)

@@ -1820,16 +1820,36 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
 // its block maps the mixer output to the next layer's input,
 // a^{l+1} = W2^l act(W1^l z^l) (the synthetic MLP + GELU blocks of [FI]
 // "Configurazione Sperimentale"); the sampler feeds x[t+1] = a^M[t] +
-// sigma noise[t] back.  Per position, the red cells and blocks of all layers
-// run in order in one launch (k_stack_serial, a workgroup per batch row), and
-// then the gray tiles of all layers in one launch ([FI] "Parallelizzazione
-// Cross-Layer (Algoritmo 3)"): channels are (layer, b, c), each a row of the
-// state like a single mixer's, with layer l's filter rows.
-struct StackArgs {
+// sigma noise[t] back.  Channels are (layer, b, c), each a row of the state
+// like a single mixer's, with layer l's filter rows.
+//
+// One position of every layer runs in one launch (k_stack_chain) over P
+// workgroups.  Workgroup p owns the slice S_p = [D p / P, D (p+1) / P) of
+// each block's hidden units: it forms h_j = act(W1[j] . z) for j in S_p and
+// the partial product W2[:, S_p] h_{S_p}, a full D-vector.  The next layer's
+// input is the sum of the P partials in slice order, which every workgroup
+// forms for itself; every weight is read by exactly one workgroup.  Each
+// workgroup also forms the whole mixer output z itself (D fused
+// multiply-adds), and parks the inputs of its own slice of channels.
+//
+// There is no grid barrier: a partial value travels in one 64-bit word with
+// a tag naming (run, position, layer) in its high half, stored and loaded as
+// relaxed device-scope atomics, and a reader waits until every word it needs
+// carries the tag it expects.  Only the parked inputs need ordering: the
+// last layer's words are stored after a release fence and read before an
+// acquire fence.  Two buffers of words alternate by layer: a workgroup
+// overwrites layer l's words (at layer l + 2) only after it has read every
+// workgroup's layer l + 1 words, which each wrote after reading layer l.
+//
+// After the last layer the tile that position t+1 completes runs in the same
+// launch when it is small (side <= kChainFuseMax; [FI] "Parallelizzazione
+// Cross-Layer (Algoritmo 3)": the tiles of all layers at once), otherwise in
+// its own launch.
+struct ChainArgs {
     DevState d;
     int64_t B, M;
-    const float* w1t;    // [M][D][D]: w1t[(l D + k) D + j] = W1^l[j][k]
-    const float* w2t;
+    const float* w1;     // [M][D][D]: W1^l[j][k], row j = output j
+    const float* w2t;    // [M][D][D]: w2t[(l D + j) D + i] = W2^l[i][j]
     const float* x0;     // [B][D]
     const float* noise;  // [B][L][D] or NULL
     float sigma;
@@ -1837,10 +1857,19 @@ struct StackArgs {
     float* xnext;        // [B][D]: the next position's input
     float* y;            // [B][L][D]: a^M
     float* x_out;        // [B][L][D] or NULL: x
+    unsigned long long* part;   // [2][P][B][D] tagged partial products
+    float* hist;         // [M][B][D]: every layer's input at t, until the rows take it
+    int* fail;           // set when a wait passes its limit
     int64_t t;
+    unsigned tag0;       // the run's tag base: the word of (t, l) carries tag0 + t M + l + 1
+    int P;               // workgroups
+    int fuse_u;          // side of the fused tile, 0 for none
+    int pre;             // 1: stage every layer's accumulator at t in LDS first
 };
 
-constexpr int kStackThreads = 1024;
+constexpr int kChainThreads = 256;
+constexpr long kChainSpinLimit = 1L << 20;   // about a second of polling
+constexpr int kChainRegs = 16;               // weights per thread and matrix held in registers
 
 __device__ __forceinline__ float stack_act(float v, int act) {
     if (act == 0) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
@@ -1848,84 +1877,54 @@ __device__ __forceinline__ float stack_act(float v, int act) {
     return v;
 }
 
-// out[j] = act(sum_k WT[k][j] in[k]) for j < D, by the whole workgroup: G =
-// NT / D groups of D threads each sum a contiguous range of k (the weights of
-// consecutive j are contiguous, so a wavefront's loads coalesce), and the
-// groups' partial sums are added in group order.
-__device__ __forceinline__ void stack_gemv(const FI_GLOBAL float* WT, const float* in, float* out, float* part,
-                                           int64_t D, int act) {
-    const int tid = threadIdx.x;
-    const int G = D >= kStackThreads ? 1 : (int)(kStackThreads / D);
-    if (G == 1) {
-        for (int64_t j = tid; j < D; j += kStackThreads) {
-            float acc = 0.f;
-            for (int64_t k = 0; k < D; ++k) acc = __builtin_fmaf(WT[k * D + j], in[k], acc);
-            out[j] = stack_act(acc, act);
-        }
-        __syncthreads();
-        return;
-    }
-    const int g = tid / (int)D, j = tid % (int)D;
-    if (g < G) {
-        const int64_t k0 = D * g / G, k1 = D * (g + 1) / G;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int64_t k = k0; k < k1; ++k) acc = __builtin_fmaf(WT[k * D + j], in[k], acc);
-        part[g * D + j] = acc;
-    }
-    __syncthreads();
-    for (int64_t jj = tid; jj < D; jj += kStackThreads) {
-        float acc = 0.f;
-        for (int gg = 0; gg < G; ++gg) acc += part[gg * D + jj];
-        out[jj] = stack_act(acc, act);
-    }
-    __syncthreads();
+__device__ __forceinline__ unsigned long long tagged(unsigned tag, float v) {
+    return ((unsigned long long)tag << 32) | __float_as_uint(v);
 }
 
-__global__ __launch_bounds__(kStackThreads) void k_stack_serial(StackArgs a) {
-    extern __shared__ float sm[];
-    const DevState& d = a.d;
-    const int64_t b = blockIdx.x, D = d.D, L = d.L, LS = d.LS, t = a.t, B = a.B;
-    float* av = sm;                 // the current layer's input a^l_t
-    float* zv = sm + D;             // its mixer output z^l_t
-    float* hv = sm + 2 * D;         // act(W1 z)
-    float* part = sm + 3 * D;       // partial sums of the products
-    const int tid = threadIdx.x;
-    for (int64_t c = tid; c < D; c += kStackThreads) {
-        const float xv = t == 0 ? a.x0[b * D + c] : a.xnext[b * D + c];
-        av[c] = xv;
-        if (t == 0 && a.x_out) a.x_out[(b * L) * D + c] = xv;
-    }
-    __syncthreads();
-    for (int64_t l = 0; l < a.M; ++l) {
-        // the red cell: the tiles' accumulation plus the lag-0 term; the row
-        // keeps the input as history
-        for (int64_t c = tid; c < D; c += kStackThreads) {
-            float* row = d.state + ((l * B + b) * D + c) * LS;
-            zv[c] = __builtin_fmaf(d.hT[(l * D + c) * LS], av[c], row[t]);
-            row[t] = av[c];
-        }
-        __syncthreads();
-        stack_gemv(gmem(a.w1t + l * D * D), zv, hv, part, D, a.act);
-        stack_gemv(gmem(a.w2t + l * D * D), hv, av, part, D, 2);
-    }
-    for (int64_t c = tid; c < D; c += kStackThreads) {
-        const float v = av[c];
-        a.y[(b * L + t) * D + c] = v;
-        if (t + 1 < L) {
-            const float xn = a.noise ? __builtin_fmaf(a.sigma, a.noise[(b * L + t) * D + c], v) : v;
-            a.xnext[b * D + c] = xn;
-            if (a.x_out) a.x_out[(b * L + t + 1) * D + c] = xn;
-        }
-    }
+__device__ __forceinline__ void put_word(unsigned long long* w, unsigned long long v) {
+    __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A direct tile of side U (every channel): acc[i + r] += sum_{j<U} x[i-U+j]
-// h[U+r-j], j ascending, the inputs read from the channel's row history.
-__global__ void k_tile_direct(DevState d, int64_t i, int U) {
+__device__ __forceinline__ unsigned long long get_word(const unsigned long long* w) {
+    return __hip_atomic_load(const_cast<unsigned long long*>(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// sum_{q < P} value(w[q stride]) in q order, once every word carries `tag`;
+// all loads in flight together, stale ones reloaded.  A wait past the limit
+// marks the run failed and returns what it has (every wave exits).
+__device__ __forceinline__ float gather_sum(const unsigned long long* w, int64_t stride, int P, unsigned tag,
+                                            int* fail) {
+    unsigned long long x[kChainMaxWorkgroups];
+#pragma unroll
+    for (int q = 0; q < kChainMaxWorkgroups; ++q) x[q] = q < P ? get_word(w + q * stride) : tagged(tag, 0.f);
+    for (long spins = 0;; ++spins) {
+        bool ready = true;
+#pragma unroll
+        for (int q = 0; q < kChainMaxWorkgroups; ++q) ready &= (unsigned)(x[q] >> 32) == tag;
+        if (ready) break;
+        if (spins > kChainSpinLimit) {
+            __hip_atomic_store(fail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int q = 0; q < kChainMaxWorkgroups; ++q)
+            if ((unsigned)(x[q] >> 32) != tag) x[q] = get_word(w + q * stride);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kChainMaxWorkgroups; ++q) s += __uint_as_float((unsigned)x[q]);
+    return s;
+}
+
+// A direct tile of side U over channels [idx0, ...) with stride `step`:
+// acc[i + r] += sum_{j<U} x[i-U+j] h[U+r-j], j ascending, the inputs read
+// from the channel's row history.  With `last` given, the input at position
+// i-1 of channel ch is last[ch] instead of the row's.
+__device__ __forceinline__ void tile_direct_range(const DevState& d, int64_t i, int U, int64_t idx0, int64_t step,
+                                                  const float* last = nullptr) {
     const int64_t n = d.C * (int64_t)U;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
-         idx += (int64_t)gridDim.x * blockDim.x) {
+    for (int64_t idx = idx0; idx < n; idx += step) {
         const int64_t ch = idx / U;
         const int r = (int)(idx % U);
         if (i + r >= d.L) continue;
@@ -1934,9 +1933,212 @@ __global__ void k_tile_direct(DevState d, int64_t i, int U) {
         float* row = d.state + ch * d.LS;
         const float* xr = row + (i - U);
         float acc = 0.f;
-        for (int j = 0; j < U; ++j) acc = __builtin_fmaf(xr[j], hu[-j], acc);
+        for (int j = 0; j < U - 1; ++j) acc = __builtin_fmaf(xr[j], hu[-j], acc);
+        acc = __builtin_fmaf(last ? last[ch] : xr[U - 1], hu[1 - U], acc);
         row[i + r] += acc;
     }
+}
+
+// tile_direct_range at a side known at compile time, every load in flight
+// before the sum (the same products in the same order).
+template <int U>
+__device__ __forceinline__ void tile_small(const DevState& d, int64_t i, int64_t idx0, int64_t step, const float* last) {
+    const int64_t n = d.C * (int64_t)U;
+    for (int64_t idx = idx0; idx < n; idx += step) {
+        const int64_t ch = idx / U;
+        const int r = (int)(idx % U);
+        if (i + r >= d.L) continue;
+        const int64_t frow = (ch / (d.fset * d.D)) * d.D + ch % d.D;
+        const float* hu = d.hT + frow * d.LS + U + r;
+        float* row = d.state + ch * d.LS;
+        const float* xr = row + (i - U);
+        float xv[U], hv[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            xv[j] = j == U - 1 ? last[ch] : xr[j];
+            hv[j] = hu[-j];
+        }
+        const float old = row[i + r];
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < U; ++j) acc = __builtin_fmaf(xv[j], hv[j], acc);
+        row[i + r] = old + acc;
+    }
+}
+
+// The register plan of a slice (REGW): W1's rows of the slice, TPR threads
+// per row (a power of two <= 64), KC weights each; W2's columns of the
+// slice, IC outputs per thread, ns weights each.
+struct ChainRegPlan {
+    int tpr, kc, ic;
+};
+
+__host__ __device__ inline ChainRegPlan chain_reg_plan(int64_t D, int64_t ns) {
+    ChainRegPlan r{0, 0, 0};
+    if (ns < 1 || ns > kChainThreads) return r;
+    int tpr = 64;
+    while (tpr > 1 && (int64_t)tpr * ns > kChainThreads) tpr >>= 1;
+    r.tpr = tpr;
+    r.kc = (int)((D + tpr - 1) / tpr);
+    r.ic = (int)((D + kChainThreads - 1) / kChainThreads);
+    return r;
+}
+
+__host__ __device__ inline bool chain_regs_fit(int64_t D, int64_t ns) {
+    const ChainRegPlan r = chain_reg_plan(D, ns);
+    return r.tpr > 0 && r.kc <= kChainRegs && ns * r.ic <= kChainRegs;
+}
+
+template <bool REGW>
+__global__ __launch_bounds__(kChainThreads) void k_stack_chain(ChainArgs a) {
+    extern __shared__ float sm[];
+    const DevState& d = a.d;
+    const int p = (int)blockIdx.x, P = a.P, tid = threadIdx.x;
+    const int64_t D = d.D, L = d.L, LS = d.LS, t = a.t, B = a.B, M = a.M;
+    const int64_t j0 = D * p / P, j1 = D * (p + 1) / P, ns = j1 - j0;
+    float* zv = sm;                           // the mixer output of one batch row
+    float* hv = sm + D;                       // act(W1 z) on this slice
+    float* accp = sm + D + ((ns + 63) & ~63LL);   // [M][B][D] accumulators at t
+    if (a.pre) {
+        // eight independent loads in flight per thread
+        const int64_t n = M * B * D;
+        for (int64_t k0 = tid; k0 < n; k0 += 8 * kChainThreads) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t k = k0 + (int64_t)u * kChainThreads;
+                v[u] = k < n ? d.state[k * LS + t] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t k = k0 + (int64_t)u * kChainThreads;
+                if (k < n) accp[k] = v[u];
+            }
+        }
+    }
+    const ChainRegPlan rp = chain_reg_plan(D, ns);
+    const int row = REGW ? tid / rp.tpr : 0, li = REGW ? tid % rp.tpr : 0;
+    const unsigned tag_t = a.tag0 + (unsigned)(t * M);
+    for (int64_t l = 0; l < M; ++l) {
+        const unsigned tag_prev = tag_t + (unsigned)l, tag_mine = tag_prev + 1u;
+        const unsigned long long* prev = a.part + ((l - 1) & 1) * P * B * D;
+        unsigned long long* mine = a.part + ((l & 1) * P + p) * B * D;
+        // this layer's weights of the slice, in flight while the inputs arrive
+        float w1r[REGW ? kChainRegs : 1], w2r[REGW ? kChainRegs : 1];
+        if (REGW) {
+#pragma unroll
+            for (int m = 0; m < kChainRegs; ++m) {
+                const int64_t k = li + (int64_t)m * rp.tpr;
+                w1r[m] = (m < rp.kc && row < ns && k < D) ? a.w1[(l * D + j0 + row) * D + k] : 0.f;
+            }
+#pragma unroll
+            for (int m = 0; m < kChainRegs; ++m) {
+                const int64_t jj = m / (rp.ic > 0 ? rp.ic : 1), i = tid + (int64_t)(m % (rp.ic > 0 ? rp.ic : 1)) * kChainThreads;
+                w2r[m] = (jj < ns && i < D && m < ns * rp.ic) ? a.w2t[(l * D + j0 + jj) * D + i] : 0.f;
+            }
+        }
+        for (int64_t b = 0; b < B; ++b) {
+            // the red cell: the tiles' accumulation plus the lag-0 term; the
+            // slice owner parks the input (other workgroups may still read
+            // the accumulator at t until they have formed their last partial)
+            for (int64_t c = tid; c < D; c += kChainThreads) {
+                const float v = l == 0 ? (t == 0 ? a.x0[b * D + c] : a.xnext[b * D + c])
+                                       : gather_sum(prev + b * D + c, B * D, P, tag_prev, a.fail);
+                const int64_t ch = (l * B + b) * D + c;
+                const float acc = a.pre ? accp[ch] : d.state[ch * LS + t];
+                zv[c] = __builtin_fmaf(d.hT[(l * D + c) * LS], v, acc);
+                if (c >= j0 && c < j1) {
+                    a.hist[ch] = v;
+                    if (l == 0 && t == 0 && a.x_out) a.x_out[(b * L) * D + c] = v;
+                }
+            }
+            __syncthreads();
+            // the parked inputs of every layer (this row's of the last layer
+            // included) before the last layer's words
+            if (l == M - 1) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (REGW) {
+                // h_j = act(W1[j] . z) for j in the slice
+                float s = 0.f;
+#pragma unroll
+                for (int m = 0; m < kChainRegs; ++m) {
+                    const int64_t k = li + (int64_t)m * rp.tpr;
+                    if (m < rp.kc && k < D) s = __builtin_fmaf(w1r[m], zv[k], s);
+                }
+                for (int o = rp.tpr >> 1; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+                if (li == 0 && row < ns) hv[row] = stack_act(s, a.act);
+                __syncthreads();
+                // this slice's share of W2 h, every output
+                for (int m2 = 0; m2 < rp.ic; ++m2) {
+                    const int64_t i = tid + (int64_t)m2 * kChainThreads;
+                    float acc = 0.f;
+#pragma unroll
+                    for (int m = 0; m < kChainRegs; ++m) {
+                        const int64_t jj = m / rp.ic;
+                        if (m % rp.ic == m2 && jj < ns) acc = __builtin_fmaf(w2r[m], hv[jj], acc);
+                    }
+                    if (i < D) put_word(mine + b * D + i, tagged(tag_mine, acc));
+                }
+            } else {
+                const int wave = tid >> 6, lane = tid & 63;
+                for (int64_t j = j0 + wave; j < j1; j += kChainThreads / 64) {
+                    const float* wr = a.w1 + (l * D + j) * D;
+                    float s = 0.f;
+#pragma unroll 8
+                    for (int64_t k = lane; k < D; k += 64) s = __builtin_fmaf(wr[k], zv[k], s);
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+                    if (lane == 0) hv[j - j0] = stack_act(s, a.act);
+                }
+                __syncthreads();
+                for (int64_t i = tid; i < D; i += kChainThreads) {
+                    const float* wc = a.w2t + (l * D + j0) * D + i;
+                    float acc = 0.f;
+#pragma unroll 8
+                    for (int64_t jj = 0; jj < ns; ++jj) acc = __builtin_fmaf(wc[jj * D], hv[jj], acc);
+                    put_word(mine + b * D + i, tagged(tag_mine, acc));
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // a^M on this workgroup's slice: the output, and the sampler's next input
+    const unsigned long long* last = a.part + ((M - 1) & 1) * P * B * D;
+    const unsigned tag_last = tag_t + (unsigned)M;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t c = j0 + tid; c < j1; c += kChainThreads) {
+            const float v = gather_sum(last + b * D + c, B * D, P, tag_last, a.fail);
+            a.y[(b * L + t) * D + c] = v;
+            if (t + 1 < L) {
+                const float xn = a.noise ? __builtin_fmaf(a.sigma, a.noise[(b * L + t) * D + c], v) : v;
+                a.xnext[b * D + c] = xn;
+                if (a.x_out) a.x_out[(b * L + t + 1) * D + c] = xn;
+            }
+        }
+    }
+    // every workgroup has formed its last partial, so every accumulator at t
+    // has been read: the parked inputs become the rows' histories, and the
+    // small tile position t+1 completes reads them on every layer's channels
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+    for (int64_t k = tid; k < M * B * ns; k += kChainThreads) {
+        const int64_t ch = (k / ns) * D + j0 + k % ns;
+        d.state[ch * LS + t] = a.hist[ch];
+    }
+    const int64_t i0 = (int64_t)p * kChainThreads + tid, st = (int64_t)P * kChainThreads;
+    switch (a.fuse_u) {
+        case 1: tile_small<1>(d, t + 1, i0, st, a.hist); break;
+        case 2: tile_small<2>(d, t + 1, i0, st, a.hist); break;
+        case 4: tile_small<4>(d, t + 1, i0, st, a.hist); break;
+        case 8: tile_small<8>(d, t + 1, i0, st, a.hist); break;
+        case 16: tile_small<16>(d, t + 1, i0, st, a.hist); break;
+        case 32: tile_small<32>(d, t + 1, i0, st, a.hist); break;
+        default: if (a.fuse_u) tile_direct_range(d, t + 1, a.fuse_u, i0, st, a.hist); break;
+    }
+}
+
+// A direct tile of side U on every channel, over the whole grid.
+__global__ void k_tile_direct(DevState d, int64_t i, int U) {
+    tile_direct_range(d, i, U, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
 }
 
 // ======================================================= static workspace
@@ -2030,14 +2232,25 @@ hipError_t launch_step_tile(const DevState& d, int64_t t, const void* x_t, float
     return hipGetLastError();
 }
 
-hipError_t launch_stack_serial(const DevState& d, int64_t B, int64_t M, const float* w1t, const float* w2t,
-                               const float* x0, const float* noise, float sigma, int act, float* xnext, float* y,
-                               float* x_out, int64_t t, hipStream_t st) {
-    StackArgs a{d, B, M, w1t, w2t, x0, noise, sigma, act, xnext, y, x_out, t};
-    const int64_t G = d.D >= kStackThreads ? 1 : kStackThreads / d.D;
-    const size_t lds = (size_t)(3 * d.D + (G > 1 ? G * d.D : 0)) * sizeof(float);
-    if (lds > 65536) (void)hipFuncSetAttribute((const void*)k_stack_serial, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(k_stack_serial, dim3((unsigned)B), dim3(kStackThreads), lds, st, a);
+int stack_chain_lds_bytes(int64_t B, int64_t D, int64_t M, int P, int* pre) {
+    const int64_t ns = (D + P - 1) / P;
+    const int64_t base = D + ((ns + 63) & ~63LL);
+    const int64_t staged = M * B * D;
+    *pre = (base + staged) * 4 <= kChainStageBytes ? 1 : 0;
+    return (int)((base + (*pre ? staged : 0)) * 4);
+}
+
+hipError_t launch_stack_chain(const DevState& d, const StackChain& sc, const float* x0, const float* noise,
+                              float sigma, float* y, float* x_out, int64_t t, unsigned tag0, int fuse_u,
+                              hipStream_t st) {
+    ChainArgs a{d, sc.B, sc.M, sc.w1, sc.w2t, x0, noise, sigma, sc.act, sc.xnext, y, x_out, sc.part, sc.hist,
+                sc.fail, t, tag0, sc.P, fuse_u, 0};
+    const size_t lds = (size_t)stack_chain_lds_bytes(sc.B, d.D, sc.M, sc.P, &a.pre);
+    const bool regw = chain_regs_fit(d.D, (d.D + sc.P - 1) / sc.P);
+    const void* fn = regw ? (const void*)k_stack_chain<true> : (const void*)k_stack_chain<false>;
+    if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (regw) hipLaunchKernelGGL(k_stack_chain<true>, dim3((unsigned)sc.P), dim3(kChainThreads), lds, st, a);
+    else hipLaunchKernelGGL(k_stack_chain<false>, dim3((unsigned)sc.P), dim3(kChainThreads), lds, st, a);
     return hipGetLastError();
 }
 

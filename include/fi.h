@@ -187,7 +187,7 @@ typedef struct fi_stack fi_stack;   /* opaque; owns its device memory */
 typedef enum { FI_ACT_GELU = 0, FI_ACT_TANH = 1, FI_ACT_IDENTITY = 2 } fi_activation;
 typedef struct {
     int64_t B;                /* batch rows, >= 1 */
-    int64_t D;                /* channels (the blocks are D x D), 1 <= D <= 65536 */
+    int64_t D;                /* channels (the blocks are D x D), 1 <= D <= 8192 */
     int64_t L;                /* positions = filter length, >= 1 */
     int64_t M;                /* layers, >= 1 */
     fi_activation act;        /* the blocks' activation: GELU (exact, erf), tanh or identity */
@@ -198,15 +198,23 @@ typedef struct {
 /* fi_stack_create: copies rho[M][L][D], w1[M][D][D] and w2[M][D][D] (device
  * pointers, fp32; W[l][j][k] is the weight of input k in output j) and
  * precomputes every layer's filter spectra.  Synchronous.  Errors as
- * fi_create (FI_ERR_INVALID for an unknown act or M < 1). */
+ * fi_create (FI_ERR_INVALID for an unknown act or M < 1;
+ * FI_ERR_UNSUPPORTED for D > 8192). */
 int fi_stack_create(const fi_stack_config *cfg, const float *rho, const float *w1, const float *w2,
                     fi_stack **out);
 
 /* fi_stack_run: generates all L positions from x0[B][D]: y[B][L][D]
  * receives a^M_t, x_out[B][L][D] (or NULL) the inputs x_t; noise[B][L][D]
- * (or NULL: no noise) is scaled by sigma.  Asynchronous on the stream (two
- * launches per position); each call starts from position 0.  Device
- * pointers, owned by the caller until the stream has passed the call. */
+ * (or NULL: no noise) is scaled by sigma.  Each call starts from position 0.
+ * It first waits for the stream to pass the handle's earlier runs, then
+ * queues one launch per position (two where the position completes a tile
+ * of side > 16) and returns: device pointers, owned by the caller until the
+ * stream has passed the call.  A position's layers run on up to 16
+ * workgroups that wait for each other's partial products; a wait past its
+ * limit (about a second: the workgroups could not all be resident) leaves
+ * garbage in that run's outputs and makes this and every later call on the
+ * handle return FI_ERR_HIP.  L M must not exceed 2^30 (FI_ERR_UNSUPPORTED
+ * at fi_stack_create). */
 int fi_stack_run(fi_stack *s, const float *x0, const float *noise, float sigma, float *y, float *x_out);
 
 /* fi_stack_destroy: synchronise the stream and free everything; NULL is a no-op. */
