@@ -33,7 +33,9 @@ if ROOT not in sys.path:
 
 METRIC = "mixer tokens/sec (B·L/s) at D=1024, L=16K; % HBM roofline"
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_run_hyena-d1024-l16k_traffic.json")
+def traffic_file(workload: str) -> str:
+    """The committed counter summary of k_run on one workload."""
+    return os.path.join(ROOT, "profiles", f"k_run_{workload}_traffic.json")
 KERNEL_SOURCES = ["exact_online_amd/csrc/fi_kernels.hip", "exact_online_amd/csrc/fi_device.hpp",
                   "exact_online_amd/csrc/fi_internal.h"]
 
@@ -74,7 +76,7 @@ def load_traffic(sha: str, workload: str, mode: str):
     """The committed counter summary's HBM bytes per launch, when it was taken
     on this kernel source, workload and mode; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -107,10 +109,11 @@ def _counter_rows(path: str, kernel_regex: str):
     return list(per.values())
 
 
-def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, command):
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, command, workload, mode):
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, in KiB per
     dispatch, of k_run and of a plain copy of copy_mib MiB) into HBM bytes per
-    k_run launch, each counter scaled by what it reads for the copy."""
+    k_run launch on `workload` in `mode`, each counter scaled by what it reads
+    for the copy."""
     mean = lambda v: sum(v) / len(v)
     nbytes = copy_mib * (1 << 20)
     kf = mean(_counter_rows(fetch_dir, r"k_run"))
@@ -119,7 +122,7 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib
     cw = mean(_counter_rows(copy_write_dir, r"neg"))
     f_scale = nbytes / (cf * 1024.0)
     w_scale = nbytes / (cw * 1024.0)
-    out = {"kernel": "k_run", "workload": "hyena-d1024-l16k", "mode": "closed-loop tanh",
+    out = {"kernel": "k_run", "workload": workload, "mode": mode,
            "kernel_source_sha": kernel_source_sha(),
            "fetch_kib_per_launch": kf, "write_kib_per_launch": kw,
            "copy_bytes": nbytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
@@ -128,11 +131,37 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib
            "hbm_write_bytes_per_launch": round(kw * 1024.0 * w_scale),
            "command": command}
     out["hbm_bytes_per_launch"] = out["hbm_read_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
     return 0
+
+
+def run_mode(closed: bool, prompt: int) -> str:
+    return (f"prompt of {prompt}, then closed-loop tanh" if prompt else
+            "closed-loop tanh" if closed else "open loop")
+
+
+def cpu_points(w, h, x, n: int, seed: int = 5):
+    """The oracle on n sampled (b, c, t) outputs of an open-loop run (each
+    costs t + 1 multiply-adds), single-threaded: the check the parity tests
+    make at full size."""
+    import numpy as np
+
+    import oracle
+    r = np.random.default_rng(seed)
+    bs = r.integers(0, w.B, n)
+    cs = r.integers(0, w.D, n)
+    ts = r.integers(0, w.L, n)
+    orc = oracle.Oracle(threads=1)
+    t0 = time.perf_counter()
+    for b, c, t in zip(bs, cs, ts):
+        orc.conv_points(np.ascontiguousarray(h[:, c]), np.ascontiguousarray(x[b, :, c]), [int(t)])
+    dt = time.perf_counter() - t0
+    return {"pairs": n, "seconds": round(dt, 3), "us_per_pair": round(dt / n * 1e6, 1), "threads": 1,
+            "sample": f"{n} uniform (b, c, t) outputs, seed {seed}, fp64, one thread (each pays its "
+                      f"channel's column copies, L = {w.L})"}
 
 
 def copy_probe(mib: int, reps: int = 5) -> int:
@@ -459,6 +488,8 @@ def main() -> int:
                     help="time the oracle on this many channels at all positions (default: a sample "
                          "sized to about 10-30 s, see oracle_sample)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-points", type=int, default=0, metavar="N",
+                    help="also time the oracle on N sampled outputs (open loop)")
     ap.add_argument("--per-token", action="store_true",
                     help="time the online interface fi_step one position per call instead")
     ap.add_argument("--prompt", type=int, default=0, metavar="P",
@@ -477,8 +508,12 @@ def main() -> int:
     ap.add_argument("--traffic-command", default="", help="recorded with --write-traffic")
     args = ap.parse_args()
     if args.write_traffic:
+        import workloads
         a = args.write_traffic
-        return write_traffic(a[0], a[1], a[2], a[3], int(a[4]), args.traffic_command)
+        w = workloads.get(args.workload)
+        closed = (args.mode or w.modes[0]) == "closed"
+        return write_traffic(a[0], a[1], a[2], a[3], int(a[4]), args.traffic_command, w.name,
+                             run_mode(closed, args.prompt))
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): the path shards "
@@ -580,8 +615,7 @@ def main() -> int:
     s_x = 2 if w.dtype == "bf16" else 4
     fed = w.L - P if P else None
     ab = algorithmic_bytes(w.B, w.D, w.L, s_x, s_x, 128, closed, fed)
-    mode = (f"prompt of {P}, then closed-loop tanh" if P else
-            "closed-loop tanh" if closed else "open loop")
+    mode = run_mode(closed, P)
     achieved = ab / (kern_ms * 1e-3) / 1e9
     sha = kernel_source_sha()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -594,9 +628,13 @@ def main() -> int:
         progress("bench: timing the CPU oracle on a sample of the workload")
         cpu = cpu_baseline(w, h, None if P else xh, closed, prompt, args.cpu_channels)
         progress(f"bench: oracle {cpu['sample']}")
+        if args.cpu_points and not closed and not P:
+            cpu["points"] = cpu_points(w, h, xh, args.cpu_points)
+            progress(f"bench: oracle on sampled outputs {cpu['points']}")
     value = w.B * w.L / (ms_step * 1e-3)
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC if w.name == "hyena-d1024-l16k" else "mixer tokens/sec (B·L/s); % HBM roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
