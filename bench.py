@@ -381,6 +381,28 @@ def phases(args, w, fi, torch) -> int:
     if blocks > 0:
         for k in range(4):
             out["chain_cycles_per_position"][str(k)] = round(mean[2 + k] / (blocks * 64), 2)
+    # where the teams' wavefronts ran (XCC id << 32 | HW_ID: SIMD in bits
+    # 4-5, CU in 8-11, shader array 12, shader engine 13-15)
+    from collections import Counter
+
+    def where(v):
+        v = int(v)
+        hw = v & 0xFFFFFFFF
+        return (v >> 32, (hw >> 13) & 7, (hw >> 12) & 1, (hw >> 8) & 15), (hw >> 4) & 3
+    if S > 15 and teams[:, 14].any():
+        wc = [where(v) for v in teams[:, 14]]
+        wh = [where(v) for v in teams[:, 15]]
+        chains = Counter(wc)
+        waves = Counter(wc + wh)
+        out["placement"] = {
+            "cus": len({c for c, _ in wc + wh}),
+            "teams_per_cu": dict(Counter(Counter(c for c, _ in wc).values())),
+            "chain_wavefronts_per_simd_holding_one": dict(Counter(chains.values())),
+            "wavefronts_per_simd": dict(Counter(waves.values())),
+            "teams_with_both_wavefronts_on_one_simd": int(sum(a == b for a, b in zip(wc, wh))),
+            "chain_simd_index": dict(Counter(sd for _, sd in wc)),
+            "helper_simd_index": dict(Counter(sd for _, sd in wh)),
+        }
     ser = rec[4 + G * S:4 + G * S + 8 * N].reshape(N, 8)
     if N and ser[0, 0] > 0:
         t_us = (ser[:, 0] - ser[0, 0]) / mhz
@@ -499,7 +521,7 @@ def main() -> int:
                     help="phase breakdown of one pass from the phase-timing build "
                          "(python exact_online_amd/build.py --profile)")
     ap.add_argument("--stack", default="", metavar="NAME",
-                    help="time the layer stack workload NAME (e.g. stack-m18-d256-l16k) instead")
+                    help="time the layer stack workload NAME (e.g. stack-m18-d256-l32k) instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--write-traffic", nargs=5,

@@ -33,6 +33,8 @@ enum {
     kPfPrologue = 11,  // chain wavefront: block start to its first chain step (part of kPfChainRest)
     kPfEpilogue = 12,  // chain wavefront: last chain step to the barrier (part of kPfChainRest)
     kPfLoadWait = 13,  // the wait for the block's loads after its chain (part of kPfEpilogue)
+    kPfHwChain = 14,   // where the chain wavefront runs: XCC id << 32 | HW_ID register
+    kPfHwHelper = 15,  // the same for the team's other wavefront
     kPfTile = 16,      // + q: the block-boundary tile of side 2^q, barriers included
     kPfTileCount = 40  // + q: how many such tiles
 };

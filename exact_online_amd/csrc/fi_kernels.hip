@@ -1331,6 +1331,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     // build and all of this folds away): the chain wavefront's cycle sums,
     // per-level tile sums and counts in LDS.
     __shared__ unsigned long long s_pf[kProfile ? 2 * 24 : 1];
+    __shared__ unsigned long long s_hw[kProfile ? 2 : 1];   // each wavefront's XCC id and HW_ID
     [[maybe_unused]] unsigned long long pf_t0 = 0, pf_tb = 0, pf_tc = 0, pf_td = 0, pf_te = 0;
     [[maybe_unused]] unsigned long long pf_setup = 0, pf_chain = 0, pf_wait = 0, pf_store = 0;
     [[maybe_unused]] unsigned long long pf_blocks = 0, pf_chans = 0;
@@ -1339,6 +1340,12 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     if constexpr (kProfile) {
         pf_t0 = clock64();
         for (int q = tid; q < 2 * 24; q += kTeam) s_pf[q] = 0;
+        if (lane == 0) {
+            // s_getreg operands: (size - 1) << 11 | offset << 6 | register (HW_ID = 4, XCC_ID = 20)
+            const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+            const unsigned xcc = __builtin_amdgcn_s_getreg((15 << 11) | 20);
+            s_hw[chain_wave ? 0 : 1] = ((unsigned long long)xcc << 32) | hw;
+        }
     }
 
     for (int64_t ch = ch0; ch < d.C; ch += G) {
@@ -1800,6 +1807,8 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             o[kPfPrologue] = pf_pro;
             o[kPfEpilogue] = pf_epi;
             o[kPfLoadWait] = pf_vm;
+            o[kPfHwChain] = s_hw[0];
+            o[kPfHwHelper] = s_hw[1];
             for (int q = 0; q < 24; ++q) {
                 o[kPfTile + q] = s_pf[q];
                 o[kPfTileCount + q] = s_pf[24 + q];

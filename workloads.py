@@ -199,8 +199,8 @@ class StackWorkload:
 STACKS = {
     # small: every output checkable against the full oracle in seconds
     "stack-m3-d32-l1k": StackWorkload("stack-m3-d32-l1k", 2, 32, 1024, 3),
-    # the pages' Hyena sweep at its smallest width and depth (M = 18, D = 256)
-    "stack-m18-d256-l16k": StackWorkload("stack-m18-d256-l16k", 1, 256, 16384, 18),
+    # the smallest point of the pages' Hyena sweep (M = 18, D = 256, L = 2^15)
+    "stack-m18-d256-l32k": StackWorkload("stack-m18-d256-l32k", 1, 256, 32768, 18),
 }
 
 
