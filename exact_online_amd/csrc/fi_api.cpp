@@ -8,6 +8,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -192,13 +193,30 @@ int build(fi_handle *s, const void *h) {
     return FI_OK;
 }
 
+// The int a caller put in an enum-typed field or argument, read as its
+// bytes: a value outside the enumeration is not one the enum type may hold,
+// so it is never loaded as that type.
+template <typename E>
+int raw_int(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "an int-sized enum");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 // Validation shared by fi_create and fi_conv_static; fills the handle's
 // configuration fields.
 int configure(const fi_config *cfg, fi_handle *s) {
     if (cfg->B < 1 || cfg->D < 1 || cfg->L < 1) return FI_ERR_INVALID;
-    const int dt = static_cast<int>(cfg->io_dtype);   // the caller may store any int there
+    const int dt = raw_int(cfg->io_dtype);   // the caller may store any int there
     if (dt != FI_F32 && dt != FI_BF16) return FI_ERR_INVALID;
-    int T = cfg->small_tile_max == 0 ? FI_DEFAULT_SMALL_TILE_MAX : cfg->small_tile_max;
+    int T = cfg->small_tile_max;
+    if (T == 0) {
+        // left to the library: the environment's FI_SMALL_TILE_MAX (an
+        // ablation override) or the default
+        const char *env = std::getenv("FI_SMALL_TILE_MAX");
+        T = env && *env ? std::atoi(env) : FI_DEFAULT_SMALL_TILE_MAX;
+    }
     if (!is_pow2(T) || T < 64 || T > 256) return FI_ERR_INVALID;
     // sizes: every element count must fit comfortably in int64 and the
     // per-channel position index in int32 kernels' loop bounds
@@ -287,7 +305,7 @@ int fi_step(fi_handle *s, const void *x_t, float *y_t) {
 
 int fi_run_closed_loop(fi_handle *s, const void *x_in, fi_feedback fb, float *y, void *x_out) {
     if (!s || !x_in || !y) return FI_ERR_INVALID;
-    const int fbv = static_cast<int>(fb);   // the caller may pass any int
+    const int fbv = raw_int(fb);   // the caller may pass any int
     if (fbv != FI_FEEDBACK_NONE && fbv != FI_FEEDBACK_TANH) return FI_ERR_INVALID;
     if (s->pos != 0) return FI_ERR_STATE;
     const int mode = fbv == FI_FEEDBACK_TANH ? fi::kRunClosed : fi::kRunOpen;
@@ -313,7 +331,7 @@ int fi_run_prompted(fi_handle *s, const void *x_prompt, int64_t p, float *y, voi
 int fi_conv_static(const fi_config *cfg, const void *h, const void *x_in, fi_feedback fb, float *y,
                    void *x_out) {
     if (!cfg || !h || !x_in || !y) return FI_ERR_INVALID;
-    const int fbv = static_cast<int>(fb);   // the caller may pass any int
+    const int fbv = raw_int(fb);   // the caller may pass any int
     if (fbv != FI_FEEDBACK_NONE && fbv != FI_FEEDBACK_TANH) return FI_ERR_INVALID;
     fi_handle s;   // host-side only: its device buffers are carved from the workspace
     int rc = configure(cfg, &s);
@@ -459,7 +477,7 @@ int fi_stack_create(const fi_stack_config *cfg, const float *rho, const float *w
                     fi_stack **out) {
     if (out) *out = nullptr;
     if (!cfg || !rho || !w1 || !w2 || !out) return FI_ERR_INVALID;
-    const int act = static_cast<int>(cfg->act);
+    const int act = raw_int(cfg->act);
     if (act != FI_ACT_GELU && act != FI_ACT_TANH && act != FI_ACT_IDENTITY) return FI_ERR_INVALID;
     const int64_t lim = (int64_t)1 << 31;
     if (cfg->M < 1 || cfg->B < 1 || cfg->M >= lim || cfg->B >= lim || cfg->M > lim / cfg->B) return FI_ERR_INVALID;

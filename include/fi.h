@@ -82,8 +82,9 @@ typedef struct {
     fi_dtype io_dtype;       /* FI_F32 or FI_BF16 (an int-sized enum) */
     void *stream;            /* hipStream_t the handle works on; NULL = the null stream */
     int32_t small_tile_max;  /* T: the largest tile side fi_step does as a direct product, tiles of
-                                side > T being FFT tiles; 0 = FI_DEFAULT_SMALL_TILE_MAX; otherwise
-                                64, 128 or 256.  The persistent pass (fi_run_closed_loop,
+                                side > T being FFT tiles: 64, 128 or 256; 0 = the environment's
+                                FI_SMALL_TILE_MAX when set (an override for ablations; any other
+                                value there gives FI_ERR_INVALID), else FI_DEFAULT_SMALL_TILE_MAX.  The persistent pass (fi_run_closed_loop,
                                 fi_run_prompted) does every tile of side < 256 directly whatever T
                                 is; it does the tile of side 256 from LDS when T = 256, else on
                                 the matrix cores, and the larger ones by FFT. */
