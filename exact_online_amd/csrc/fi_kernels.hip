@@ -1199,12 +1199,14 @@ __device__ __forceinline__ void mm_tile256(const FI_SHARED float* xz, const FI_S
 // decimated order, lag d + 16 (alpha - bt): with the filter copy hz holding
 // h[g] for g in [-256, 256) at slot s(g) = (g + 256) + (g + 256) / 16 (zero
 // at negative lags), G = 256 + d - 64 c.  bt = 4c + kk <= 15 suffices (larger
-// bt only meets negative lags): 64 steps.  Returns init + the triangle, by
-// the calling wavefront, in MFMA layout.
-__device__ __forceinline__ v4f mm_triangle256(const FI_SHARED float* xz, const FI_SHARED float* hz, v4f init) {
+// bt only meets negative lags): 64 steps, split by d between the team's two
+// wavefronts (mm_triangle_half<0> from init, mm_triangle_half<8> from zero),
+// each result in MFMA layout.
+template <int D0>
+__device__ __forceinline__ v4f mm_triangle_half(const FI_SHARED float* xz, const FI_SHARED float* hz, v4f init) {
     const int l = team_tid() & (kWave - 1);
     const int al = l & 15, kk = l >> 4;
-    return mm_toeplitz<4, 256>(hz + 17 * (al - kk), xz + al + 16 * kk, init);
+    return mm_toeplitz<4, 256, D0, 8>(hz + 17 * (al - kk), xz + al + 16 * kk, init);
 }
 
 constexpr int kTapBatch = 4;         // chain: taps loaded per batch, one batch ahead
@@ -1466,6 +1468,17 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                                                          (FI_SHARED void*)(xst + k), 4, 0, 0);
                 }
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                // an open block's own triangle: this wavefront forms the
+                // products d >= 8 and hands them over through LDS (the first
+                // 256 floats of the FFT region, which no staging reaches)
+                if (open_block(t0)) {
+                    team_sync();   // the chain wavefront has written the block's inputs
+                    const v4f yh = mm_triangle_half<8>(mxz, hz, v4f{0.f, 0.f, 0.f, 0.f});
+                    FI_SHARED float* part = reinterpret_cast<FI_SHARED float*>(lbuf);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) part[4 * lane + r] = yh[r];
+                    team_sync();
+                }
             }
             if (chain_wave) {
                 // the serial chain goes first wherever it shares a SIMD with
@@ -1507,7 +1520,8 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 const int pl = (int)(P - t0);   // given inputs of a boundary block
                 if (openb) {
                     // every input of the block is known, so its own
-                    // triangle is one matrix-core product (mm_triangle256) on
+                    // triangle is one matrix-core product (mm_triangle_half on
+                    // each wavefront) on
                     // top of the ring's accumulators; the inputs go to the
                     // padded block the product (and the tile of side kBlk at
                     // the block's end) reads, and y comes back to the lane
@@ -1519,8 +1533,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     v4f init;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) init[r] = accw[al + 16 * (4 * kk + r)];
-                    wave_sync();
-                    const v4f yq = mm_triangle256(mxz, hz, init);
+                    // the products d < 8 here, d >= 8 on the other wavefront
+                    team_sync();
+                    v4f yq = mm_triangle_half<0>(mxz, hz, init);
+                    team_sync();
+                    const FI_SHARED float* part = reinterpret_cast<const FI_SHARED float*>(lbuf);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) yq[r] += part[4 * lane + r];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) myb[al + 16 * (4 * kk + r)] = yq[r];
                     wave_sync();

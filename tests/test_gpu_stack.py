@@ -149,3 +149,29 @@ def test_stack_runs_are_deterministic():
         s.run(to_dev(x0, "f32"), y2, None, nzd, w.sigma)
         torch.cuda.synchronize()
     assert torch.equal(y, y2)
+
+
+def test_stack_benchmark_size_prefix_and_sampler():
+    """The benchmark's stack (M = 18, D = 256, L = 2^15, the launch bench.py
+    times): the first 512 outputs depend on nothing later, so they must match
+    the oracle's stack over that prefix.  Eighteen blocks damp the signal to
+    ~1e-8 there, so the bound is relative: rel L2 <= 1e-4 free-running and
+    teacher-forced.  At every position the output is finite and the recorded
+    input is the sampler applied to the previous output."""
+    w = workloads.get_stack("stack-m18-d256-l32k")
+    P = 512
+    rho, w1, w2, x0, nz = _inputs(w)
+    log("case stack benchmark size", w.name)
+    y, xo = gpu_stack(rho, w1, w2, x0, nz, w.sigma, "gelu")
+    assert np.isfinite(y).all() and np.isfinite(xo).all()
+    fb = np.abs(xo[:, 1:] - (y[:, :-1] + np.float32(w.sigma) * nz[:, :-1].astype(np.float64))).max()
+    scale = max(1.0, float(np.abs(y).max()))
+    orc = oracle.default()
+    yr, xr = orc.conv_stack(rho[:, :P], w1, w2, x0, noise=nz[:, :P], sigma=np.float32(w.sigma), act="gelu")
+    ytf, _ = orc.conv_stack(rho[:, :P], w1, w2, xo[:, :P], act="gelu", teacher_forced=True)
+    rel = lambda a, b: float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    free, tf = rel(y[:, :P], yr), rel(y[:, :P], ytf)
+    log("sampler", fb, "prefix rel L2 free-running", free, "teacher-forced", tf, "max |y|", float(np.abs(y).max()))
+    assert fb <= 1e-6 * scale
+    assert tf <= 1e-4
+    assert free <= 1e-4
