@@ -305,10 +305,18 @@ def per_token(args, w, fi, torch) -> int:
     for u in np.unique(U):
         sel = us[U == u]
         by_u[str(int(u))] = {"count": int(sel.size), "mean_us": round(float(sel.mean()), 2)}
+    # the method's bytes for the whole sequence (every red cell and tile, open
+    # loop, at this T) over the calls' summed GPU time
+    s_x = 2 if w.dtype == "bf16" else 4
+    ab = algorithmic_bytes(w.B, w.D, w.L, s_x, s_x, T, False)
+    gbs = ab / (us.sum() * 1e-6) / 1e9
     out = {"metric": "fi_step GPU time per token", "unit": "us", "workload": w.name,
            "B": w.B, "D": w.D, "L": w.L, "io_dtype": w.dtype, "small_tile_max": T,
            "mean_us": round(float(us.mean()), 2), "median_us": round(float(np.median(us)), 2),
            "p99_us": round(float(np.percentile(us, 99)), 2), "max_us": round(float(us.max()), 2),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 5), "algorithmic_bytes": ab,
+                        "note": "launch-bound: one or two launches per position"},
            "wall_us_per_token": round(wall / w.L * 1e6, 2),
            "by_tile_side": by_u}
     print(json.dumps(out), flush=True)
