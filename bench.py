@@ -484,8 +484,9 @@ def stack_bench(args, fi, torch) -> int:
         t1 = time.perf_counter()
         orc.conv_stack(rho[:, :P], w1, w2, x0, noise=nz[:, :P], sigma=np.float32(w.sigma), act="gelu")
         sec = time.perf_counter() - t1
+        _, cpus, model = host_cpu()
         cpu = {"value": round(w.B * P / sec, 2), "unit": "tokens/s", "cores": min(w.B, orc.threads),
-               "kind": "oracle", "cpu_model": host_cpu(),
+               "kind": "oracle", "host_cpus": cpus, "cpu_model": model,
                "sample": f"the first {P} of {w.L} positions, all {w.B} batch rows and {w.M} layers, "
                          f"{sec:.1f} s (one thread per batch row; later positions cost more, "
                          f"so the full sequence runs slower than this rate)"}
