@@ -85,6 +85,17 @@ def test_stack_ragged(L, T, act):
     check(rho, w1, w2, x0, nz, w.sigma, act, T)
 
 
+@pytest.mark.parametrize("B,D,L,M", [(1, 768, 300, 2), (1, 864, 200, 2), (2, 100, 300, 3), (3, 17, 129, 4)])
+def test_stack_widths(B, D, L, M):
+    """Widths of the pages' sweep (768, 864: each workgroup streams its
+    slice's weights instead of holding them in registers) and uneven slices
+    (100 and 17 channels over 16 workgroups)."""
+    w = workloads.get_stack("stack-m3-d32-l1k").with_(B=B, D=D, L=L, M=M, seed=D + L)
+    log("case stack widths B", B, "D", D, "L", L, "M", M)
+    rho, w1, w2, x0, nz = _inputs(w)
+    check(rho, w1, w2, x0, nz, w.sigma)
+
+
 @pytest.mark.parametrize("L,D", [(16384, 8), (1 << 15, 4)])
 def test_stack_fft_tiles(L, D):
     """Tiles up to L/2 points (the LDS routes, the two-half 8192-point tile,
