@@ -411,6 +411,12 @@ def phases(args, w, fi, torch) -> int:
             "chain_simd_index": dict(Counter(sd for _, sd in wc)),
             "helper_simd_index": dict(Counter(sd for _, sd in wh)),
         }
+        # pairs: the team whose second wavefront shares this team's chain
+        # SIMD has its chain on this team's second wavefront's SIMD
+        helper_at = {v: k for k, v in enumerate(wh)}
+        sym = sum(1 for k in range(len(wc)) if wc[k] in helper_at and wc[helper_at[wc[k]]] == wh[k])
+        out["placement"]["teams_in_symmetric_pairs"] = int(sym)
+        out["placement"]["chain_simd_parity_vs_helper"] = dict(Counter(f"{a[1] % 2}{b[1] % 2}" for a, b in zip(wc, wh)))
     ser = rec[4 + G * S:4 + G * S + 8 * N].reshape(N, 8)
     if N and ser[0, 0] > 0:
         t_us = (ser[:, 0] - ser[0, 0]) / mhz
