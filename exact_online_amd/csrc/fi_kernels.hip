@@ -1892,12 +1892,14 @@ struct ChainArgs {
     unsigned tag0;       // the run's tag base: the word of (t, l) carries tag0 + t M + l + 1
     int P;               // workgroups
     int fuse_u;          // side of the fused tile, 0 for none
-    int pre;             // 1: stage every layer's accumulator at t in LDS first
+    int pre;             // 1: stage every layer's accumulator at t in LDS first; 0 on the register
+                         // path with B <= kChainPreB: each layer prefetches its own
 };
 
 constexpr int kChainThreads = 256;
 constexpr long kChainSpinLimit = 1L << 20;   // about a second of polling
 constexpr int kChainRegs = 16;               // weights per thread and matrix held in registers
+constexpr int kChainPreB = 4;                // batch rows whose accumulators a thread prefetches per layer
 
 __device__ __forceinline__ float stack_act(float v, int act) {
     if (act == 0) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
@@ -1922,9 +1924,16 @@ __device__ __forceinline__ unsigned long long get_word(const unsigned long long*
 // marks the run failed and returns what it has (every wave exits).
 __device__ __forceinline__ float gather_sum(const unsigned long long* w, int64_t stride, int P, unsigned tag,
                                             int* fail) {
+    // every load unconditional (slots past P read the last workgroup's word
+    // and are replaced by a zero that carries the tag): a load under a
+    // per-lane branch would wait for the ones before it
     unsigned long long x[kChainMaxWorkgroups];
+    const unsigned long long zero = tagged(tag, 0.f);
 #pragma unroll
-    for (int q = 0; q < kChainMaxWorkgroups; ++q) x[q] = q < P ? get_word(w + q * stride) : tagged(tag, 0.f);
+    for (int q = 0; q < kChainMaxWorkgroups; ++q) {
+        const unsigned long long v = get_word(w + (q < P ? q : P - 1) * stride);
+        x[q] = q < P ? v : zero;
+    }
     for (long spins = 0;; ++spins) {
         bool ready = true;
 #pragma unroll
@@ -1936,8 +1945,10 @@ __device__ __forceinline__ float gather_sum(const unsigned long long* w, int64_t
         }
         __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-        for (int q = 0; q < kChainMaxWorkgroups; ++q)
-            if ((unsigned)(x[q] >> 32) != tag) x[q] = get_word(w + q * stride);
+        for (int q = 0; q < kChainMaxWorkgroups; ++q) {
+            const unsigned long long v = get_word(w + (q < P ? q : P - 1) * stride);
+            x[q] = ((unsigned)(x[q] >> 32) == tag) ? x[q] : (q < P ? v : zero);
+        }
     }
     float s = 0.f;
 #pragma unroll
@@ -1996,7 +2007,7 @@ __device__ __forceinline__ void tile_small(const DevState& d, int64_t i, int64_t
 
 // The register plan of a slice (REGW): W1's rows of the slice, TPR threads
 // per row (a power of two <= 64), KC weights each; W2's columns of the
-// slice, IC outputs per thread, ns weights each.
+// slice, one output per thread (IC = 1: D <= kChainThreads), ns weights.
 struct ChainRegPlan {
     int tpr, kc, ic;
 };
@@ -2014,7 +2025,17 @@ __host__ __device__ inline ChainRegPlan chain_reg_plan(int64_t D, int64_t ns) {
 
 __host__ __device__ inline bool chain_regs_fit(int64_t D, int64_t ns) {
     const ChainRegPlan r = chain_reg_plan(D, ns);
-    return r.tpr > 0 && r.kc <= kChainRegs && ns * r.ic <= kChainRegs;
+    return r.tpr > 0 && r.kc <= kChainRegs && r.ic == 1 && ns <= kChainRegs;
+}
+
+// A workgroup barrier that orders LDS only: a thread passes it without
+// waiting for its global stores (the tagged words and parked inputs need no
+// order among the workgroup's threads; the parked inputs are released by
+// every thread's own fence before the last layer's words).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <bool REGW>
@@ -2044,6 +2065,10 @@ __global__ __launch_bounds__(kChainThreads) void k_stack_chain(ChainArgs a) {
             }
         }
     }
+    lds_barrier();   // the staged accumulators, for every thread
+    // per-layer prefetch of the red cell's operands instead of the staging
+    const bool pf = REGW && a.pre == 0 && B <= kChainPreB;
+    static_assert(kChainPreB == 4, "the red cell selects among four prefetched rows");
     const ChainRegPlan rp = chain_reg_plan(D, ns);
     const int row = REGW ? tid / rp.tpr : 0, li = REGW ? tid % rp.tpr : 0;
     const unsigned tag_t = a.tag0 + (unsigned)(t * M);
@@ -2052,18 +2077,35 @@ __global__ __launch_bounds__(kChainThreads) void k_stack_chain(ChainArgs a) {
         const unsigned long long* prev = a.part + ((l - 1) & 1) * P * B * D;
         unsigned long long* mine = a.part + ((l & 1) * P + p) * B * D;
         // this layer's weights of the slice, in flight while the inputs arrive
+        // (loaded unconditionally from a clamped in-range index, then zeroed
+        // where unused: the zero weights cancel the clamped operands below)
         float w1r[REGW ? kChainRegs : 1], w2r[REGW ? kChainRegs : 1];
         if (REGW) {
+            const int64_t rr = row < ns ? row : ns - 1;
 #pragma unroll
             for (int m = 0; m < kChainRegs; ++m) {
                 const int64_t k = li + (int64_t)m * rp.tpr;
-                w1r[m] = (m < rp.kc && row < ns && k < D) ? a.w1[(l * D + j0 + row) * D + k] : 0.f;
+                const bool ok = m < rp.kc && row < ns && k < D;
+                const float v = a.w1[(l * D + j0 + rr) * D + (k < D ? k : D - 1)];
+                w1r[m] = ok ? v : 0.f;
             }
+            const int64_t ic = tid < D ? tid : D - 1;
 #pragma unroll
             for (int m = 0; m < kChainRegs; ++m) {
-                const int64_t jj = m / (rp.ic > 0 ? rp.ic : 1), i = tid + (int64_t)(m % (rp.ic > 0 ? rp.ic : 1)) * kChainThreads;
-                w2r[m] = (jj < ns && i < D && m < ns * rp.ic) ? a.w2t[(l * D + j0 + jj) * D + i] : 0.f;
+                const bool ok = m < ns && tid < D;
+                const float v = a.w2t[(l * D + j0 + (m < ns ? m : ns - 1)) * D + ic];
+                w2r[m] = ok ? v : 0.f;
             }
+        }
+        // the red cell's lag-0 tap and accumulators at t of this thread's
+        // channel (c = tid on the register path), in flight with the weights
+        float h0r = 0.f, accr[kChainPreB];
+        if (pf) {
+            const int64_t c = tid < D ? tid : D - 1;
+            h0r = d.hT[(l * D + c) * LS];
+#pragma unroll
+            for (int bb = 0; bb < kChainPreB; ++bb)
+                accr[bb] = d.state[((l * B + (bb < B ? bb : B - 1)) * D + c) * LS + t];
         }
         for (int64_t b = 0; b < B; ++b) {
             // the red cell: the tiles' accumulation plus the lag-0 term; the
@@ -2073,14 +2115,21 @@ __global__ __launch_bounds__(kChainThreads) void k_stack_chain(ChainArgs a) {
                 const float v = l == 0 ? (t == 0 ? a.x0[b * D + c] : a.xnext[b * D + c])
                                        : gather_sum(prev + b * D + c, B * D, P, tag_prev, a.fail);
                 const int64_t ch = (l * B + b) * D + c;
-                const float acc = a.pre ? accp[ch] : d.state[ch * LS + t];
-                zv[c] = __builtin_fmaf(d.hT[(l * D + c) * LS], v, acc);
+                float acc, h0;
+                if (pf) {
+                    acc = b == 0 ? accr[0] : b == 1 ? accr[1] : b == 2 ? accr[2] : accr[3];
+                    h0 = h0r;
+                } else {
+                    acc = a.pre ? accp[ch] : d.state[ch * LS + t];
+                    h0 = d.hT[(l * D + c) * LS];
+                }
+                zv[c] = __builtin_fmaf(h0, v, acc);
                 if (c >= j0 && c < j1) {
                     a.hist[ch] = v;
                     if (l == 0 && t == 0 && a.x_out) a.x_out[(b * L) * D + c] = v;
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // the parked inputs of every layer (this row's of the last layer
             // included) before the last layer's words
             if (l == M - 1) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -2090,22 +2139,16 @@ __global__ __launch_bounds__(kChainThreads) void k_stack_chain(ChainArgs a) {
 #pragma unroll
                 for (int m = 0; m < kChainRegs; ++m) {
                     const int64_t k = li + (int64_t)m * rp.tpr;
-                    if (m < rp.kc && k < D) s = __builtin_fmaf(w1r[m], zv[k], s);
+                    s = __builtin_fmaf(w1r[m], zv[k < D ? k : D - 1], s);
                 }
                 for (int o = rp.tpr >> 1; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
                 if (li == 0 && row < ns) hv[row] = stack_act(s, a.act);
-                __syncthreads();
-                // this slice's share of W2 h, every output
-                for (int m2 = 0; m2 < rp.ic; ++m2) {
-                    const int64_t i = tid + (int64_t)m2 * kChainThreads;
-                    float acc = 0.f;
+                lds_barrier();
+                // this slice's share of W2 h, every output (one per thread)
+                float acc = 0.f;
 #pragma unroll
-                    for (int m = 0; m < kChainRegs; ++m) {
-                        const int64_t jj = m / rp.ic;
-                        if (m % rp.ic == m2 && jj < ns) acc = __builtin_fmaf(w2r[m], hv[jj], acc);
-                    }
-                    if (i < D) put_word(mine + b * D + i, tagged(tag_mine, acc));
-                }
+                for (int m = 0; m < kChainRegs; ++m) acc = __builtin_fmaf(w2r[m], hv[m < ns ? m : 0], acc);
+                if (tid < D) put_word(mine + b * D + tid, tagged(tag_mine, acc));
             } else {
                 const int wave = tid >> 6, lane = tid & 63;
                 for (int64_t j = j0 + wave; j < j1; j += kChainThreads / 64) {
@@ -2117,7 +2160,7 @@ __global__ __launch_bounds__(kChainThreads) void k_stack_chain(ChainArgs a) {
                     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
                     if (lane == 0) hv[j - j0] = stack_act(s, a.act);
                 }
-                __syncthreads();
+                lds_barrier();
                 for (int64_t i = tid; i < D; i += kChainThreads) {
                     const float* wc = a.w2t + (l * D + j0) * D + i;
                     float acc = 0.f;
@@ -2126,7 +2169,7 @@ __global__ __launch_bounds__(kChainThreads) void k_stack_chain(ChainArgs a) {
                     put_word(mine + b * D + i, tagged(tag_mine, acc));
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
     // a^M on this workgroup's slice: the output, and the sampler's next input
@@ -2273,8 +2316,12 @@ hipError_t launch_stack_chain(const DevState& d, const StackChain& sc, const flo
                               hipStream_t st) {
     ChainArgs a{d, sc.B, sc.M, sc.w1, sc.w2t, x0, noise, sigma, sc.act, sc.xnext, y, x_out, sc.part, sc.hist,
                 sc.fail, t, tag0, sc.P, fuse_u, 0};
-    const size_t lds = (size_t)stack_chain_lds_bytes(sc.B, d.D, sc.M, sc.P, &a.pre);
     const bool regw = chain_regs_fit(d.D, (d.D + sc.P - 1) / sc.P);
+    size_t lds = (size_t)stack_chain_lds_bytes(sc.B, d.D, sc.M, sc.P, &a.pre);
+    if (regw && sc.B <= kChainPreB) {   // each layer prefetches its own accumulators: no staging
+        a.pre = 0;
+        lds = (size_t)(d.D + ((d.D + sc.P - 1) / sc.P + 63) / 64 * 64) * sizeof(float);
+    }
     const void* fn = regw ? (const void*)k_stack_chain<true> : (const void*)k_stack_chain<false>;
     if (lds > 65536) (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (regw) hipLaunchKernelGGL(k_stack_chain<true>, dim3((unsigned)sc.P), dim3(kChainThreads), lds, st, a);
