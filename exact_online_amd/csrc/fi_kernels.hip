@@ -1391,12 +1391,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             __builtin_amdgcn_s_waitcnt(0x0F70);
         }
         if constexpr (kProfile) pf_setup += clock64() - pf_tb;
-        // y and x_out of a block go out during the next block's chain (their
+        // y and x_out of a block go out during the next block (their
         // addresses are D floats apart per position, so each store touches 64
-        // lines; issued between the chain's transcendentals they cost next to
-        // nothing): the chain wavefront leaves them in LDS (myb, mxz) and
-        // stores them from there, as the last use of that LDS before it
-        // rewrites it.  Lane l writes position t0 + 64 k + l of column c.
+        // lines and holds up the wavefront that issues it for about as many
+        // cycles): the chain wavefront leaves them in LDS (myb, mxz).  Before
+        // a chain block the other wavefront stores them; before a block with
+        // known inputs the chain wavefront does, at the block's start.  Lane l
+        // writes position t0 + 64 k + l of column c.
         const uint32_t ylane = (uint32_t)lane * (uint32_t)D;
         bool defer_prev = false;   // the previous block's y / x_out wait in LDS
         auto store_deferred = [&](int64_t tp) {
@@ -1448,6 +1449,34 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     }
                 }
             };
+            // The next block's accumulators beyond the LDS ring: some earlier
+            // tile left them in the row exactly when a bit of base other than
+            // its lowest is set at or above 2 kBlk (the tile of that bit's
+            // level covered them, its ring did not).
+            const int64_t base = t0 + kBlk;
+            const bool nx_in_row = ((base & (base - 1)) >> (kLog2Blk + 1)) != 0;
+            // A closed-loop block that runs the serial chain: the other
+            // wavefront, idle during the chain, issues the previous block's
+            // deferred y / x_out stores from LDS and moves the next block's
+            // accumulators from the row into the ring, work that would
+            // otherwise sit on the chain wavefront's critical path.  It meets
+            // the chain wavefront at the start of the chain's second segment:
+            // by then the chain wavefront has read the ring, and it rewrites
+            // the LDS copies of y / x only after its chain.
+            const bool chain_block = CLOSED && !open_block(t0);
+            float hnx[kRegs];
+            if (!chain_wave && chain_block) {
+                if (defer_prev) store_deferred(t0 - kBlk);
+                team_sync();
+#pragma unroll
+                for (int k = 0; k < kRegs; ++k) {
+                    // loaded from a clamped index, kept where in range: a
+                    // load under a per-lane branch would wait for the stores
+                    const int64_t pn = base + kWave * k + lane;
+                    const float v = row[pn < L ? pn : L - 1];
+                    hnx[k] = (nx_in_row && pn < L) ? v : 0.f;
+                }
+            }
             if (!chain_wave) {
                 // The other wavefront, idle during the chain, stages the next
                 // tile's spectrum and the older part of its input block
@@ -1468,6 +1497,10 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                                                          (FI_SHARED void*)(xst + k), 4, 0, 0);
                 }
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                if (chain_block) {
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) accw[kWave * k + lane] = hnx[k];   // the ring now holds the next block
+                }
                 // an open block's own triangle: this wavefront forms the
                 // products d >= 8 and hands them over through LDS (the first
                 // 256 floats of the FFT region, which no staging reaches)
@@ -1484,7 +1517,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 // the serial chain goes first wherever it shares a SIMD with
                 // another team's tile work
                 __builtin_amdgcn_s_setprio(2);
-                if (defer_prev) store_deferred(t0 - kBlk);
+                if (defer_prev && !chain_block) store_deferred(t0 - kBlk);
                 float xb[kRegs];
 #pragma unroll
                 for (int k = 0; k < kRegs; ++k) {
@@ -1500,17 +1533,17 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         }
                     }
                 }
-                // The accumulators of the next block's positions, from the row:
-                // some earlier tile left them outside its ring exactly when a bit
-                // of base other than its lowest is set at or above 2 kBlk (the
-                // tile of that bit's level covered them, its ring did not).
-                const int64_t base = t0 + kBlk;
-                const bool nx_in_row = ((base & (base - 1)) >> (kLog2Blk + 1)) != 0;
+                // the accumulators of the next block's positions that wait in
+                // the row (the other wavefront moves them in chain blocks)
                 float nx[kRegs];
 #pragma unroll
-                for (int k = 0; k < kRegs; ++k) {
-                    const int64_t pn = base + kWave * k + lane;
-                    nx[k] = (nx_in_row && pn < L) ? row[pn] : 0.f;
+                for (int k = 0; k < kRegs; ++k) nx[k] = 0.f;
+                if (!chain_block) {
+#pragma unroll
+                    for (int k = 0; k < kRegs; ++k) {
+                        const int64_t pn = base + kWave * k + lane;
+                        nx[k] = (nx_in_row && pn < L) ? row[pn] : 0.f;
+                    }
                 }
                 float xstart = 0.f;
                 const bool openb = open_block(t0);
@@ -1637,6 +1670,9 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         }
                     };
                     auto timed = [&](auto kc, auto bndc) {
+                        // the other wavefront has taken what it stores and
+                        // moves (see chain_block): meet it here
+                        if constexpr (decltype(kc)::value == 1) team_sync();
                         [[maybe_unused]] unsigned long long ts = 0;
                         if constexpr (kProfile) {
                             ts = clock64();
@@ -1671,7 +1707,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
 #pragma unroll
                     for (int k = 0; k < kRegs; ++k) {
                         const float prev = k == 0 ? xstart : readlane(f[k - 1], kWave - 1);
-                        const float sh = __shfl_up(f[k], 1);
+                        const float sh = wave_shr1(f[k]);
                         xk[k] = lane == 0 ? prev : sh;
                         if (bnd && t0 + kWave * k + lane < P) xk[k] = xb[k];   // given
                         p[k] *= 1.0f / kTanhScale;
@@ -1690,8 +1726,10 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 }
                 // p now holds y of the block (lane m's accumulator stopped
                 // changing at step m: later pushes carry a zero tap there)
+                if (!chain_block) {
 #pragma unroll
-                for (int k = 0; k < kRegs; ++k) accw[kWave * k + lane] = nx[k];   // the ring now holds the next block
+                    for (int k = 0; k < kRegs; ++k) accw[kWave * k + lane] = nx[k];   // the ring now holds the next block
+                }
                 if (direct) {
 #pragma unroll
                     for (int k = 0; k < kRegs; ++k) xring[(t0 + kWave * k + lane) & xmask] = xk[k];
