@@ -46,15 +46,28 @@ constexpr int kTwLds = 132;       // LDS twiddle table: w_64^a, w_4096^b (64 eac
 constexpr int kTapTableBytes = (64 + kRunBlock + 4) * 16;
 // LDS FFT buffers hold one spare slot per 8 points (bank spreading).
 constexpr int lds_fft_elems(int M) { return M + M / 8; }
-// The run kernel's tile of side kRunBlock on the matrix cores keeps in its
-// FFT region, above every staging area of the tiles up to 2048 points, the
-// input block zero-padded (15 zeros before, 65 after) and the filter
-// h[-64, 2 kRunBlock) (zero at negative lags) with one spare slot per 16
-// (bank spreading), then the block's outputs y (handed to the other
-// wavefronts, which store them during that tile).
+// The run kernel keeps in its FFT region, above every staging area of the
+// tiles up to 2048 points, the block's inputs zero-padded (15 zeros before,
+// 65 after; the open loop's block triangle on the matrix cores reads them,
+// and the other wavefront stores them as x_out), then the block's outputs y
+// (handed to the other wavefront, which stores them during the next block).
 constexpr int kMmXFloats = 15 + kRunBlock + 65;
-constexpr int kMmHSlots = (64 + 2 * kRunBlock) + (64 + 2 * kRunBlock) / 16 + 4;
-constexpr int kMmBytes = (kMmXFloats + kMmHSlots + kRunBlock) * 4;
+constexpr int kMmBytes = (kMmXFloats + kRunBlock) * 4;
+// The tiles of side kRunBlock and 2 kRunBlock on the matrix cores in fp16
+// halves (hi + lo of each operand, scaled by powers of two) keep, at the
+// bottom of the FFT region above its first KiB (the two wavefronts'
+// hand-over area), the filter table -- lags kH16Lo .. kH16Lo + kH16N - 1,
+// the hi parts then the lo parts -- and three slots of input blocks, each two
+// reversed copies (the second shifted by one position) of hi and of lo parts.
+// FFT tiles of side >= 4 kRunBlock and their staging overwrite the area; it
+// is rebuilt after them.
+constexpr int kH16Lo = -16;
+constexpr int kH16N = 1040;
+constexpr int kX16N = 304;
+constexpr int kH16Off = 1024;
+constexpr int kX16Off = kH16Off + 2 * kH16N * 2;
+constexpr int kX16Slot = 4 * kX16N;   // halfs per slot
+constexpr int kX16End = kX16Off + 3 * kX16Slot * 2;
 // The run kernel's FFT / staging region has one fixed layout (compile-time
 // offsets, whatever L is): the staging area of the largest staged tile (side
 // 2048: its transform buffer and input block; smaller tiles also stage their
@@ -66,6 +79,7 @@ constexpr int kRunFftReg = lds_fft_elems(kLdsFftMax) * 8 > kRunMmOff + kMmBytes 
                                ? lds_fft_elems(kLdsFftMax) * 8
                                : kRunMmOff + kMmBytes + kTapTableBytes;
 static_assert(lds_fft_elems(1024) * 8 + 4 * 1024 + 8 * (1024 + 2) <= kRunMmOff, "staging of the tiles up to 1024 fits");
+static_assert(kX16End <= kRunMmOff && kH16Off % 16 == 0 && kX16Off % 16 == 0, "the fp16 tile area fits below the matrix-core data");
 
 // Device state of one handle.  Layouts (rows padded to LS = L rounded up to 64):
 //   hT[D][LS]      filter, one contiguous row per channel c, fp32

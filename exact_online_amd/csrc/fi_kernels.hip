@@ -1163,34 +1163,175 @@ __device__ __forceinline__ v4f mm_toeplitz(const FI_SHARED float* ab, const FI_S
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-__device__ __forceinline__ void mm_tile256(const FI_SHARED float* xz, const FI_SHARED float* hsk,
+// ------------------------------- tiles of side 256 and 512, fp16 halves
+// The tiles at the block boundaries i with lowbit(i) = 256 or 512 (the
+// relaxed tiling of [FI] "Strategia di Tiling (Algoritmo 1)") as direct
+// Toeplitz products on the matrix cores.  Every product here takes one input
+// block of 256 positions and adds into the next block's accumulators (the
+// LDS ring), with filter lags G + q - p (q, p the output and input offsets in
+// their blocks):
+//   i = 256 mod 512: the tile of side 256, G = 256 (lags 1 .. 511);
+//   i = 512 mod 1024: the tile of side 512 into its first output block --
+//     inputs [i-256, i) with G = 256 and [i-512, i-256) with G = 512;
+//   i = 768 mod 1024: also the second output block of the tile of side 512
+//     formed at i - 256 -- inputs [i-512, i-256) with G = 512 and
+//     [i-768, i-512) with G = 768 -- since those outputs are the block that
+//     now comes next.
+// Outputs q = a + 16 alpha and inputs p = a - d + 16 bt (a, alpha, d < 16):
+// the lag G + d + 16 (alpha - bt) does not depend on a, so with K = (bt, d)
+//   A[alpha][(bt, d)] = h[G + d + 16 (alpha - bt)],  B[(bt, d)][a] = x[a - d + 16 bt]
+// (x = 0 outside the block) the tile is the 16 x 16 product A B, K = 18 x 16
+// (bt < 17 suffices): nine 16x16x32 steps, one per pair of bt values, a lane
+// holding eight consecutive d for one bt.  Each operand is the sum of two
+// fp16 parts, hi = fp16(v) and lo = fp16(v - hi), after an exact power-of-two
+// scaling that puts the largest |v| in [2^13, 2^14): a step is the three
+// products hi hi + hi lo + lo hi, accumulated in fp32, and the result is
+// scaled back exactly.  The part left out, lo lo, and the parts' rounding are
+// below 2^-21 of the largest product.
+// Operands in LDS: A from the filter table (H[lag - kH16Lo], eight
+// consecutive lags, 16-byte aligned); B from the slot's reversed input copies
+// (copy c holds x[287 + c - m] at m, so the eight values x[s], x[s-1], ...,
+// x[s-7] sit at m = 287 - s + c, .. + 7, with c the parity that makes m
+// even: four aligned dwords).
+// MFMA lane layout (16x16x32 f16): A[i][k] in lane i + 16 (k / 8), half k % 8;
+// B[k][j] in lane j + 16 (k / 8); D[i][j] in lane j + 16 (i / 4), register i % 4.
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// The largest |v| over a wavefront (every lane gets it).
+__device__ __forceinline__ float wave_max_abs(float v) {
+    int m = __float_as_int(fabsf(v));   // non-negative floats order as integers
+    m = max(m, __builtin_amdgcn_update_dpp(0, m, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x124, 0xF, 0xF, false));   // row_ror 4
+    m = max(m, __builtin_amdgcn_update_dpp(0, m, 0x128, 0xF, 0xF, false));   // row_ror 8
+    const int r = max(max(__builtin_amdgcn_readlane(m, 0), __builtin_amdgcn_readlane(m, 16)),
+                      max(__builtin_amdgcn_readlane(m, 32), __builtin_amdgcn_readlane(m, 48)));
+    return __int_as_float(r);
+}
+// The scale exponent e with m 2^e < 2^14 (m = the largest magnitude; 14 when m = 0).
+__device__ __forceinline__ int scale16(float m) { return 14 - __builtin_amdgcn_frexp_expf(m); }
+// The fp16 parts of v 2^e.
+__device__ __forceinline__ void split16(float v, int e, _Float16& hi, _Float16& lo) {
+    const float s = __builtin_amdgcn_ldexpf(v, e);
+    hi = (_Float16)s;
+    lo = (_Float16)(s - (float)hi);
+}
+
+// One wavefront's steps n in [N0, N1) of the product of an input slot X with
+// filter offset G, added to acc (D layout above, still scaled).
+template <int N0, int N1>
+__device__ __forceinline__ v4f mm16_steps(const FI_SHARED _Float16* H, const FI_SHARED _Float16* X, int G, v4f acc) {
+    const int l = team_tid() & (kWave - 1);
+    const int r = l & 15, g = l >> 4;
+    const int d0 = 8 * (g & 1), bh = g >> 1;   // step n: bt = 2 n + bh, d = d0 .. d0 + 7
+    const FI_SHARED _Float16* ah = H + (G - kH16Lo + 16 * (r - bh) + d0);   // step n: - 32 n
+    const int e0 = 287 - (r + 16 * bh - d0);                                 // step n: - 32 n
+    const int cp = e0 & 1;
+    const FI_SHARED _Float16* xh = X + cp * kX16N + e0 + cp;
+    h8v a_hi[2], a_lo[2], b_hi[2], b_lo[2];
+    auto load = [&](int n, int u) {
+        a_hi[u] = *reinterpret_cast<const FI_SHARED h8v*>(ah - 32 * n);
+        a_lo[u] = *reinterpret_cast<const FI_SHARED h8v*>(ah - 32 * n + kH16N);
+        const FI_SHARED unsigned* ph = reinterpret_cast<const FI_SHARED unsigned*>(xh - 32 * n);
+        const FI_SHARED unsigned* pl = reinterpret_cast<const FI_SHARED unsigned*>(xh - 32 * n + 2 * kX16N);
+        b_hi[u] = __builtin_bit_cast(h8v, u4v{ph[0], ph[1], ph[2], ph[3]});
+        b_lo[u] = __builtin_bit_cast(h8v, u4v{pl[0], pl[1], pl[2], pl[3]});
+    };
+    load(N0, 0);
+#pragma unroll
+    for (int n = N0; n < N1; ++n) {
+        const int u = (n - N0) & 1;
+        if (n + 1 < N1) load(n + 1, u ^ 1);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[u], b_hi[u], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[u], b_lo[u], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[u], b_hi[u], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// The products of the boundary i (lowbit(i) = U in {256, 512}; see above),
+// added into the LDS ring.  The first wavefront takes steps 0 .. 4 of every
+// product, the second 5 .. 8 and hands its sums over through `part` (256
+// floats); the first adds both to the ring in a fixed order.  ex[slot] and eh
+// are the scale exponents of the input slots and the filter table.
+__device__ __forceinline__ void mm16_tiles(int64_t i, int U, const FI_SHARED _Float16* H,
+                                           const FI_SHARED _Float16* X16, const FI_SHARED int* ex, int eh,
                                            FI_SHARED float* ring, FI_SHARED float* part) {
-    static_assert(kBlk == 256 && kTeamWaves == 2, "the matrix-core tile covers one block, on two wavefronts");
     const int tid = team_tid();
     const int l = tid & (kWave - 1);
-    const int al = l & 15, kk = l >> 4;
-    // A of step (d, c), lane (alpha, kk): lag g = 256 + d - 64 c + 16 j with
-    // j = alpha - kk; with G = g - 16 j + 64 = 320 + d - 64 c (>= 64), s(g) =
-    // G + G / 16 + 17 j (16 j / 16 = j exactly).  B of step (d, c), lane
-    // (a, kk): x[a - d + 16 (4c + kk)] = xz[a + 16 kk + 64 c - d + 15].
-    // The two wavefronts take d < 8 and d >= 8 (40 steps each); the second
-    // hands its partial sums over through LDS (`part`, 256 floats), and the
-    // first adds both to the ring in a fixed order.
     const bool first = __builtin_amdgcn_readfirstlane(tid) < kWave;
-    const FI_SHARED float* ab = hsk + 17 * (al - kk);
-    const FI_SHARED float* bb = xz + al + 16 * kk;
-    v4f y;
-    if (first) y = mm_toeplitz<5, 320, 0, 8>(ab, bb, v4f{0.f, 0.f, 0.f, 0.f});
-    else y = mm_toeplitz<5, 320, 8, 8>(ab, bb, v4f{0.f, 0.f, 0.f, 0.f});
+    const int np = U == kBlk ? (((i & (4 * kBlk - 1)) == 3 * kBlk) ? 3 : 1) : 2;
+    v4f y = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pr = 0; pr < 3; ++pr) {
+        if (pr < np) {
+            const int64_t tin = i - (int64_t)kBlk * (pr + 1);   // the input block
+            const int G = kBlk * (pr + 1);
+            const int slot = (int)(tin >> kLog2Blk) & 3;
+            const FI_SHARED _Float16* X = X16 + slot * kX16Slot;
+            v4f a = v4f{0.f, 0.f, 0.f, 0.f};
+            if (first) a = mm16_steps<0, 5>(H, X, G, a);
+            else a = mm16_steps<5, 9>(H, X, G, a);
+            const int e = -(ex[slot] + eh);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) y[k] += __builtin_amdgcn_ldexpf(a[k], e);
+        }
+    }
     if (!first) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part[4 * l + r] = y[r];
+        for (int k = 0; k < 4; ++k) part[4 * l + k] = y[k];
     }
     team_sync();
     if (first) {
-        // position q = a + 16 alpha of the next block
+        const int al = l & 15, kk = l >> 4;
+        // position q = al + 16 alpha, alpha = 4 kk + k
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ring[al + 16 * (4 * kk + r)] += y[r] + part[4 * l + r];
+        for (int k = 0; k < 4; ++k) ring[al + 16 * (4 * kk + k)] += y[k] + part[4 * l + k];
+    }
+}
+
+// The block's inputs x[p] (lane l holds p = 64 k + l in v[k]) into input slot
+// X as fp16 parts scaled by 2^e, in both reversed copies.
+__device__ __forceinline__ void put_x16(FI_SHARED _Float16* X, const float* v, int e) {
+    const int l = team_tid() & (kWave - 1);
+#pragma unroll
+    for (int k = 0; k < kRegs; ++k) {
+        const int p = kWave * k + l;
+        _Float16 hi, lo;
+        split16(v[k], e, hi, lo);
+        X[287 - p] = hi;
+        X[kX16N + 288 - p] = hi;
+        X[2 * kX16N + 287 - p] = lo;
+        X[3 * kX16N + 288 - p] = lo;
+    }
+}
+
+// The zero padding of the three input slots: in each copy the positions no
+// input reaches (x[p] for p outside [0, 256)), as whole dwords: [0, 17) and
+// [144, 152) (a dword there that also holds an input is written before the
+// block's inputs are).  Run by NT threads from tid.
+template <int NT>
+__device__ __forceinline__ void zero_x16_pad(FI_SHARED _Float16* X16, int tid) {
+    FI_SHARED unsigned* w = reinterpret_cast<FI_SHARED unsigned*>(X16);
+    constexpr int kPerCopy = 17 + 8, kCopies = 3 * 4;
+    for (int q = tid; q < kPerCopy * kCopies; q += NT) {
+        const int cpy = q / kPerCopy, o = q % kPerCopy;
+        w[cpy * (kX16N / 2) + (o < 17 ? o : 144 + (o - 17))] = 0u;
+    }
+}
+
+// The filter table from the channel's filter row (lags <= 0, >= 1024 and
+// >= L are zero), scaled by 2^eh.  Run by NT threads from tid.
+template <int NT>
+__device__ __forceinline__ void build_h16(FI_SHARED _Float16* H, const FI_GLOBAL float* hrow, int64_t L, int eh, int tid) {
+    for (int q = tid; q < kH16N; q += NT) {
+        const int g = q + kH16Lo;
+        const float v = (g >= 1 && g < L) ? hrow[g] : 0.f;
+        _Float16 hi, lo;
+        split16(v, eh, hi, lo);
+        H[q] = hi;
+        H[kH16N + q] = lo;
     }
 }
 
@@ -1314,20 +1455,22 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             }
         }
     };
-    // the matrix-core tile's zero-padded input block and its filter h[-64,
-    // 512) at slots (g + 64) + (g + 64) / 16 (zero at g < 0 and g >= L):
-    // built when a channel starts and after a tile whose transform reaches
-    // them
+    // the block's zero-padded inputs (cleared when a channel starts and
+    // after a tile whose transform reaches them)
     FI_SHARED float* mxz = reinterpret_cast<FI_SHARED float*>(smem_ptr(smem) + kRunMmOff);
-    FI_SHARED float* mhs = mxz + kMmXFloats;
-    FI_SHARED float* myb = mhs + kMmHSlots;   // the block's y, for the other wavefronts' stores
+    FI_SHARED float* myb = mxz + kMmXFloats;   // the block's y, for the other wavefronts' stores
     auto build_mm = [&](const FI_GLOBAL float* hrow) {
         for (int q = tid; q < kMmXFloats; q += kTeam) mxz[q] = 0.f;
-        for (int e = tid; e < 64 + 2 * kBlk; e += kTeam) {
-            const int g = e - 64;
-            mhs[e + e / 16] = (g >= 0 && g < L) ? hrow[g] : 0.f;
-        }
     };
+    // The tiles of side kBlk and 2 kBlk on the matrix cores in fp16 halves
+    // (mm16_tiles) wherever the direct tiles stop below kBlk: the filter
+    // table, the input slots and their scale exponents.
+    const bool f16 = d.T < kBlk;
+    FI_SHARED _Float16* H16 = reinterpret_cast<FI_SHARED _Float16*>(smem_ptr(smem) + kH16Off);
+    FI_SHARED _Float16* X16 = reinterpret_cast<FI_SHARED _Float16*>(smem_ptr(smem) + kX16Off);
+    __shared__ int s_ex16[4];
+    __shared__ float s_hmax[kTeamWaves];
+    int eh = 0;   // the filter table's scale exponent (per channel)
     fill_lds_twiddles(twl);
     // Phase timing (profile build only; kProfile is false in the product
     // build and all of this folds away): the chain wavefront's cycle sums,
@@ -1364,6 +1507,17 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             for (int q = tid; q < 2 * d.T; q += kTeam) htap[q] = q < L ? hrow[q] : 0.f;
         build_taps4(hrow, open_block(0));
         build_mm(hrow);
+        if (f16) {
+            // the filter table's scale: the largest |h| over the lags it holds
+            float hm = 0.f;
+            for (int g = 1 + tid; g < kH16N + kH16Lo && g < L; g += kTeam) hm = fmaxf(hm, fabsf(hrow[g]));
+            hm = wave_max_abs(hm);
+            if (lane == 0) smem_ptr(s_hmax)[tid / kWave] = hm;
+            for (int q = tid; q < 3 * kX16Slot / 2; q += kTeam) reinterpret_cast<FI_SHARED unsigned*>(X16)[q] = 0u;
+            team_sync();
+            eh = scale16(fmaxf(smem_ptr(s_hmax)[0], smem_ptr(s_hmax)[1]));
+            build_h16<kTeam>(H16, hrow, L, eh, tid);
+        }
         if constexpr (RPUSH) {
             const FI_GLOBAL float* pr = gmem(d.pre + c * kBlk);
             for (int q = tid; q < kBlk; q += kTeam) s_pre[q] = pr[q];
@@ -1426,7 +1580,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             const int64_t inext = t0 + kBlk;
             const int Un = inext < L ? (int)(inext & -inext) : 0;
             // next tile of side kBlk: on the matrix cores (mm_tile256)
-            const bool mm_next = Un == kBlk && Un > d.T;
+            const bool mm_next = Un > d.T && (Un == kBlk || (f16 && Un == 2 * kBlk));
             const bool stage_x = Un > d.T && Un <= 2 * kStageSpecMax && !mm_next;
             const bool stage_spec = Un > d.T && Un <= kStageSpecMax && !mm_next;
             FI_SHARED float* xst = reinterpret_cast<FI_SHARED float*>(lbuf + lds_fft_elems(Un));
@@ -1454,7 +1608,9 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             // its lowest is set at or above 2 kBlk (the tile of that bit's
             // level covered them, its ring did not).
             const int64_t base = t0 + kBlk;
-            const bool nx_in_row = ((base & (base - 1)) >> (kLog2Blk + 1)) != 0;
+            // (with the tiles of side 2 kBlk on the matrix cores, no tile
+            // below 4 kBlk writes the row)
+            const bool nx_in_row = ((base & (base - 1)) >> (kLog2Blk + (f16 ? 2 : 1))) != 0;
             // A closed-loop block that runs the serial chain: the other
             // wavefront, idle during the chain, issues the previous block's
             // deferred y / x_out stores from LDS and moves the next block's
@@ -1465,6 +1621,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             // the LDS copies of y / x only after its chain.
             const bool chain_block = CLOSED && !open_block(t0);
             float hnx[kRegs];
+            // after a tile that overwrote the fp16 area (every FFT tile, at
+            // multiples of 4 kBlk), the other wavefront restores it: the slots'
+            // zero padding before its first barrier (before the chain
+            // wavefront writes this block's inputs there), the filter table
+            // before the block ends
+            const bool redo16 = f16 && t0 > 0 && (t0 & (4 * kBlk - 1)) == 0;
+            if (!chain_wave && redo16) zero_x16_pad<kWave>(X16, lane);
             if (!chain_wave && chain_block) {
                 if (defer_prev) store_deferred(t0 - kBlk);
                 team_sync();
@@ -1496,6 +1659,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(row + (inext - Un) + k + lane),
                                                          (FI_SHARED void*)(xst + k), 4, 0, 0);
                 }
+                if (redo16) build_h16<kWave>(H16, hrow, L, eh, lane);
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
                 if (chain_block) {
 #pragma unroll
@@ -1724,6 +1888,21 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     pf_tw = clock64();
                     pf_vm += pf_tw - pf_w0;
                 }
+                // the block's inputs for the fp16 tiles of the next three
+                // boundaries (the block before a multiple of 4 kBlk feeds an
+                // FFT tile instead); fed-back inputs are tanh values in [-1, 1]
+                if (f16 && t0 + kBlk < L && (t0 & (4 * kBlk - 1)) != 3 * kBlk) {
+                    const int slot = (int)(t0 >> kLog2Blk) & 3;
+                    int e = 14;
+                    if (!chain_block || bnd) {
+                        float m = fabsf(xk[0]);
+#pragma unroll
+                        for (int k = 1; k < kRegs; ++k) m = fmaxf(m, fabsf(xk[k]));
+                        e = scale16(wave_max_abs(m));
+                    }
+                    put_x16(X16 + slot * kX16Slot, xk, e);
+                    if (lane == 0) smem_ptr(s_ex16)[slot] = e;
+                }
                 // p now holds y of the block (lane m's accumulator stopped
                 // changing at step m: later pushes carry a zero tap there)
                 if (!chain_block) {
@@ -1780,8 +1959,8 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 const int U = (int)(i & -i);
                 if (U <= d.T) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
-                } else if (U == kBlk) {
-                    mm_tile256(mxz, mhs, accw, reinterpret_cast<FI_SHARED float*>(lbuf));
+                } else if (f16 && U <= 2 * kBlk) {
+                    mm16_tiles(i, U, H16, X16, smem_ptr(s_ex16), eh, accw, reinterpret_cast<FI_SHARED float*>(lbuf));
                 } else {
                     const int q = ilog2(U);
                     const FI_GLOBAL V2* spec =
