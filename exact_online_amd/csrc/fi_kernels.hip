@@ -1250,19 +1250,45 @@ __device__ __forceinline__ v4f mm16_steps(const FI_SHARED _Float16* H, const FI_
     return acc;
 }
 
-// The products of the boundary i (lowbit(i) = U in {256, 512}; see above),
-// added into the LDS ring.  The first wavefront takes steps 0 .. 4 of every
-// product, the second 5 .. 8 and hands its sums over through `part` (256
-// floats); the first adds both to the ring in a fixed order.  ex[slot] and eh
-// are the scale exponents of the input slots and the filter table.
-__device__ __forceinline__ void mm16_tiles(int64_t i, int U, const FI_SHARED _Float16* H,
+// The number of products at boundary i (lowbit(i) = U in {256, 512}).
+__device__ __forceinline__ int mm16_count(int64_t i, int U) {
+    return U == kBlk ? (((i & (4 * kBlk - 1)) == 3 * kBlk) ? 3 : 1) : 2;
+}
+
+// Products 1 .. np-1 of boundary i, whose inputs are older than the block
+// before i: formed by one wavefront alone (all nine steps), so that the team's
+// second wavefront can form them during the chain of that block, on the
+// matrix cores the chain leaves idle.
+__device__ __forceinline__ v4f mm16_pre(int64_t i, int np, const FI_SHARED _Float16* H, const FI_SHARED _Float16* X16,
+                                        const FI_SHARED int* ex, int eh) {
+    v4f y = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int pr = 1; pr < 3; ++pr) {
+        if (pr < np) {
+            const int64_t tin = i - (int64_t)kBlk * (pr + 1);
+            const int slot = (int)(tin >> kLog2Blk) & 3;
+            const v4f a = mm16_steps<0, 9>(H, X16 + slot * kX16Slot, kBlk * (pr + 1), v4f{0.f, 0.f, 0.f, 0.f});
+            const int e = -(ex[slot] + eh);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) y[k] += __builtin_amdgcn_ldexpf(a[k], e);
+        }
+    }
+    return y;
+}
+
+// The products 0 .. np-1 of boundary i (see above), added into the LDS ring,
+// plus `pre` (the second wavefront's sum of products formed earlier; zero
+// elsewhere).  The first wavefront takes steps 0 .. 4 of every product, the
+// second 5 .. 8 and hands its sums over through `part` (256 floats); the first
+// adds both to the ring in a fixed order.  ex[slot] and eh are the scale
+// exponents of the input slots and of the filter table.
+__device__ __forceinline__ void mm16_tiles(int64_t i, int np, const FI_SHARED _Float16* H,
                                            const FI_SHARED _Float16* X16, const FI_SHARED int* ex, int eh,
-                                           FI_SHARED float* ring, FI_SHARED float* part) {
+                                           FI_SHARED float* ring, FI_SHARED float* part, v4f pre) {
     const int tid = team_tid();
     const int l = tid & (kWave - 1);
     const bool first = __builtin_amdgcn_readfirstlane(tid) < kWave;
-    const int np = U == kBlk ? (((i & (4 * kBlk - 1)) == 3 * kBlk) ? 3 : 1) : 2;
-    v4f y = v4f{0.f, 0.f, 0.f, 0.f};
+    v4f y = pre;
 #pragma unroll
     for (int pr = 0; pr < 3; ++pr) {
         if (pr < np) {
@@ -1322,18 +1348,43 @@ __device__ __forceinline__ void zero_x16_pad(FI_SHARED _Float16* X16, int tid) {
 }
 
 // The filter table from the channel's filter row (lags <= 0, >= 1024 and
-// >= L are zero), scaled by 2^eh.  Run by NT threads from tid.
+// >= L are zero), scaled by 2^eh: load (every load issued before any is
+// used), then store.  Run by NT threads from tid.
 template <int NT>
-__device__ __forceinline__ void build_h16(FI_SHARED _Float16* H, const FI_GLOBAL float* hrow, int64_t L, int eh, int tid) {
-    for (int q = tid; q < kH16N; q += NT) {
-        const int g = q + kH16Lo;
-        const float v = (g >= 1 && g < L) ? hrow[g] : 0.f;
-        _Float16 hi, lo;
-        split16(v, eh, hi, lo);
-        H[q] = hi;
-        H[kH16N + q] = lo;
+struct H16Rows {
+    static constexpr int NPER = (kH16N + NT - 1) / NT;
+    float v[NPER];
+    __device__ __forceinline__ void load(const FI_GLOBAL float* hrow, int64_t L, int tid) {
+#pragma unroll
+        for (int u = 0; u < NPER; ++u) {
+            const int64_t g = (int64_t)(tid + NT * u) + kH16Lo;
+            v[u] = hrow[g < 1 ? 0 : (g < L ? g : L - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < NPER; ++u) {
+            const int g = tid + NT * u + kH16Lo;
+            if (!(g >= 1 && g < L && g < 1024)) v[u] = 0.f;
+        }
     }
-}
+    __device__ __forceinline__ float max_abs() const {
+        float m = 0.f;
+#pragma unroll
+        for (int u = 0; u < NPER; ++u) m = fmaxf(m, fabsf(v[u]));
+        return m;
+    }
+    __device__ __forceinline__ void store(FI_SHARED _Float16* H, int eh, int tid) const {
+#pragma unroll
+        for (int u = 0; u < NPER; ++u) {
+            const int q = tid + NT * u;
+            if (q < kH16N) {
+                _Float16 hi, lo;
+                split16(v[u], eh, hi, lo);
+                H[q] = hi;
+                H[kH16N + q] = lo;
+            }
+        }
+    }
+};
 
 // Open loop: a block's own lower triangle (lags 0 .. 255; the inputs are all
 // known, so nothing is serial) as one matrix-core product in the same
@@ -1508,15 +1559,16 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
         build_taps4(hrow, open_block(0));
         build_mm(hrow);
         if (f16) {
-            // the filter table's scale: the largest |h| over the lags it holds
-            float hm = 0.f;
-            for (int g = 1 + tid; g < kH16N + kH16Lo && g < L; g += kTeam) hm = fmaxf(hm, fabsf(hrow[g]));
-            hm = wave_max_abs(hm);
+            // the filter table and its scale (the largest |h| over the lags
+            // it holds), and zeroed input slots
+            H16Rows<kTeam> hr;
+            hr.load(hrow, L, tid);
+            const float hm = wave_max_abs(hr.max_abs());
             if (lane == 0) smem_ptr(s_hmax)[tid / kWave] = hm;
             for (int q = tid; q < 3 * kX16Slot / 2; q += kTeam) reinterpret_cast<FI_SHARED unsigned*>(X16)[q] = 0u;
             team_sync();
             eh = scale16(fmaxf(smem_ptr(s_hmax)[0], smem_ptr(s_hmax)[1]));
-            build_h16<kTeam>(H16, hrow, L, eh, tid);
+            hr.store(H16, eh, tid);
         }
         if constexpr (RPUSH) {
             const FI_GLOBAL float* pr = gmem(d.pre + c * kBlk);
@@ -1621,6 +1673,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             // the LDS copies of y / x only after its chain.
             const bool chain_block = CLOSED && !open_block(t0);
             float hnx[kRegs];
+            v4f pre16 = v4f{0.f, 0.f, 0.f, 0.f};   // the other wavefront's early products (mm16_pre)
             // after a tile that overwrote the fp16 area (every FFT tile, at
             // multiples of 4 kBlk), the other wavefront restores it: the slots'
             // zero padding before its first barrier (before the chain
@@ -1659,11 +1712,18 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         __builtin_amdgcn_global_load_lds((const FI_GLOBAL void*)(row + (inext - Un) + k + lane),
                                                          (FI_SHARED void*)(xst + k), 4, 0, 0);
                 }
-                if (redo16) build_h16<kWave>(H16, hrow, L, eh, lane);
+                if (redo16) {
+                    H16Rows<kWave> hr;
+                    hr.load(hrow, L, lane);
+                    hr.store(H16, eh, lane);
+                }
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
                 if (chain_block) {
 #pragma unroll
                     for (int k = 0; k < kRegs; ++k) accw[kWave * k + lane] = hnx[k];   // the ring now holds the next block
+                    // the next boundary's products of inputs older than this
+                    // block, on the matrix cores the chain leaves idle
+                    if (f16 && inext < L && Un > d.T && Un <= 2 * kBlk) pre16 = mm16_pre(inext, mm16_count(inext, Un), H16, X16, smem_ptr(s_ex16), eh);
                 }
                 // an open block's own triangle: this wavefront forms the
                 // products d >= 8 and hands them over through LDS (the first
@@ -1960,7 +2020,11 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 if (U <= d.T) {
                     direct_tile_lds(i, U, xring, xmask, htap, accw, wmask, L);
                 } else if (f16 && U <= 2 * kBlk) {
-                    mm16_tiles(i, U, H16, X16, smem_ptr(s_ex16), eh, accw, reinterpret_cast<FI_SHARED float*>(lbuf));
+                    // after a chain block the second wavefront has formed
+                    // the products of the older inputs during the chain
+                    const int np = mm16_count(i, U);
+                    mm16_tiles(i, CLOSED && !open_block(t0) ? 1 : np, H16, X16, smem_ptr(s_ex16), eh, accw,
+                               reinterpret_cast<FI_SHARED float*>(lbuf), pre16);
                 } else {
                     const int q = ilog2(U);
                     const FI_GLOBAL V2* spec =
