@@ -1262,7 +1262,7 @@ __device__ __forceinline__ int mm16_count(int64_t i, int U) {
 __device__ __forceinline__ v4f mm16_pre(int64_t i, int np, const FI_SHARED _Float16* H, const FI_SHARED _Float16* X16,
                                         const FI_SHARED int* ex, int eh) {
     v4f y = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+#pragma unroll 1   // one code path, cached between boundaries (faster than unrolled)
     for (int pr = 1; pr < 3; ++pr) {
         if (pr < np) {
             const int64_t tin = i - (int64_t)kBlk * (pr + 1);
@@ -1289,7 +1289,7 @@ __device__ __forceinline__ void mm16_tiles(int64_t i, int np, const FI_SHARED _F
     const int l = tid & (kWave - 1);
     const bool first = __builtin_amdgcn_readfirstlane(tid) < kWave;
     v4f y = pre;
-#pragma unroll
+#pragma unroll 1   // one code path, cached between boundaries (faster than unrolled)
     for (int pr = 0; pr < 3; ++pr) {
         if (pr < np) {
             const int64_t tin = i - (int64_t)kBlk * (pr + 1);   // the input block
