@@ -53,21 +53,36 @@ constexpr int lds_fft_elems(int M) { return M + M / 8; }
 // (handed to the other wavefront, which stores them during the next block).
 constexpr int kMmXFloats = 15 + kRunBlock + 65;
 constexpr int kMmBytes = (kMmXFloats + kRunBlock) * 4;
-// The tiles of side kRunBlock and 2 kRunBlock on the matrix cores in fp16
-// halves (hi + lo of each operand, scaled by powers of two) keep, at the
-// bottom of the FFT region above its first KiB (the two wavefronts'
-// hand-over area), the filter table -- lags kH16Lo .. kH16Lo + kH16N - 1,
-// the hi parts then the lo parts -- and three slots of input blocks, each two
-// reversed copies (the second shifted by one position) of hi and of lo parts.
-// FFT tiles of side >= 4 kRunBlock and their staging overwrite the area; it
-// is rebuilt after them.
-constexpr int kH16Lo = -16;
-constexpr int kH16N = 1040;
+// The block products on the matrix cores in fp16 halves (hi + lo of each
+// operand, scaled by powers of two) -- the tiles of side kRunBlock and
+// 2 kRunBlock, and (TRI: runs with blocks whose inputs are all given) those
+// blocks' own triangles -- keep, at the bottom of the FFT region above its
+// first KiB (the two wavefronts' hand-over area), the filter table -- lags
+// lo .. lo + n - 1, the hi parts then the lo parts -- and the slots of input
+// blocks, each two reversed copies (the second shifted by one position) of hi
+// and of lo parts.  FFT tiles of side >= 4 kRunBlock and their staging
+// overwrite the area; it is rebuilt after them.  A triangle is a product at
+// lag offset 0, so TRI adds 256 zero lags below the table (lag 0 included)
+// and a fourth slot, placed first so that it lies below the staging area of
+// the FFT tile that follows its block; without TRI the table starts at lag 1
+// (lags below 16 are never read) and the three slots are the blocks at 0,
+// 256 and 512 mod 1024.
 constexpr int kX16N = 304;
 constexpr int kH16Off = 1024;
-constexpr int kX16Off = kH16Off + 2 * kH16N * 2;
 constexpr int kX16Slot = 4 * kX16N;   // halfs per slot
-constexpr int kX16End = kX16Off + 3 * kX16Slot * 2;
+template <bool TRI>
+struct F16Area {
+    static constexpr int kLo = TRI ? -272 : -16;       // the table's lowest lag
+    static constexpr int kN = TRI ? 1296 : 1040;       // lags in the table
+    static constexpr int kFirst = TRI ? 0 : 1;         // the lowest nonzero lag
+    static constexpr int kSlots = TRI ? 4 : 3;
+    static constexpr int kXOff = kH16Off + 2 * kN * 2;   // bytes
+    // slot s (the block at 256 s mod 1024), in halfs from kXOff
+    static constexpr int slot_off(int s) { return (TRI ? ((s + 1) & 3) : s) * kX16Slot; }
+    static constexpr int kEnd = kXOff + kSlots * kX16Slot * 2;
+};
+static_assert(F16Area<true>::kXOff + kX16Slot * 2 <= lds_fft_elems(1024) * 8,
+              "slot 3 lies below the staging of the 1024-point tile");
 // The run kernel's FFT / staging region has one fixed layout (compile-time
 // offsets, whatever L is): the staging area of the largest staged tile (side
 // 2048: its transform buffer and input block; smaller tiles also stage their
@@ -79,7 +94,9 @@ constexpr int kRunFftReg = lds_fft_elems(kLdsFftMax) * 8 > kRunMmOff + kMmBytes 
                                ? lds_fft_elems(kLdsFftMax) * 8
                                : kRunMmOff + kMmBytes + kTapTableBytes;
 static_assert(lds_fft_elems(1024) * 8 + 4 * 1024 + 8 * (1024 + 2) <= kRunMmOff, "staging of the tiles up to 1024 fits");
-static_assert(kX16End <= kRunMmOff && kH16Off % 16 == 0 && kX16Off % 16 == 0, "the fp16 tile area fits below the matrix-core data");
+static_assert(F16Area<true>::kEnd <= kRunMmOff && F16Area<false>::kEnd <= kRunMmOff && kH16Off % 16 == 0 &&
+                  F16Area<true>::kXOff % 16 == 0 && F16Area<false>::kXOff % 16 == 0,
+              "the fp16 tile area fits below the matrix-core data");
 
 // Device state of one handle.  Layouts (rows padded to LS = L rounded up to 64):
 //   hT[D][LS]      filter, one contiguous row per channel c, fp32

@@ -1188,7 +1188,7 @@ __device__ __forceinline__ v4f mm_toeplitz(const FI_SHARED float* ab, const FI_S
 // products hi hi + hi lo + lo hi, accumulated in fp32, and the result is
 // scaled back exactly.  The part left out, lo lo, and the parts' rounding are
 // below 2^-21 of the largest product.
-// Operands in LDS: A from the filter table (H[lag - kH16Lo], eight
+// Operands in LDS: A from the filter table (H[lag - lo], eight
 // consecutive lags, 16-byte aligned); B from the slot's reversed input copies
 // (copy c holds x[287 + c - m] at m, so the eight values x[s], x[s-1], ...,
 // x[s-7] sit at m = 287 - s + c, .. + 7, with c the parity that makes m
@@ -1220,19 +1220,20 @@ __device__ __forceinline__ void split16(float v, int e, _Float16& hi, _Float16& 
 
 // One wavefront's steps n in [N0, N1) of the product of an input slot X with
 // filter offset G, added to acc (D layout above, still scaled).
-template <int N0, int N1>
+template <int N0, int N1, bool TRI>
 __device__ __forceinline__ v4f mm16_steps(const FI_SHARED _Float16* H, const FI_SHARED _Float16* X, int G, v4f acc) {
     const int l = team_tid() & (kWave - 1);
     const int r = l & 15, g = l >> 4;
     const int d0 = 8 * (g & 1), bh = g >> 1;   // step n: bt = 2 n + bh, d = d0 .. d0 + 7
-    const FI_SHARED _Float16* ah = H + (G - kH16Lo + 16 * (r - bh) + d0);   // step n: - 32 n
+    using A16 = F16Area<TRI>;
+    const FI_SHARED _Float16* ah = H + (G - A16::kLo + 16 * (r - bh) + d0);   // step n: - 32 n
     const int e0 = 287 - (r + 16 * bh - d0);                                 // step n: - 32 n
     const int cp = e0 & 1;
     const FI_SHARED _Float16* xh = X + cp * kX16N + e0 + cp;
     h8v a_hi[2], a_lo[2], b_hi[2], b_lo[2];
     auto load = [&](int n, int u) {
         a_hi[u] = *reinterpret_cast<const FI_SHARED h8v*>(ah - 32 * n);
-        a_lo[u] = *reinterpret_cast<const FI_SHARED h8v*>(ah - 32 * n + kH16N);
+        a_lo[u] = *reinterpret_cast<const FI_SHARED h8v*>(ah - 32 * n + A16::kN);
         const FI_SHARED unsigned* ph = reinterpret_cast<const FI_SHARED unsigned*>(xh - 32 * n);
         const FI_SHARED unsigned* pl = reinterpret_cast<const FI_SHARED unsigned*>(xh - 32 * n + 2 * kX16N);
         b_hi[u] = __builtin_bit_cast(h8v, u4v{ph[0], ph[1], ph[2], ph[3]});
@@ -1259,6 +1260,7 @@ __device__ __forceinline__ int mm16_count(int64_t i, int U) {
 // before i: formed by one wavefront alone (all nine steps), so that the team's
 // second wavefront can form them during the chain of that block, on the
 // matrix cores the chain leaves idle.
+template <bool TRI>
 __device__ __forceinline__ v4f mm16_pre(int64_t i, int np, const FI_SHARED _Float16* H, const FI_SHARED _Float16* X16,
                                         const FI_SHARED int* ex, int eh) {
     v4f y = v4f{0.f, 0.f, 0.f, 0.f};
@@ -1267,7 +1269,8 @@ __device__ __forceinline__ v4f mm16_pre(int64_t i, int np, const FI_SHARED _Floa
         if (pr < np) {
             const int64_t tin = i - (int64_t)kBlk * (pr + 1);
             const int slot = (int)(tin >> kLog2Blk) & 3;
-            const v4f a = mm16_steps<0, 9>(H, X16 + slot * kX16Slot, kBlk * (pr + 1), v4f{0.f, 0.f, 0.f, 0.f});
+            const v4f a = mm16_steps<0, 9, TRI>(H, X16 + F16Area<TRI>::slot_off(slot), kBlk * (pr + 1),
+                                                v4f{0.f, 0.f, 0.f, 0.f});
             const int e = -(ex[slot] + eh);
 #pragma unroll
             for (int k = 0; k < 4; ++k) y[k] += __builtin_amdgcn_ldexpf(a[k], e);
@@ -1282,6 +1285,7 @@ __device__ __forceinline__ v4f mm16_pre(int64_t i, int np, const FI_SHARED _Floa
 // second 5 .. 8 and hands its sums over through `part` (256 floats); the first
 // adds both to the ring in a fixed order.  ex[slot] and eh are the scale
 // exponents of the input slots and of the filter table.
+template <bool TRI>
 __device__ __forceinline__ void mm16_tiles(int64_t i, int np, const FI_SHARED _Float16* H,
                                            const FI_SHARED _Float16* X16, const FI_SHARED int* ex, int eh,
                                            FI_SHARED float* ring, FI_SHARED float* part, v4f pre) {
@@ -1295,10 +1299,10 @@ __device__ __forceinline__ void mm16_tiles(int64_t i, int np, const FI_SHARED _F
             const int64_t tin = i - (int64_t)kBlk * (pr + 1);   // the input block
             const int G = kBlk * (pr + 1);
             const int slot = (int)(tin >> kLog2Blk) & 3;
-            const FI_SHARED _Float16* X = X16 + slot * kX16Slot;
+            const FI_SHARED _Float16* X = X16 + F16Area<TRI>::slot_off(slot);
             v4f a = v4f{0.f, 0.f, 0.f, 0.f};
-            if (first) a = mm16_steps<0, 5>(H, X, G, a);
-            else a = mm16_steps<5, 9>(H, X, G, a);
+            if (first) a = mm16_steps<0, 5, TRI>(H, X, G, a);
+            else a = mm16_steps<5, 9, TRI>(H, X, G, a);
             const int e = -(ex[slot] + eh);
 #pragma unroll
             for (int k = 0; k < 4; ++k) y[k] += __builtin_amdgcn_ldexpf(a[k], e);
@@ -1333,37 +1337,54 @@ __device__ __forceinline__ void put_x16(FI_SHARED _Float16* X, const float* v, i
     }
 }
 
-// The zero padding of the three input slots: in each copy the positions no
-// input reaches (x[p] for p outside [0, 256)), as whole dwords: [0, 17) and
-// [144, 152) (a dword there that also holds an input is written before the
-// block's inputs are).  Run by NT threads from tid.
-template <int NT>
+// The zero padding of the input slots: in each copy the positions no input
+// reaches (x[p] for p outside [0, 256); copy 0 holds inputs at [32, 288),
+// copy 1 at [33, 289)).  Without TRI, as whole dwords [0, 17) and [144, 152)
+// (a dword there that also holds an input is written before the block's
+// inputs are); with TRI, no dword an input reaches, so the chain wavefront
+// may write a block's inputs at any time.  Run by NT threads from tid.
+template <int NT, bool TRI>
 __device__ __forceinline__ void zero_x16_pad(FI_SHARED _Float16* X16, int tid) {
     FI_SHARED unsigned* w = reinterpret_cast<FI_SHARED unsigned*>(X16);
-    constexpr int kPerCopy = 17 + 8, kCopies = 3 * 4;
-    for (int q = tid; q < kPerCopy * kCopies; q += NT) {
-        const int cpy = q / kPerCopy, o = q % kPerCopy;
-        w[cpy * (kX16N / 2) + (o < 17 ? o : 144 + (o - 17))] = 0u;
+    if constexpr (!TRI) {
+        constexpr int kPerCopy = 17 + 8, kCopies = 3 * 4;
+        for (int q = tid; q < kPerCopy * kCopies; q += NT) {
+            const int cpy = q / kPerCopy, o = q % kPerCopy;
+            w[cpy * (kX16N / 2) + (o < 17 ? o : 144 + (o - 17))] = 0u;
+        }
+    } else {
+        constexpr int kPerCopy = 16 + 8, kCopies = F16Area<TRI>::kSlots * 4;
+        for (int q = tid; q < kPerCopy * kCopies; q += NT) {
+            const int cpy = q / kPerCopy, o = q % kPerCopy;
+            const bool c1 = cpy & 1;   // copy 1 of its part
+            if (o < 16) w[cpy * (kX16N / 2) + o] = 0u;   // halfs [0, 32)
+            else if (!c1 || o > 16) w[cpy * (kX16N / 2) + 144 + (o - 16)] = 0u;   // [288 (c1: 290), 304)
+            else {   // copy 1: the halfs 32 and 289
+                X16[cpy * kX16N + 32] = (_Float16)0.f;
+                X16[cpy * kX16N + 289] = (_Float16)0.f;
+            }
+        }
     }
 }
 
-// The filter table from the channel's filter row (lags <= 0, >= 1024 and
-// >= L are zero), scaled by 2^eh: load (every load issued before any is
+// The filter table from the channel's filter row (lags below kFirst, >= 1024
+// and >= L are zero), scaled by 2^eh: load (every load issued before any is
 // used), then store.  Run by NT threads from tid.
-template <int NT>
+template <int NT, bool TRI>
 struct H16Rows {
-    static constexpr int NPER = (kH16N + NT - 1) / NT;
+    using A16 = F16Area<TRI>;
+    static constexpr int NPER = (A16::kN + NT - 1) / NT;
     float v[NPER];
     __device__ __forceinline__ void load(const FI_GLOBAL float* hrow, int64_t L, int tid) {
 #pragma unroll
         for (int u = 0; u < NPER; ++u) {
-            const int64_t g = (int64_t)(tid + NT * u) + kH16Lo;
-            v[u] = hrow[g < 1 ? 0 : (g < L ? g : L - 1)];
+            const int64_t g = (int64_t)(tid + NT * u) + A16::kLo;
+            v[u] = hrow[g < A16::kFirst ? 0 : (g < L ? g : L - 1)];
         }
 #pragma unroll
         for (int u = 0; u < NPER; ++u) {
-            const int g = tid + NT * u + kH16Lo;
-            if (!(g >= 1 && g < L && g < 1024)) v[u] = 0.f;
+            const int g = tid + NT * u + A16::kLo;
+            if (!(g >= A16::kFirst && g < L && g < 1024)) v[u] = 0.f;
         }
     }
     __device__ __forceinline__ float max_abs() const {
@@ -1376,11 +1397,11 @@ struct H16Rows {
 #pragma unroll
         for (int u = 0; u < NPER; ++u) {
             const int q = tid + NT * u;
-            if (q < kH16N) {
+            if (q < A16::kN) {
                 _Float16 hi, lo;
                 split16(v[u], eh, hi, lo);
                 H[q] = hi;
-                H[kH16N + q] = lo;
+                H[A16::kN + q] = lo;
             }
         }
     }
@@ -1518,8 +1539,12 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     // table, the input slots and their scale exponents.
     const bool f16 = d.T < kBlk;
     FI_SHARED _Float16* H16 = reinterpret_cast<FI_SHARED _Float16*>(smem_ptr(smem) + kH16Off);
-    FI_SHARED _Float16* X16 = reinterpret_cast<FI_SHARED _Float16*>(smem_ptr(smem) + kX16Off);
-    __shared__ int s_ex16[4];
+    // runs with blocks whose inputs are all given form those blocks'
+    // triangles in fp16 halves too (a wider table and a fourth input slot)
+    constexpr bool TRI = !CLOSED || PROMPT;
+    using A16 = F16Area<TRI>;
+    FI_SHARED _Float16* X16 = reinterpret_cast<FI_SHARED _Float16*>(smem_ptr(smem) + A16::kXOff);
+    __shared__ int s_ex16[A16::kSlots];
     __shared__ float s_hmax[kTeamWaves];
     int eh = 0;   // the filter table's scale exponent (per channel)
     fill_lds_twiddles(twl);
@@ -1561,11 +1586,11 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
         if (f16) {
             // the filter table and its scale (the largest |h| over the lags
             // it holds), and zeroed input slots
-            H16Rows<kTeam> hr;
+            H16Rows<kTeam, TRI> hr;
             hr.load(hrow, L, tid);
             const float hm = wave_max_abs(hr.max_abs());
             if (lane == 0) smem_ptr(s_hmax)[tid / kWave] = hm;
-            for (int q = tid; q < 3 * kX16Slot / 2; q += kTeam) reinterpret_cast<FI_SHARED unsigned*>(X16)[q] = 0u;
+            for (int q = tid; q < A16::kSlots * kX16Slot / 2; q += kTeam) reinterpret_cast<FI_SHARED unsigned*>(X16)[q] = 0u;
             team_sync();
             eh = scale16(fmaxf(smem_ptr(s_hmax)[0], smem_ptr(s_hmax)[1]));
             hr.store(H16, eh, tid);
@@ -1680,7 +1705,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             // wavefront writes this block's inputs there), the filter table
             // before the block ends
             const bool redo16 = f16 && t0 > 0 && (t0 & (4 * kBlk - 1)) == 0;
-            if (!chain_wave && redo16) zero_x16_pad<kWave>(X16, lane);
+            if (!chain_wave && redo16) zero_x16_pad<kWave, TRI>(X16, lane);
             if (!chain_wave && chain_block) {
                 if (defer_prev) store_deferred(t0 - kBlk);
                 team_sync();
@@ -1713,7 +1738,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                                                          (FI_SHARED void*)(xst + k), 4, 0, 0);
                 }
                 if (redo16) {
-                    H16Rows<kWave> hr;
+                    H16Rows<kWave, TRI> hr;
                     hr.load(hrow, L, lane);
                     hr.store(H16, eh, lane);
                 }
@@ -1723,14 +1748,23 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     for (int k = 0; k < kRegs; ++k) accw[kWave * k + lane] = hnx[k];   // the ring now holds the next block
                     // the next boundary's products of inputs older than this
                     // block, on the matrix cores the chain leaves idle
-                    if (f16 && inext < L && Un > d.T && Un <= 2 * kBlk) pre16 = mm16_pre(inext, mm16_count(inext, Un), H16, X16, smem_ptr(s_ex16), eh);
+                    if (f16 && inext < L && Un > d.T && Un <= 2 * kBlk) pre16 = mm16_pre<TRI>(inext, mm16_count(inext, Un), H16, X16, smem_ptr(s_ex16), eh);
                 }
                 // an open block's own triangle: this wavefront forms the
                 // products d >= 8 and hands them over through LDS (the first
                 // 256 floats of the FFT region, which no staging reaches)
                 if (open_block(t0)) {
                     team_sync();   // the chain wavefront has written the block's inputs
-                    const v4f yh = mm_triangle_half<8>(mxz, hz, v4f{0.f, 0.f, 0.f, 0.f});
+                    v4f yh;
+                    if (f16) {
+                        const int bslot = (int)(t0 >> kLog2Blk) & 3;
+                        const v4f a = mm16_steps<5, 9, TRI>(H16, X16 + A16::slot_off(bslot), 0, v4f{0.f, 0.f, 0.f, 0.f});
+                        const int e = -(smem_ptr(s_ex16)[bslot] + eh);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) yh[r] = __builtin_amdgcn_ldexpf(a[r], e);
+                    } else {
+                        yh = mm_triangle_half<8>(mxz, hz, v4f{0.f, 0.f, 0.f, 0.f});
+                    }
                     FI_SHARED float* part = reinterpret_cast<FI_SHARED float*>(lbuf);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) part[4 * lane + r] = yh[r];
@@ -1790,9 +1824,31 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     v4f init;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) init[r] = accw[al + 16 * (4 * kk + r)];
+                    const int bslot = (int)(t0 >> kLog2Blk) & 3;
+                    if (f16) {
+                        // the block's inputs as fp16 halves: its triangle here
+                        // (a block product with lag offset 0: the table is
+                        // zero at negative lags) and the block products of the
+                        // boundaries after it
+                        float m = fabsf(xb[0]);
+#pragma unroll
+                        for (int k = 1; k < kRegs; ++k) m = fmaxf(m, fabsf(xb[k]));
+                        const int e = scale16(wave_max_abs(m));
+                        put_x16(X16 + A16::slot_off(bslot), xb, e);
+                        if (lane == 0) smem_ptr(s_ex16)[bslot] = e;
+                    }
                     // the products d < 8 here, d >= 8 on the other wavefront
+                    // (fp16 halves: steps 0 .. 4 here, 5 .. 8 there)
                     team_sync();
-                    v4f yq = mm_triangle_half<0>(mxz, hz, init);
+                    v4f yq;
+                    if (f16) {
+                        const v4f a = mm16_steps<0, 5, TRI>(H16, X16 + A16::slot_off(bslot), 0, v4f{0.f, 0.f, 0.f, 0.f});
+                        const int e = -(smem_ptr(s_ex16)[bslot] + eh);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) yq[r] = init[r] + __builtin_amdgcn_ldexpf(a[r], e);
+                    } else {
+                        yq = mm_triangle_half<0>(mxz, hz, init);
+                    }
                     team_sync();
                     const FI_SHARED float* part = reinterpret_cast<const FI_SHARED float*>(lbuf);
 #pragma unroll
@@ -1951,7 +2007,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                 // the block's inputs for the fp16 tiles of the next three
                 // boundaries (the block before a multiple of 4 kBlk feeds an
                 // FFT tile instead); fed-back inputs are tanh values in [-1, 1]
-                if (f16 && t0 + kBlk < L && (t0 & (4 * kBlk - 1)) != 3 * kBlk) {
+                if (f16 && !openb && t0 + kBlk < L && (t0 & (4 * kBlk - 1)) != 3 * kBlk) {
                     const int slot = (int)(t0 >> kLog2Blk) & 3;
                     int e = 14;
                     if (!chain_block || bnd) {
@@ -1960,7 +2016,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         for (int k = 1; k < kRegs; ++k) m = fmaxf(m, fabsf(xk[k]));
                         e = scale16(wave_max_abs(m));
                     }
-                    put_x16(X16 + slot * kX16Slot, xk, e);
+                    put_x16(X16 + A16::slot_off(slot), xk, e);
                     if (lane == 0) smem_ptr(s_ex16)[slot] = e;
                 }
                 // p now holds y of the block (lane m's accumulator stopped
@@ -2023,7 +2079,7 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     // after a chain block the second wavefront has formed
                     // the products of the older inputs during the chain
                     const int np = mm16_count(i, U);
-                    mm16_tiles(i, CLOSED && !open_block(t0) ? 1 : np, H16, X16, smem_ptr(s_ex16), eh, accw,
+                    mm16_tiles<TRI>(i, CLOSED && !open_block(t0) ? 1 : np, H16, X16, smem_ptr(s_ex16), eh, accw,
                                reinterpret_cast<FI_SHARED float*>(lbuf), pre16);
                 } else {
                     const int q = ilog2(U);

@@ -14,9 +14,10 @@ reaches.  Routes covered here:
    first/last global passes, the radix-8/4 global stages and the paired-block
    untangle) and at L = 2^20 (tiles up to 2^19 points).
 Tolerance: 2e-5 absolute per element (|x| < 6, FFT rounding of a unit tap);
-fi_step exact below its first FFT tile; the persistent pass exact below 256
-(the block's own triangle in fp32) and within 2^-21 relative up to 1024 (the
-tiles of side 256 and 512, matrix-core products of fp16 halves).  A random filter through fi_step at L = 2^15
+fi_step exact below its first FFT tile; the persistent pass (open loop here)
+within 2^-21 relative up to 1024: there every contribution is a matrix-core
+block product of fp16 halves (the block's own triangle, the tiles of side
+256 and 512).  A random filter through fi_step at L = 2^15
 is compared with the oracle (relative L2 <= 1e-5 overall and per channel).
 """
 import numpy as np
@@ -47,8 +48,8 @@ def _delta_case(L, ks, seed, run):
 
 def _check_delta(x, y, ks, exact_below, tol=2e-5, close_below=0):
     """Every position within tol; exact below exact_below; below close_below
-    (the reach of the persistent pass's fp16-half products, the tiles of side
-    256 and 512) within 2^-21 of |x|."""
+    (the reach of the persistent pass's fp16-half block products) within
+    2^-21 of |x| plus a floor of 2^-30 of the largest |x|."""
     L = x.shape[1]
     for c, k in enumerate(ks):
         ref = np.zeros(L)
@@ -58,7 +59,10 @@ def _check_delta(x, y, ks, exact_below, tol=2e-5, close_below=0):
         assert bad.size == 0, (k, int(bad[0]), float(err.max()))
         assert np.array_equal(y[0, :exact_below, c], ref[:exact_below].astype(np.float32)), k
         if close_below:
-            assert (err[:close_below] <= 2.0 ** -21 * np.abs(ref[:close_below])).all(), k
+            # x = hi + lo + r, |r| <= 2^-22 |x|, or an absolute 2^-24 of the
+            # scaled block (2^-37 of its largest |x|) where lo is subnormal
+            bound = 2.0 ** -21 * np.abs(ref[:close_below]) + 2.0 ** -30 * np.abs(x[0, :close_below, c]).max()
+            assert (err[:close_below] <= bound).all(), k
 
 
 @pytest.mark.parametrize("T", [64, 256])
@@ -99,7 +103,7 @@ def test_persistent_delta_l128k():
     log("case persistent delta filters L=131072")
     x, y = _delta_case(L, ks, 31, lambda hd, D, xd: gpu_run(hd, 1, D, L, "f32", xd, closed=False,
                                                               want_x=False)[0])
-    _check_delta(x, y, ks, exact_below=256, close_below=1024)
+    _check_delta(x, y, ks, exact_below=0, close_below=1024)
 
 
 def test_persistent_delta_l1m():
@@ -110,7 +114,7 @@ def test_persistent_delta_l1m():
     log("case persistent delta filters L=1048576")
     x, y = _delta_case(L, ks, 41, lambda hd, D, xd: gpu_run(hd, 1, D, L, "f32", xd, closed=False,
                                                               want_x=False)[0])
-    _check_delta(x, y, ks, exact_below=256, tol=4e-5, close_below=1024)
+    _check_delta(x, y, ks, exact_below=0, tol=4e-5, close_below=1024)
 
 
 def test_create_out_of_device_memory():
