@@ -1284,8 +1284,11 @@ __device__ __forceinline__ v4f mm16_pre(int64_t i, int np, const FI_SHARED _Floa
 // elsewhere).  The first wavefront takes steps 0 .. 4 of every product, the
 // second 5 .. 8 and hands its sums over through `part` (256 floats); the first
 // adds both to the ring in a fixed order.  ex[slot] and eh are the scale
-// exponents of the input slots and of the filter table.
-template <bool TRI>
+// exponents of the input slots and of the filter table.  EARLY (np = 1): the
+// second wavefront formed steps 0 .. 3 of product 0 during the chain, from
+// the first half of the block's inputs (they only reach inputs below 128),
+// and `pre` holds them; the rest is split 4 .. 6 / 7 .. 8.
+template <bool TRI, bool EARLY = false>
 __device__ __forceinline__ void mm16_tiles(int64_t i, int np, const FI_SHARED _Float16* H,
                                            const FI_SHARED _Float16* X16, const FI_SHARED int* ex, int eh,
                                            FI_SHARED float* ring, FI_SHARED float* part, v4f pre) {
@@ -1293,9 +1296,19 @@ __device__ __forceinline__ void mm16_tiles(int64_t i, int np, const FI_SHARED _F
     const int l = tid & (kWave - 1);
     const bool first = __builtin_amdgcn_readfirstlane(tid) < kWave;
     v4f y = pre;
+    if constexpr (EARLY) {
+        const int slot = (int)((i - kBlk) >> kLog2Blk) & 3;
+        const FI_SHARED _Float16* X = X16 + F16Area<TRI>::slot_off(slot);
+        v4f a = v4f{0.f, 0.f, 0.f, 0.f};
+        if (first) a = mm16_steps<4, 7, TRI>(H, X, kBlk, a);
+        else a = mm16_steps<7, 9, TRI>(H, X, kBlk, a);
+        const int e = -(ex[slot] + eh);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[k] += __builtin_amdgcn_ldexpf(a[k], e);
+    }
 #pragma unroll 1   // one code path, cached between boundaries (faster than unrolled)
     for (int pr = 0; pr < 3; ++pr) {
-        if (pr < np) {
+        if (!EARLY && pr < np) {
             const int64_t tin = i - (int64_t)kBlk * (pr + 1);   // the input block
             const int G = kBlk * (pr + 1);
             const int slot = (int)(tin >> kLog2Blk) & 3;
@@ -1321,12 +1334,14 @@ __device__ __forceinline__ void mm16_tiles(int64_t i, int np, const FI_SHARED _F
     }
 }
 
-// The block's inputs x[p] (lane l holds p = 64 k + l in v[k]) into input slot
-// X as fp16 parts scaled by 2^e, in both reversed copies.
+// The block's inputs x[p] (lane l holds p = 64 k + l in v[k]), for k in
+// [K0, K1), into input slot X as fp16 parts scaled by 2^e, in both reversed
+// copies.
+template <int K0 = 0, int K1 = kRegs>
 __device__ __forceinline__ void put_x16(FI_SHARED _Float16* X, const float* v, int e) {
     const int l = team_tid() & (kWave - 1);
 #pragma unroll
-    for (int k = 0; k < kRegs; ++k) {
+    for (int k = K0; k < K1; ++k) {
         const int p = kWave * k + l;
         _Float16 hi, lo;
         split16(v[k], e, hi, lo);
@@ -1547,6 +1562,15 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     __shared__ int s_ex16[A16::kSlots];
     __shared__ float s_hmax[kTeamWaves];
     int eh = 0;   // the filter table's scale exponent (per channel)
+    // RPUSH chain blocks before a boundary of side kBlk or 2 kBlk: the chain
+    // wavefront writes the fp16 parts of the block's first 128 inputs after
+    // the chain's second segment and then stores the count of such blocks
+    // so far here; the other wavefront, waiting for that count, forms the
+    // steps of the block's product that reach only those inputs during the
+    // rest of the chain (mm16_tiles, EARLY)
+    __shared__ int s_early;
+    int n_early = 0;
+    if (tid == 0) *smem_ptr(&s_early) = 0;   // ordered by the first channel's barrier
     fill_lds_twiddles(twl);
     // Phase timing (profile build only; kProfile is false in the product
     // build and all of this folds away): the chain wavefront's cycle sums,
@@ -1697,6 +1721,8 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
             // by then the chain wavefront has read the ring, and it rewrites
             // the LDS copies of y / x only after its chain.
             const bool chain_block = CLOSED && !open_block(t0);
+            const bool early16 = RPUSH && f16 && inext < L && Un > d.T && Un <= 2 * kBlk;
+            if (early16) ++n_early;
             float hnx[kRegs];
             v4f pre16 = v4f{0.f, 0.f, 0.f, 0.f};   // the other wavefront's early products (mm16_pre)
             // after a tile that overwrote the fp16 area (every FFT tile, at
@@ -1749,6 +1775,20 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     // the next boundary's products of inputs older than this
                     // block, on the matrix cores the chain leaves idle
                     if (f16 && inext < L && Un > d.T && Un <= 2 * kBlk) pre16 = mm16_pre<TRI>(inext, mm16_count(inext, Un), H16, X16, smem_ptr(s_ex16), eh);
+                    if (early16) {
+                        // wait (bounded) for the first half of this block's
+                        // inputs, then form the steps of its product that
+                        // reach only those
+                        for (int it = 0; it < (1 << 22); ++it) {
+                            if (__hip_atomic_load(smem_ptr(&s_early), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == n_early) break;
+                            __builtin_amdgcn_s_sleep(1);
+                        }
+                        const int s0 = (int)(t0 >> kLog2Blk) & 3;
+                        const v4f a = mm16_steps<0, 4, TRI>(H16, X16 + A16::slot_off(s0), kBlk, v4f{0.f, 0.f, 0.f, 0.f});
+                        const int e = -(smem_ptr(s_ex16)[s0] + eh);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) pre16[r] += __builtin_amdgcn_ldexpf(a[r], e);
+                    }
                 }
                 // an open block's own triangle: this wavefront forms the
                 // products d >= 8 and hands them over through LDS (the first
@@ -1953,6 +1993,23 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         // the other wavefront has taken what it stores and
                         // moves (see chain_block): meet it here
                         if constexpr (decltype(kc)::value == 1) team_sync();
+                        if constexpr (RPUSH && decltype(kc)::value == 2) {
+                            if (early16) {
+                                // the first 128 inputs are final (the registers of
+                                // positions below 128 no longer change): their
+                                // fp16 parts (tanh values: scale 2^14), then the count
+                                float f0 = __builtin_fmaf(-2.0f, tanh_rcp_scaled(p[0]), 1.0f);
+                                float f1 = __builtin_fmaf(-2.0f, tanh_rcp_scaled(p[1]), 1.0f);
+                                float xh[2];
+                                const float s0 = wave_shr1(f0), s1 = wave_shr1(f1);
+                                xh[0] = lane == 0 ? xstart : s0;
+                                xh[1] = lane == 0 ? readlane(f0, kWave - 1) : s1;
+                                const int slot = (int)(t0 >> kLog2Blk) & 3;
+                                put_x16<0, 2>(X16 + A16::slot_off(slot), xh, 14);
+                                if (lane == 0) smem_ptr(s_ex16)[slot] = 14;
+                                __hip_atomic_store(smem_ptr(&s_early), n_early, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                            }
+                        }
                         [[maybe_unused]] unsigned long long ts = 0;
                         if constexpr (kProfile) {
                             ts = clock64();
@@ -2016,8 +2073,12 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         for (int k = 1; k < kRegs; ++k) m = fmaxf(m, fabsf(xk[k]));
                         e = scale16(wave_max_abs(m));
                     }
-                    put_x16(X16 + A16::slot_off(slot), xk, e);
-                    if (lane == 0) smem_ptr(s_ex16)[slot] = e;
+                    if (early16) {
+                        put_x16<2, kRegs>(X16 + A16::slot_off(slot), xk, e);   // the first half went during the chain
+                    } else {
+                        put_x16(X16 + A16::slot_off(slot), xk, e);
+                        if (lane == 0) smem_ptr(s_ex16)[slot] = e;
+                    }
                 }
                 // p now holds y of the block (lane m's accumulator stopped
                 // changing at step m: later pushes carry a zero tap there)
@@ -2079,8 +2140,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     // after a chain block the second wavefront has formed
                     // the products of the older inputs during the chain
                     const int np = mm16_count(i, U);
-                    mm16_tiles<TRI>(i, CLOSED && !open_block(t0) ? 1 : np, H16, X16, smem_ptr(s_ex16), eh, accw,
-                               reinterpret_cast<FI_SHARED float*>(lbuf), pre16);
+                    if constexpr (RPUSH) {   // every block a chain block, early16 here
+                        mm16_tiles<TRI, true>(i, 1, H16, X16, smem_ptr(s_ex16), eh, accw,
+                                              reinterpret_cast<FI_SHARED float*>(lbuf), pre16);
+                    } else {
+                        mm16_tiles<TRI>(i, CLOSED && !open_block(t0) ? 1 : np, H16, X16, smem_ptr(s_ex16), eh, accw,
+                                        reinterpret_cast<FI_SHARED float*>(lbuf), pre16);
+                    }
                 } else {
                     const int q = ilog2(U);
                     const FI_GLOBAL V2* spec =
