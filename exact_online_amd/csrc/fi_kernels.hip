@@ -1776,14 +1776,29 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                     // block, on the matrix cores the chain leaves idle
                     if (f16 && inext < L && Un > d.T && Un <= 2 * kBlk) pre16 = mm16_pre<TRI>(inext, mm16_count(inext, Un), H16, X16, smem_ptr(s_ex16), eh);
                     if (early16) {
-                        // wait (bounded) for the first half of this block's
-                        // inputs, then form the steps of its product that
-                        // reach only those
+                        // wait (bounded) for the chain wavefront's registers of
+                        // the block's first 128 positions; from them, with the
+                        // same operations as its epilogue, the inputs x of those
+                        // positions into the block's slot as fp16 parts (tanh
+                        // values: scale 2^14); then the steps of the block's
+                        // product that reach only those inputs
                         for (int it = 0; it < (1 << 22); ++it) {
                             if (__hip_atomic_load(smem_ptr(&s_early), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == n_early) break;
                             __builtin_amdgcn_s_sleep(1);
                         }
                         const int s0 = (int)(t0 >> kLog2Blk) & 3;
+                        {
+                            const FI_SHARED float* hv = reinterpret_cast<const FI_SHARED float*>(lbuf);
+                            const float f0 = __builtin_fmaf(-2.0f, tanh_rcp_scaled(hv[lane]), 1.0f);
+                            const float f1 = __builtin_fmaf(-2.0f, tanh_rcp_scaled(hv[kWave + lane]), 1.0f);
+                            const float xs = hv[2 * kWave];
+                            float xh[2];
+                            const float sh0 = wave_shr1(f0), sh1 = wave_shr1(f1);
+                            xh[0] = lane == 0 ? xs : sh0;
+                            xh[1] = lane == 0 ? readlane(f0, kWave - 1) : sh1;
+                            put_x16<0, 2>(X16 + A16::slot_off(s0), xh, 14);
+                            if (lane == 0) smem_ptr(s_ex16)[s0] = 14;
+                        }
                         const v4f a = mm16_steps<0, 4, TRI>(H16, X16 + A16::slot_off(s0), kBlk, v4f{0.f, 0.f, 0.f, 0.f});
                         const int e = -(smem_ptr(s_ex16)[s0] + eh);
 #pragma unroll
@@ -1995,18 +2010,14 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
                         if constexpr (decltype(kc)::value == 1) team_sync();
                         if constexpr (RPUSH && decltype(kc)::value == 2) {
                             if (early16) {
-                                // the first 128 inputs are final (the registers of
-                                // positions below 128 no longer change): their
-                                // fp16 parts (tanh values: scale 2^14), then the count
-                                float f0 = __builtin_fmaf(-2.0f, tanh_rcp_scaled(p[0]), 1.0f);
-                                float f1 = __builtin_fmaf(-2.0f, tanh_rcp_scaled(p[1]), 1.0f);
-                                float xh[2];
-                                const float s0 = wave_shr1(f0), s1 = wave_shr1(f1);
-                                xh[0] = lane == 0 ? xstart : s0;
-                                xh[1] = lane == 0 ? readlane(f0, kWave - 1) : s1;
-                                const int slot = (int)(t0 >> kLog2Blk) & 3;
-                                put_x16<0, 2>(X16 + A16::slot_off(slot), xh, 14);
-                                if (lane == 0) smem_ptr(s_ex16)[slot] = 14;
+                                // the registers of positions below 128 no longer
+                                // change: hand them over (with x of the block's
+                                // first position) through the hand-over area, idle
+                                // during the chain, then the count
+                                FI_SHARED float* hv = reinterpret_cast<FI_SHARED float*>(lbuf);
+                                hv[lane] = p[0];
+                                hv[kWave + lane] = p[1];
+                                if (lane == 0) hv[2 * kWave] = xstart;
                                 __hip_atomic_store(smem_ptr(&s_early), n_early, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
                             }
                         }
