@@ -1562,12 +1562,13 @@ __global__ __launch_bounds__(kTeam) __attribute__((amdgpu_waves_per_eu(kTeamWave
     __shared__ int s_ex16[A16::kSlots];
     __shared__ float s_hmax[kTeamWaves];
     int eh = 0;   // the filter table's scale exponent (per channel)
-    // RPUSH chain blocks before a boundary of side kBlk or 2 kBlk: the chain
-    // wavefront writes the fp16 parts of the block's first 128 inputs after
-    // the chain's second segment and then stores the count of such blocks
-    // so far here; the other wavefront, waiting for that count, forms the
-    // steps of the block's product that reach only those inputs during the
-    // rest of the chain (mm16_tiles, EARLY)
+    // RPUSH chain blocks before a boundary of side kBlk or 2 kBlk: after the
+    // chain's second segment the chain wavefront hands over its registers of
+    // the block's first 128 positions and then stores the count of such
+    // blocks so far here; the other wavefront, waiting for that count, forms
+    // those positions' inputs in fp16 parts and the steps of the block's
+    // product that reach only them, during the rest of the chain (mm16_tiles,
+    // EARLY)
     __shared__ int s_early;
     int n_early = 0;
     if (tid == 0) *smem_ptr(&s_early) = 0;   // ordered by the first channel's barrier
